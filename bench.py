@@ -1,0 +1,383 @@
+"""Benchmark of the SSD layer core on one MI355X.
+
+One step = one full chunked prefill (all prefill stages: cumulative decay,
+chunk states, inter-chunk state passing, intra-chunk + off-diagonal output)
+over the Mamba-2-130M-shaped workload (batch 1, 4096 tokens, 24 heads,
+headdim 64, d_state 128, chunk 256, bf16 inputs, fp32 state and output),
+with inputs resident in HBM.  Each timed step starts cold: a 512 MiB read
+evicts the 256 MiB Infinity Cache and the L2s first, outside the timed
+events.  The decode update (batch 64, 80 heads, 1024 tokens) is timed in the
+same run and reported under "decode".
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on.  The oracle (fp64 CPU recurrence) is timed on
+the host's cores as "cpu_baseline".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mamba_ssd_scan_amd import ssd, synth  # noqa: E402
+
+METRIC = "SSD tokens/s + % roofline (prefill MFMA TFLOPS, decode-step HBM GB/s)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 matrix, published
+PREFILL_WORKLOAD = 1
+DECODE_WORKLOAD = 4
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_state_kernel": "ssd_chunk_state.hip",
+    "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
+    "step_kernel": "ssd_step.hip",
+}
+
+
+# ---------------------------------------------------------------------------- algorithmic work
+
+def alg_counts(s: synth.PrefillShape) -> dict:
+    """Algorithmic bytes and flops per launch of each prefill kernel.
+
+    Bytes: every tensor a kernel must read or write, once.  Flops: the
+    causal triangle of the intra-chunk products is counted (Q(Q+1)/2 pairs per
+    chunk), C.B^T once per group, multiply-add = 2 flops.
+    """
+    B, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
+    ib = 2 if s.dtype == "bf16" else 4
+    nc = -(-L // Q)
+    x = B * L * H * P * ib
+    dt = B * L * H * ib
+    bc = B * L * G * N * ib            # one of B or C
+    y = B * L * H * P * 4
+    chunk_tab = 2 * B * H * nc * Q * 4  # dA_cum + dt regrouped per chunk
+    states = B * H * nc * P * N * 4
+    st = B * H * P * N * 4
+    h0 = st if s.init_state != "zero" else 0
+    tri = Q * (Q + 1)                  # 2 flops x Q(Q+1)/2 pairs
+    k = {
+        "chunk_cumsum_kernel": dict(bytes=dt + chunk_tab, flops=2 * B * L * H),
+        "chunk_state_kernel": dict(bytes=x + bc + chunk_tab + states, flops=2 * B * H * L * P * N),
+        "state_passing_kernel": dict(bytes=2 * states + B * H * nc * 4 + h0 + st, flops=2 * B * H * nc * P * N),
+        "chunk_scan_kernel": dict(bytes=x + 2 * bc + chunk_tab + states + y,
+                                  flops=B * nc * (G * N * tri + H * P * tri) + 2 * B * H * L * P * N),
+    }
+    fused_bytes = x + dt + 2 * bc + y + st + h0
+    fused_flops = B * nc * (G * N * tri + H * P * tri) + 4 * B * H * L * P * N
+    return dict(kernels=k, fused_bytes=fused_bytes, fused_flops=fused_flops)
+
+
+def decode_bytes_per_step(s: synth.DecodeShape) -> int:
+    ib = 2 if s.dtype == "bf16" else 4
+    B, H, P, N, G = s.batch, s.nheads, s.headdim, s.dstate, s.ngroups
+    return 2 * B * H * P * N * 4 + B * H * P * ib + B * H * ib + 2 * B * G * N * ib + B * H * P * 4
+
+
+def source_hash(kernel: str) -> str:
+    path = os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, or None.
+
+    The summary is used only if it was taken on the current kernel source.
+    """
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------- GPU timing
+
+class Flusher:
+    """Evicts the Infinity Cache (256 MiB) and the L2s with a 512 MiB read."""
+
+    def __init__(self, torch, mib=512):
+        self.buf = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.sink += self.buf.sum()
+
+
+def time_launches(torch, fn, n, flush=None, before=None):
+    """Mean and min duration (us) of ``fn`` over n launches, HIP events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    stream = torch.cuda.current_stream()
+    for a, b in evs:
+        if before is not None:
+            before()
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return float(t.mean()), float(t.min())
+
+
+def prefill_buffers(torch, s, inp):
+    g = {k: synth.to_torch(inp[k], s.dtype) for k in ("x", "dt", "B", "C")}
+    g["A"] = torch.from_numpy(inp["A"]).cuda()
+    g["D"] = torch.from_numpy(inp["D"]).cuda()
+    g["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).cuda()
+    nc = -(-s.seqlen // s.chunk)
+    g["y"] = torch.empty((s.batch, s.seqlen, s.nheads, s.headdim), dtype=torch.float32, device="cuda")
+    g["final"] = torch.empty((s.batch, s.nheads, s.headdim, s.dstate), dtype=torch.float32, device="cuda")
+    g["ws"] = ssd.alloc_workspace(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk)
+    g["acum"] = torch.empty((s.batch, s.nheads, nc, s.chunk), dtype=torch.float32, device="cuda")
+    g["dtc"] = torch.empty_like(g["acum"])
+    g["states"] = torch.empty((s.batch, s.nheads, nc, s.headdim, s.dstate), dtype=torch.float32, device="cuda")
+    return g
+
+
+def run_prefill(g, s):
+    ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk, y=g["y"],
+                final_state=g["final"], workspace=g["ws"])
+
+
+def stage_fns(torch, g, s):
+    Q = s.chunk
+    pristine = {}
+
+    def cumsum():
+        ssd.chunk_cumsum(g["dt"], g["A"], chunk=Q, acum=g["acum"], dtc=g["dtc"])
+
+    def cstate():
+        ssd.chunk_state(g["x"], g["B"], g["acum"], g["dtc"], chunk=Q, states=g["states"])
+
+    def passing():
+        ssd.state_passing(g["states"], g["acum"], g["h0"], chunk=Q, final_state=g["final"])
+
+    def restore_states():  # state passing works in place: restart from the chunk states every launch
+        g["states"].copy_(pristine["states"])
+
+    def scan():
+        ssd.chunk_scan(g["x"], g["B"], g["C"], g["acum"], g["dtc"], g["states"], g["D"], chunk=Q, y=g["y"])
+
+    cumsum()
+    cstate()
+    torch.cuda.synchronize()
+    pristine["states"] = g["states"].clone()
+    passing()
+    torch.cuda.synchronize()
+    return {"chunk_cumsum_kernel": (cumsum, None), "chunk_state_kernel": (cstate, None),
+            "state_passing_kernel": (passing, restore_states), "chunk_scan_kernel": (scan, None)}
+
+
+# ---------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(s, inp, min_seconds=10.0, max_reps=2000):
+    from oracle import ref  # the oracle: test infrastructure, timed here as the CPU baseline
+    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("SSD_ORACLE_THREADS", "16")))
+    f64 = {k: (None if inp[k] is None else np.ascontiguousarray(inp[k], np.float64))
+           for k in ("x", "dt", "A", "B", "C", "D", "h0")}
+    ref.load()
+    reps, total = 0, 0.0
+    while reps < max_reps and (total < min_seconds or reps == 0):
+        t0 = time.perf_counter()
+        ref.prefill(f64["x"], f64["dt"], f64["A"], f64["B"], f64["C"], f64["D"], f64["h0"], nthreads=cores)
+        total += time.perf_counter() - t0
+        reps += 1
+    tokens = s.batch * s.seqlen * reps
+    return {"value": tokens / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full workload ({s.batch}x{s.seqlen} tokens, all {s.nheads} heads), fp64 sequential "
+                      f"recurrence, repeated {reps}x ({total:.1f} s)"}
+
+
+# ---------------------------------------------------------------------------- decode
+
+def bench_decode(torch, steps, flush):
+    s = synth.WORKLOADS[DECODE_WORKLOAD]
+    inp = synth.decode_inputs(s, synth.SEED_BASE + DECODE_WORKLOAD, steps=steps)
+    xs, dts = synth.to_torch(inp["x"], s.dtype), synth.to_torch(inp["dt"], s.dtype)
+    Bs, Cs = synth.to_torch(inp["B"], s.dtype), synth.to_torch(inp["C"], s.dtype)
+    del inp["x"]
+    A = torch.from_numpy(inp["A"]).cuda()
+    D = torch.from_numpy(inp["D"]).cuda()
+    state = torch.from_numpy(inp["state"]).cuda()
+    y = torch.empty((s.batch, s.nheads, s.headdim), dtype=torch.float32, device="cuda")
+    for t in range(min(8, steps)):  # warm-up
+        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for t in range(steps):
+        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us_loop = a.elapsed_time(b) * 1e3 / steps
+    # cold: flush before each step (64 sampled steps)
+    k = [0]
+
+    def one():
+        t = k[0] % steps
+        k[0] += 1
+        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+
+    us_cold, _ = time_launches(torch, one, min(64, steps), flush=flush)
+    nbytes = decode_bytes_per_step(s)
+    return {
+        "workload": synth.WORKLOAD_NAMES[DECODE_WORKLOAD], "steps": steps,
+        "us_per_step": us_loop, "tokens_per_s": s.batch / (us_loop * 1e-6),
+        "alg_bytes_per_step": nbytes, "gbps": nbytes / (us_loop * 1e-6) / 1e9,
+        "hbm_frac": nbytes / (us_loop * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "cold_us_per_step": us_cold, "cold_gbps": nbytes / (us_cold * 1e-6) / 1e9,
+        "cold_hbm_frac": nbytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "note": "us_per_step: 1024 back-to-back ssd_step launches on one state (the 168 MB state can stay in "
+                "the 256 MiB Infinity Cache between steps); cold: 512 MiB cache eviction before each step",
+    }
+
+
+# ---------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
+                                       "chunk_cumsum_kernel", "step", "copy"],
+                    help="profiling aid: launch only this work --steps times (cold), print nothing else")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the SSD core here is a single-GPU "
+              f"library and no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    ssd.lib()
+    flush = Flusher(torch)
+    s = synth.WORKLOADS[PREFILL_WORKLOAD]
+    wname = synth.WORKLOAD_NAMES[PREFILL_WORKLOAD]
+
+    if args.only == "copy":  # plain copy of known size, to scale HBM counters
+        src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            flush()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": args.steps}))
+        return 0
+    if args.only == "step":
+        print(json.dumps(bench_decode(torch, args.decode_steps, flush)))
+        return 0
+
+    inp = synth.prefill_inputs(s, synth.SEED_BASE + PREFILL_WORKLOAD)
+    g = prefill_buffers(torch, s, inp)
+    for _ in range(args.warmup):
+        run_prefill(g, s)
+    torch.cuda.synchronize()
+
+    if args.only == "prefill":
+        time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
+        return 0
+    stages = stage_fns(torch, g, s)
+    if args.only is not None:
+        fn, before = stages[args.only]
+        time_launches(torch, fn, args.steps, flush=flush, before=before)
+        return 0
+
+    # ---- timed region: exactly K cold steps, bracketed by synchronisations
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    us_step, us_step_min = time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    tokens = s.batch * s.seqlen
+
+    # warm (back-to-back) steps, for reference only
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        run_prefill(g, s)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us_warm = a.elapsed_time(b) * 1e3 / args.steps
+
+    # ---- per-kernel durations (cold), events on the launch stream
+    counts = alg_counts(s)
+    kernels = {}
+    for name, (fn, before) in stages.items():
+        us, us_min = time_launches(torch, fn, args.steps, flush=flush, before=before)
+        kb, kf = counts["kernels"][name]["bytes"], counts["kernels"][name]["flops"]
+        kernels[name] = {"us": us, "us_min": us_min, "alg_bytes": kb, "alg_flops": kf,
+                         "gbps": kb / (us * 1e-6) / 1e9, "tflops": kf / (us * 1e-6) / 1e12}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    d = kernels[dom]
+    intensity = d["alg_flops"] / d["alg_bytes"]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if intensity < ridge else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["gbps"] / HBM_PEAK_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": d["tflops"] / MFMA_BF16_PEAK_TFLOPS}
+    roof.update({"traffic": counter_traffic(dom, wname), "kernel": dom, "us_per_launch": d["us"],
+                 "alg_bytes_per_launch": d["alg_bytes"], "alg_flops_per_launch": d["alg_flops"],
+                 "intensity_flop_per_byte": intensity})
+
+    sec = us_step * 1e-6
+    prefill = {
+        "us_per_step_cold": us_step, "us_per_step_cold_min": us_step_min, "us_per_step_warm": us_warm,
+        "alg_tflops": counts["fused_flops"] / sec / 1e12,
+        "alg_mfma_frac": counts["fused_flops"] / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "alg_gbps_fused_bytes": counts["fused_bytes"] / sec / 1e9,
+        "hbm_frac_fused_bytes": counts["fused_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+        "fused_alg_bytes": counts["fused_bytes"], "alg_flops": counts["fused_flops"],
+        "attainable_frac": (counts["fused_bytes"] / (HBM_PEAK_GBS * 1e9)) / sec,
+        "warm_tokens_per_s": tokens / (us_warm * 1e-6),
+    }
+    out = {
+        "metric": METRIC, "value": tokens / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us_step / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wname, "batch": s.batch, "seqlen": s.seqlen, "nheads": s.nheads,
+                   "headdim": s.headdim, "dstate": s.dstate, "ngroups": s.ngroups, "chunk": s.chunk,
+                   "cache": "cold (512 MiB eviction before each step, outside the events)",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "prefill": prefill,
+        "kernels": kernels,
+        "timed_wall_s": wall,
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, args.decode_steps, flush)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(s, inp)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,164 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD layer core.
+ *
+ * The layer core is the per-head state-space recurrence with a scalar
+ * ("input-dependent diagonal") decay:
+ *
+ *   H_t = exp(dt_t * A_h) * H_{t-1} + dt_t * x_t * B_t^T      (state [P, N])
+ *   y_t = H_t * C_t + D_h * x_t                               (output [P])
+ *
+ * for every batch entry b and head h, head h reading group g = h / (H/G) of
+ * B and C.  Sources: "Mamba-Family State-Space Model Kernels on a
+ * Programmable CGLA", Sec. III-A (in-projection output [z, x, B, C, dt];
+ * chunks of Q tokens; Step-1 intra-chunk GEMM1 / Hadamard mask / GEMM2;
+ * Step-3 sequential inter-chunk update of the recurrent state with a
+ * diagonal A_c), Sec. IV-B and IV-C; "Compiler-First State Space Duality and
+ * Portable O(1) Autoregressive Caching for Inference", abstract (diagonal
+ * per-head dynamics, fixed-size chunking, a cached state for O(1) decode).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers, dense, row-major in the
+ *   layouts written next to each argument; base addresses 16-byte aligned.
+ * - The caller owns all memory.  The library never allocates or frees device
+ *   memory and keeps no device state; scratch comes from the caller's
+ *   workspace.  No global mutable state: calls are reentrant and thread-safe.
+ * - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *   stream) and return after enqueueing; nothing synchronises inside.
+ * - Errors are negative return codes, never exceptions.  Every argument is
+ *   validated before any HIP call, so a rejected call launches nothing.
+ *   SSD_ERR_HIP means a launch failed; faults inside a kernel surface at the
+ *   caller's next synchronisation.
+ * - `in_dtype` selects the storage type of x, dt, B, C (and nothing else):
+ *   SSD_BF16 (uint16 bit patterns of bfloat16) or SSD_F32.  A and D are
+ *   always fp32; state, workspace and y are always fp32.
+ * - Non-finite values are propagated, not trapped.  With SSD_BF16 inputs the
+ *   matrix-core operands are fp16: |x|, |B|, |C| must stay below 65504.
+ *
+ * Supported shapes: batch >= 1; seqlen >= 0; nheads % ngroups == 0;
+ * headdim (P) in {32, 64, 128}; dstate (N) in {32, 64, 128};
+ * chunk (Q) in {16, 32, 64, 128, 256}.  Anything else returns
+ * SSD_ERR_UNSUPPORTED (or SSD_ERR_INVALID_ARG for non-positive sizes).
+ */
+#ifndef MAMBA_SSD_SCAN_AMD_SSD_H
+#define MAMBA_SSD_SCAN_AMD_SSD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer, H % G != 0 */
+    SSD_ERR_UNSUPPORTED = -2, /* valid but unsupported P, N, Q or dtype */
+    SSD_ERR_WORKSPACE = -3,   /* workspace missing, too small or not 256-byte aligned */
+    SSD_ERR_HIP = -4          /* a HIP launch failed */
+};
+
+/* Static description of a status code (never NULL). */
+const char *ssd_status_string(int status);
+
+/* Library ABI version, (major << 16) | minor. */
+int ssd_version(void);
+
+/*
+ * Bytes of caller-provided workspace that ssd_prefill needs, or 0 for
+ * invalid/unsupported shapes.  Layout (each region 256-byte aligned):
+ *   dA_cum  [B, H, nc, Q] fp32   per-chunk inclusive cumsum of dt*A
+ *   dt_c    [B, H, nc, Q] fp32   dt regrouped per chunk (0 past seqlen)
+ *   states  [B, H, nc, P, N] fp32  chunk states, then entering states
+ * with nc = ceil(seqlen / Q).
+ */
+size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim,
+                                  int dstate, int ngroups, int chunk);
+
+/*
+ * Chunked prefill over a whole sequence (Step-1 intra-chunk output, chunk
+ * states, Step-3 inter-chunk state passing, off-diagonal output; see the
+ * stage entry points below, which it runs in order on `hip_stream`).
+ *
+ *   x   [B, L, H, P] in_dtype       dt [B, L, H] in_dtype (used as given:
+ *   A   [H] fp32                          positive step sizes, no softplus)
+ *   Bm  [B, L, G, N] in_dtype       Cm [B, L, G, N] in_dtype
+ *   D   [H] fp32, or NULL for no skip term
+ *   initial_state [B, H, P, N] fp32, or NULL for zeros
+ *   final_state   [B, H, P, N] fp32, or NULL; may alias initial_state
+ *   y   [B, L, H, P] fp32 (written)
+ *   workspace: >= ssd_prefill_workspace_size(...) bytes, 256-byte aligned,
+ *              contents on entry ignored, clobbered on exit.
+ * The result does not depend on `chunk` beyond rounding.  seqlen == 0 only
+ * copies the initial state (or zeros) into final_state.
+ */
+int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm,
+                const void *Cm, const float *D, const float *initial_state,
+                float *final_state, float *y, ssd_dtype_t in_dtype, int batch,
+                int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                int chunk, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One decode token for every (b, h), fused: the state is read once,
+ * decayed, updated with the token's input and written back in place, and
+ * the output is read off the updated state.
+ *
+ *   state [B, H, P, N] fp32 (in/out)   x [B, H, P] in_dtype   dt [B, H] in_dtype
+ *   A [H] fp32   Bm, Cm [B, G, N] in_dtype   D [H] fp32 or NULL   y [B, H, P] fp32
+ */
+int ssd_step(float *state, const void *x, const void *dt, const float *A,
+             const void *Bm, const void *Cm, const float *D, float *y,
+             ssd_dtype_t in_dtype, int batch, int nheads, int headdim, int dstate,
+             int ngroups, void *hip_stream);
+
+/* ---- Stage entry points (the four kernels ssd_prefill runs, in order) ---- */
+
+/*
+ * Step-0: per-chunk inclusive cumulative sum of dt*A (wavefront prefix scan).
+ *   dt [B, L, H] in_dtype; A [H] fp32
+ *   dA_cum [B, H, nc, Q] fp32 (written): sum_{k<=i} dt[cQ+k]*A[h], held
+ *          constant past seqlen; dt_c [B, H, nc, Q] fp32 (written): dt, 0 past seqlen.
+ */
+int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c,
+                     ssd_dtype_t in_dtype, int batch, int seqlen, int nheads,
+                     int chunk, void *hip_stream);
+
+/*
+ * Step-2: chunk states, the state each chunk alone leaves from a zero start:
+ *   states[b,h,c] = sum_j exp(dA_cum[c][Q-1] - dA_cum[c][j]) * dt_c[c][j] * x_j B_j^T
+ *   x [B, L, H, P], Bm [B, L, G, N] in_dtype; dA_cum, dt_c as written by
+ *   ssd_chunk_cumsum; states [B, H, nc, P, N] fp32 (written).
+ */
+int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const float *dt_c,
+                    float *states, ssd_dtype_t in_dtype, int batch, int seqlen,
+                    int nheads, int headdim, int dstate, int ngroups, int chunk,
+                    void *hip_stream);
+
+/*
+ * Step-3: inter-chunk state passing, sequential over chunks, in place:
+ *   run = initial_state (or 0); for c: tmp = states[c]; states[c] = run;
+ *   run = exp(dA_cum[c][Q-1]) * run + tmp.   final_state = run (if non-NULL;
+ *   may alias initial_state).  On return states[c] holds the state entering chunk c.
+ */
+int ssd_state_passing(float *states, const float *dA_cum, const float *initial_state,
+                      float *final_state, int batch, int nheads, int headdim, int dstate,
+                      int nchunks, int chunk, void *hip_stream);
+
+/*
+ * Step-1 + Step-4 + skip: the output of every chunk,
+ *   y_i = sum_{j<=i} (C_i . B_j) exp(dA_cum[i] - dA_cum[j]) dt_c[j] x_j      (intra-chunk)
+ *       + exp(dA_cum[i]) * H_enter C_i  + D_h x_i                           (off-diagonal, skip)
+ *   h_enter [B, H, nc, P, N] fp32: entering states (ssd_state_passing output).
+ *   y [B, L, H, P] fp32 (written).
+ */
+int ssd_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *dA_cum,
+                   const float *dt_c, const float *h_enter, const float *D, float *y,
+                   ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
+                   int dstate, int ngroups, int chunk, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_SCAN_AMD_SSD_H */

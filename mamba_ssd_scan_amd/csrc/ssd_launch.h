@@ -1,0 +1,30 @@
+// ssd_launch.h -- host-side launchers of the gfx950 SSD kernels.
+// Shapes are validated by the C ABI layer before any of these is called;
+// each launcher only picks the template instance and the grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ssd {
+
+struct Dims {
+    int B, L, H, P, N, G, Q, nc;  // batch, seqlen, heads, headdim, dstate, groups, chunk, chunks
+    bool bf16;                    // input storage: bf16 (true) or fp32
+};
+
+hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, float *dtc,
+                               const Dims &d, hipStream_t s);
+hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
+                              float *states, const Dims &d, hipStream_t s);
+hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
+                                const Dims &d, hipStream_t s);
+hipError_t launch_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *acum,
+                             const float *dtc, const float *h_enter, const float *D, float *y,
+                             const Dims &d, hipStream_t s);
+// dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
+hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
+hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
+                       const void *Cm, const float *D, float *y, const Dims &d, hipStream_t s);
+
+}  // namespace ssd

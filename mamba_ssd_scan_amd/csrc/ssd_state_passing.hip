@@ -1,0 +1,93 @@
+// ssd_state_passing.hip -- Step-3: inter-chunk recurrence of the state.
+//
+// The state entering chunk c+1 is the state entering chunk c, decayed by the
+// chunk's total decay exp(dA_cum[c][Q-1]), plus the chunk's own state S_c
+// ("Mamba-Family State-Space Model Kernels on a Programmable CGLA", Sec.
+// III-A and IV-C: Step-3 is sequential across chunks; A_c is diagonal, so
+// the per-chunk update of the [P, N] state is a per-head scalar scale plus an
+// add, not a dense matrix-vector product).
+//
+// HBM-bound: each thread owns four consecutive fp32 state elements of one
+// (b, h) and walks the chunks in order, reading S_c and writing the entering
+// state in place (16-byte coalesced accesses).  The loads of the next kUnroll
+// chunks are issued before any of their results is needed, so many loads are
+// in flight per thread while the dependent scale-add chain runs.
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+constexpr int kPassThreads = 64;
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
+    float *__restrict__ states, const float *__restrict__ acum, const float *init,
+    float *fin, int H, int nc, int Q, int PN4)
+{
+    const int e = blockIdx.x * kPassThreads + threadIdx.x;  // float4 index inside one [P, N] state
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (e >= PN4) return;
+    const size_t bh = (size_t)b * H + h;
+    float4 run = init ? reinterpret_cast<const float4 *>(init)[bh * PN4 + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 *st = reinterpret_cast<float4 *>(states) + bh * nc * (size_t)PN4 + e;
+    const float *ac = acum + bh * nc * (size_t)Q + (Q - 1);
+
+    int c = 0;
+    for (; c + kUnroll <= nc; c += kUnroll) {
+        float4 s[kUnroll];
+        float dec[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            s[k] = st[(size_t)(c + k) * PN4];
+            dec[k] = ac[(size_t)(c + k) * Q];
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            st[(size_t)(c + k) * PN4] = run;
+            const float r = exp_fast(dec[k]);
+            run.x = fmaf(r, run.x, s[k].x);
+            run.y = fmaf(r, run.y, s[k].y);
+            run.z = fmaf(r, run.z, s[k].z);
+            run.w = fmaf(r, run.w, s[k].w);
+        }
+    }
+    for (; c < nc; ++c) {
+        const float4 s = st[(size_t)c * PN4];
+        st[(size_t)c * PN4] = run;
+        const float r = exp_fast(ac[(size_t)c * Q]);
+        run.x = fmaf(r, run.x, s.x);
+        run.y = fmaf(r, run.y, s.y);
+        run.z = fmaf(r, run.z, s.z);
+        run.w = fmaf(r, run.w, s.w);
+    }
+    if (fin) reinterpret_cast<float4 *>(fin)[bh * PN4 + e] = run;
+}
+
+hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
+                                const Dims &d, hipStream_t s)
+{
+    const int PN4 = d.P * d.N / 4;
+    dim3 grid((PN4 + kPassThreads - 1) / kPassThreads, d.H, d.B);
+    state_passing_kernel<<<grid, kPassThreads, 0, s>>>(states, acum, init, fin, d.H, d.nc, d.Q, PN4);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_state_kernel(float *__restrict__ dst,
+                                                         const float *__restrict__ src, size_t n4)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    reinterpret_cast<float4 *>(dst)[i] =
+        src ? reinterpret_cast<const float4 *>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s)
+{
+    const size_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    if (dst == src) return hipSuccess;
+    fill_state_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, s>>>(dst, src, n4);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,101 @@
+// ssd_step.hip -- fused single-token decode update of the recurrent state.
+//
+// For every (b, h): H <- exp(dt A_h) H + (dt x) B^T, then y = H C + D_h x,
+// with the [P, N] fp32 state read once and written once in place ("Compiler-
+// First State Space Duality and Portable O(1) Autoregressive Caching for
+// Inference", abstract: cached decode carries the state across tokens, cost
+// independent of the sequence length; "Mamba-Family State-Space Model Kernels
+// on a Programmable CGLA", Sec. III-A: the recurrent-state update).
+//
+// HBM-bound (0.5 flop per byte).  One 256-thread workgroup per (b, h).  A row
+// p of the state (N floats) is covered by N/4 adjacent lanes holding one
+// float4 each, so every access is a 16-byte coalesced load or store; all of
+// a thread's rows are loaded before any is updated so the loads are in
+// flight together.  The dot product with C is reduced across the row's lanes
+// with cross-lane shuffles.
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+template <typename TIn, int N>
+__global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, const TIn *__restrict__ x,
+                                                   const TIn *__restrict__ dt, const float *__restrict__ A,
+                                                   const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
+                                                   const float *__restrict__ D, float *__restrict__ y,
+                                                   int H, int G, int P)
+{
+    constexpr int NQ = N / 4;          // lanes per state row (8, 16 or 32)
+    constexpr int RP = 256 / NQ;       // rows per pass of the workgroup
+    constexpr int MAXIT = 128 / RP > 0 ? 128 / RP : 1;  // P <= 128
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H;
+    const int g = h / (H / G);
+    const int q = threadIdx.x % NQ;
+    const int r0 = threadIdx.x / NQ;
+
+    const float dtv = load_in(dt + bh);
+    const float r = exp_fast(dtv * A[h]);
+    const float Dh = D ? D[h] : 0.f;
+    float bv[4], cv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bv[k] = load_in(Bm + ((size_t)b * G + g) * N + 4 * q + k);
+        cv[k] = load_in(Cm + ((size_t)b * G + g) * N + 4 * q + k);
+    }
+    float4 *st = reinterpret_cast<float4 *>(state) + (size_t)bh * P * NQ;
+
+    float4 s[MAXIT];
+    float xs[MAXIT];
+#pragma unroll
+    for (int k = 0; k < MAXIT; ++k) {
+        const int p = r0 + k * RP;
+        if (p < P) {
+            s[k] = st[p * NQ + q];
+            xs[k] = load_in(x + (size_t)bh * P + p);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < MAXIT; ++k) {
+        const int p = r0 + k * RP;
+        if (p < P) {  // uniform across the NQ lanes of a row
+            const float u = dtv * xs[k];
+            float4 v = s[k];
+            v.x = fmaf(r, v.x, u * bv[0]);
+            v.y = fmaf(r, v.y, u * bv[1]);
+            v.z = fmaf(r, v.z, u * bv[2]);
+            v.w = fmaf(r, v.w, u * bv[3]);
+            st[p * NQ + q] = v;
+            float part = v.x * cv[0] + v.y * cv[1] + v.z * cv[2] + v.w * cv[3];
+#pragma unroll
+            for (int off = NQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+            if (q == 0) y[(size_t)bh * P + p] = part + Dh * xs[k];
+        }
+    }
+}
+
+template <typename TIn>
+static hipError_t launch_step_t(float *state, const void *x, const void *dt, const float *A,
+                                const void *Bm, const void *Cm, const float *D, float *y,
+                                const Dims &d, hipStream_t s)
+{
+    const dim3 grid(d.B * d.H);
+    const TIn *xx = static_cast<const TIn *>(x), *dd = static_cast<const TIn *>(dt);
+    const TIn *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
+    switch (d.N) {
+    case 32: step_kernel<TIn, 32><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
+    case 64: step_kernel<TIn, 64><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
+    case 128: step_kernel<TIn, 128><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
+                       const void *Cm, const float *D, float *y, const Dims &d, hipStream_t s)
+{
+    return d.bf16 ? launch_step_t<bf16_t>(state, x, dt, A, Bm, Cm, D, y, d, s)
+                  : launch_step_t<float>(state, x, dt, A, Bm, Cm, D, y, d, s);
+}
+
+}  // namespace ssd

@@ -1,0 +1,234 @@
+"""Python binding of the C ABI in ``include/ssd.h`` (``libssd.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  The
+library must have been built (``python -m mamba_ssd_scan_amd.build`` or
+``__graft_entry__.build()``); importing a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = 0, -1, -2, -3, -4
+
+# Every symbol include/ssd.h declares.
+EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
+           "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan")
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                           "(python -m mamba_ssd_scan_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.ssd_status_string.argtypes = [i]
+    L.ssd_status_string.restype = ctypes.c_char_p
+    L.ssd_version.argtypes = []
+    L.ssd_version.restype = i
+    L.ssd_prefill_workspace_size.argtypes = [i] * 7
+    L.ssd_prefill_workspace_size.restype = sz
+    L.ssd_prefill.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
+    L.ssd_prefill.restype = i
+    L.ssd_step.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    L.ssd_step.restype = i
+    L.ssd_chunk_cumsum.argtypes = [vp] * 4 + [i] * 5 + [vp]
+    L.ssd_chunk_cumsum.restype = i
+    L.ssd_chunk_state.argtypes = [vp] * 5 + [i] * 8 + [vp]
+    L.ssd_chunk_state.restype = i
+    L.ssd_state_passing.argtypes = [vp] * 4 + [i] * 6 + [vp]
+    L.ssd_state_passing.restype = i
+    L.ssd_chunk_scan.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    L.ssd_chunk_scan.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().ssd_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SSD_OK:
+        raise SsdError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def _f32(*ts):
+    torch = _torch()
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("A, D, states, workspace views and outputs must be float32")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def nchunks(seqlen: int, chunk: int) -> int:
+    return -(-seqlen // chunk)
+
+
+def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk) -> int:
+    n = lib().ssd_prefill_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+    if n == 0 and seqlen > 0:
+        raise SsdError(SSD_ERR_UNSUPPORTED, "ssd_prefill_workspace_size")
+    return n
+
+
+def alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, device="cuda"):
+    torch = _torch()
+    n = workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=None, final_state="new",
+            workspace=None, stream=None) -> Tuple[object, Optional[object]]:
+    """Chunked SSD prefill.  Returns (y [B,L,H,P] fp32, final_state [B,H,P,N] fp32 or None).
+
+    ``final_state``: "new" allocates it, None skips it, or pass a tensor
+    (which may be ``initial_state`` itself for an in-place update).
+    """
+    torch = _torch()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    code = _dtype_code(x)
+    for t in (dt, B, C):
+        if t.dtype != x.dtype:
+            raise TypeError("x, dt, B and C must share one dtype")
+    _dev(x, dt, A, B, C, D, initial_state, y, workspace)
+    _f32(A, D, initial_state, y)
+    if y is None:
+        y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
+    if isinstance(final_state, str):
+        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+    _dev(final_state)
+    _f32(final_state)
+    if workspace is None:
+        workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().ssd_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+                             _ptr(final_state), _ptr(y), code, batch, seqlen, nheads, headdim, dstate, ngroups,
+                             chunk, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill")
+    return y, final_state
+
+
+def step(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
+    """One fused decode token; ``state`` [B,H,P,N] fp32 is updated in place.  Returns y [B,H,P] fp32."""
+    torch = _torch()
+    batch, nheads, headdim, dstate = state.shape
+    ngroups = B.shape[1]
+    code = _dtype_code(x)
+    _dev(state, x, dt, A, B, C, D, y)
+    _f32(state, A, D, y)
+    if y is None:
+        y = torch.empty((batch, nheads, headdim), dtype=torch.float32, device=x.device)
+    _check(lib().ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), code,
+                          batch, nheads, headdim, dstate, ngroups, _stream(stream)), "ssd_step")
+    return y
+
+
+# ---- stage entry points (for unit tests and per-kernel timing)
+
+
+def chunk_cumsum(dt, A, *, chunk: int, acum=None, dtc=None, stream=None):
+    torch = _torch()
+    batch, seqlen, nheads = dt.shape
+    nc = nchunks(seqlen, chunk)
+    _dev(dt, A, acum, dtc)
+    if acum is None:
+        acum = torch.empty((batch, nheads, nc, chunk), dtype=torch.float32, device=dt.device)
+    if dtc is None:
+        dtc = torch.empty((batch, nheads, nc, chunk), dtype=torch.float32, device=dt.device)
+    _check(lib().ssd_chunk_cumsum(_ptr(dt), _ptr(A), _ptr(acum), _ptr(dtc), _dtype_code(dt), batch, seqlen, nheads,
+                                  chunk, _stream(stream)), "ssd_chunk_cumsum")
+    return acum, dtc
+
+
+def chunk_state(x, B, acum, dtc, *, chunk: int, states=None, stream=None):
+    torch = _torch()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    nc = nchunks(seqlen, chunk)
+    _dev(x, B, acum, dtc, states)
+    if states is None:
+        states = torch.empty((batch, nheads, nc, headdim, dstate), dtype=torch.float32, device=x.device)
+    _check(lib().ssd_chunk_state(_ptr(x), _ptr(B), _ptr(acum), _ptr(dtc), _ptr(states), _dtype_code(x), batch, seqlen,
+                                 nheads, headdim, dstate, ngroups, chunk, _stream(stream)), "ssd_chunk_state")
+    return states
+
+
+def state_passing(states, acum, initial_state=None, *, chunk: int, final_state="new", stream=None):
+    """In place: ``states`` [B,H,nc,P,N] becomes the entering states.  Returns final_state."""
+    torch = _torch()
+    batch, nheads, nc, headdim, dstate = states.shape
+    _dev(states, acum, initial_state)
+    if isinstance(final_state, str):
+        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=states.device)
+    _check(lib().ssd_state_passing(_ptr(states), _ptr(acum), _ptr(initial_state), _ptr(final_state), batch, nheads,
+                                   headdim, dstate, nc, chunk, _stream(stream)), "ssd_state_passing")
+    return final_state
+
+
+def chunk_scan(x, B, C, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stream=None):
+    torch = _torch()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    _dev(x, B, C, acum, dtc, h_enter, D, y)
+    if y is None:
+        y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
+    _check(lib().ssd_chunk_scan(_ptr(x), _ptr(B), _ptr(C), _ptr(acum), _ptr(dtc), _ptr(h_enter), _ptr(D), _ptr(y),
+                                _dtype_code(x), batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                _stream(stream)), "ssd_chunk_scan")
+    return y

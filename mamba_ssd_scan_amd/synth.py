@@ -212,3 +212,18 @@ def decode_inputs(shape: DecodeShape, seed: int, steps: Optional[int] = None) ->
     state = (0.1 * rng.standard_normal((s.batch, s.nheads, s.headdim, s.dstate), dtype=f)).astype(f)
     return dict(x=_store(x, s.dtype), dt=_store(dt, s.dtype), A=A, B=_store(Bm, s.dtype),
                 C=_store(Cm, s.dtype), D=D, state=state, dtype=s.dtype)
+
+
+def to_torch(a: np.ndarray, dtype: str, device="cuda"):
+    """Copy an fp32 array holding exact values to a torch tensor of ``dtype``.
+
+    ``dtype`` "bf16" moves the bf16 bit patterns (no re-rounding), "f32" the
+    fp32 values.
+    """
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits(a).view(np.int16)
+        return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+    raise ValueError(dtype)

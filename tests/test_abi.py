@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments before any HIP call (no kernel is launched)."""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+from mamba_ssd_scan_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+F, BF = ssd.SSD_F32, ssd.SSD_BF16
+INV, UNS, WS = ssd.SSD_ERR_INVALID_ARG, ssd.SSD_ERR_UNSUPPORTED, ssd.SSD_ERR_WORKSPACE
+P0 = 0x100000  # fake, aligned "device" addresses: only used on calls that must be rejected
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ssd.lib()
+    names = declared_functions()
+    assert set(names) == set(ssd.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    for s in (0, -1, -2, -3, -4, 99):
+        assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
+    assert ssd.lib().ssd_version() >> 16 == 1
+
+
+def test_workspace_size_formula():
+    L = ssd.lib()
+    al = lambda v: (v + 255) // 256 * 256
+    for (b, l, h, p, n, g, q) in [(1, 4096, 24, 64, 128, 1, 256), (8, 2048, 32, 64, 64, 1, 64),
+                                  (2, 1000, 6, 32, 128, 3, 128), (1, 1, 1, 32, 32, 1, 16)]:
+        nc = -(-l // q)
+        bhq = b * h * nc * q * 4
+        want = al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n)
+        assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 1, 48) == 0   # bad chunk
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 48, 128, 1, 64) == 0   # bad headdim
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 5, 64) == 0   # H % G
+
+
+def _prefill(**kw):
+    a = dict(x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, h0=None, hT=None, y=P0, dtype=BF, batch=1, seqlen=300,
+             nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, ws=P0, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return ssd.lib().ssd_prefill(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["h0"], a["hT"], a["y"],
+                                 a["dtype"], a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["dstate"],
+                                 a["ngroups"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), INV), (dict(batch=0), INV), (dict(seqlen=-1), INV), (dict(nheads=0), INV),
+    (dict(nheads=6, ngroups=4), INV), (dict(headdim=48), UNS), (dict(headdim=256), UNS), (dict(dstate=16), UNS),
+    (dict(dstate=256), UNS), (dict(chunk=48), UNS), (dict(chunk=512), UNS), (dict(chunk=0), INV),
+    (dict(batch=70000), UNS), (dict(x=None), INV), (dict(dt=None), INV), (dict(A=None), INV), (dict(B=None), INV),
+    (dict(C=None), INV), (dict(y=None), INV), (dict(x=P0 + 2), INV), (dict(B=P0 + 8), INV), (dict(C=P0 + 4), INV),
+    (dict(y=P0 + 4), INV), (dict(dt=P0 + 1), INV), (dict(h0=P0 + 4), INV), (dict(hT=P0 + 8), INV),
+    (dict(D=P0 + 2), INV), (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=P0 + 128), WS),
+])
+def test_prefill_rejects_before_launch(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_step_rejects_before_launch():
+    L = ssd.lib()
+    def st(**kw):
+        a = dict(state=P0, x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, y=P0, dtype=BF, batch=2, nheads=4, headdim=64,
+                 dstate=128, ngroups=1, stream=None)
+        a.update(kw)
+        return L.ssd_step(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["y"], a["dtype"], a["batch"],
+                          a["nheads"], a["headdim"], a["dstate"], a["ngroups"], a["stream"])
+    assert st(state=None) == INV
+    assert st(state=P0 + 4) == INV
+    assert st(x=None) == INV
+    assert st(y=None) == INV
+    assert st(dtype=3) == INV
+    assert st(headdim=40) == UNS
+    assert st(dstate=48) == UNS
+    assert st(nheads=3, ngroups=2) == INV
+    assert st(batch=0) == INV
+    assert st(x=P0 + 1) == INV
+
+
+def test_stage_entry_points_reject_before_launch():
+    L = ssd.lib()
+    assert L.ssd_chunk_cumsum(None, P0, P0, P0, BF, 1, 100, 4, 64, None) == INV
+    assert L.ssd_chunk_cumsum(P0, P0, P0, P0, BF, 1, 100, 4, 100, None) == UNS
+    assert L.ssd_chunk_cumsum(P0, P0, P0 + 4, P0, BF, 1, 100, 4, 64, None) == INV
+    assert L.ssd_chunk_state(P0, P0, P0, P0, None, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_state(P0, P0, P0, P0, P0, BF, 1, 100, 4, 64, 96, 1, 64, None) == UNS
+    assert L.ssd_state_passing(None, P0, None, None, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_state_passing(P0, P0, None, None, 1, 4, 64, 64, -1, 64, None) == INV
+    assert L.ssd_state_passing(P0, P0, P0 + 4, None, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, None, None, P0, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0 + 4, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0, F, 1, 100, 4, 64, 64, 3, 64, None) == INV
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle and has no CPU compute path."""
+    pkg = os.path.join(ROOT, "mamba_ssd_scan_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("Oracle", "").lower() or f == "synth.py", f
