@@ -82,25 +82,38 @@ def decode_bytes_per_step(s: synth.DecodeShape) -> int:
 
 
 def source_hash(kernel: str) -> str:
-    path = os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", KERNEL_SOURCES[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel's source file and the shared device header."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "ssd_common.h"):
+        h.update(open(os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_summary(path: str) -> dict:
+    """`key: value` lines of a profile summary (other lines ignored)."""
+    out = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
 
 
 def counter_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, or None.
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
     The summary is used only if it was taken on the current kernel source.
     """
-    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.json")
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     try:
-        d = json.load(open(path))
-    except (OSError, ValueError):
+        d = read_summary(path)
+        if d.get("source_sha256_16") != source_hash(kernel):
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
         return None
-    if d.get("source_sha256_16") != source_hash(kernel):
-        return None
-    return d.get("hbm_bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------- GPU timing
@@ -117,20 +130,39 @@ class Flusher:
 
 
 def time_launches(torch, fn, n, flush=None, before=None):
-    """Mean and min duration (us) of ``fn`` over n launches, HIP events on the current stream."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    """Duration (us) of ``fn``: mean and min over n launches, from HIP events on the current stream.
+
+    With ``flush``, every launch is preceded by the cache eviction.  A pair of
+    events costs a few microseconds of dispatch and completion signalling, so
+    the events bracket [eviction + fn] and, on interleaved iterations,
+    [eviction] alone; the difference of the means is fn's duration with the
+    event overhead cancelled (the eviction itself is outside the result).
+    """
     stream = torch.cuda.current_stream()
-    for a, b in evs:
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    with_fn, alone = [], []
+    for _ in range(n):
         if before is not None:
             before()
+        a, b = ev(), ev()
+        a.record(stream)
         if flush is not None:
             flush()
-        a.record(stream)
         fn()
         b.record(stream)
+        with_fn.append((a, b))
+        if flush is not None:
+            c, d = ev(), ev()
+            c.record(stream)
+            flush()
+            d.record(stream)
+            alone.append((c, d))
     torch.cuda.synchronize()
-    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-    return float(t.mean()), float(t.min())
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in with_fn])
+    if flush is None:
+        return float(t.mean()), float(t.min())
+    f = np.array([c.elapsed_time(d) * 1e3 for c, d in alone])
+    return float(t.mean() - f.mean()), float(t.min() - f.mean())
 
 
 def prefill_buffers(torch, s, inp):
@@ -235,7 +267,9 @@ def bench_decode(torch, steps, flush):
 
     us_cold, _ = time_launches(torch, one, min(64, steps), flush=flush)
     nbytes = decode_bytes_per_step(s)
+    traffic = counter_traffic("step_kernel", synth.WORKLOAD_NAMES[DECODE_WORKLOAD])
     return {
+        "counter_traffic_bytes_per_step": traffic,
         "workload": synth.WORKLOAD_NAMES[DECODE_WORKLOAD], "steps": steps,
         "us_per_step": us_loop, "tokens_per_s": s.batch / (us_loop * 1e-6),
         "alg_bytes_per_step": nbytes, "gbps": nbytes / (us_loop * 1e-6) / 1e9,

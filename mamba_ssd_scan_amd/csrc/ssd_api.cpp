@@ -31,6 +31,11 @@ int check_shape(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     if (need_chunk && !supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
     if (batch > 65535 || nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y/z limits
     if ((long long)batch * nheads > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+    // One chunk of x or B/C is addressed with 32-bit byte offsets inside the kernels.
+    if (need_chunk && (long long)chunk * 4 * ((long long)nheads * headdim > (long long)ngroups * dstate
+                                                  ? (long long)nheads * headdim
+                                                  : (long long)ngroups * dstate) >= 0x7fffffffLL)
+        return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -193,8 +198,7 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, c
     float *states = reinterpret_cast<float *>(ws + w.states);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 
-    SSD_TRY(hip_status(ssd::launch_chunk_cumsum(dt, A, acum, dtc, d, s)));
-    SSD_TRY(hip_status(ssd::launch_chunk_state(x, Bm, acum, dtc, states, d, s)));
+    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state(x, Bm, dt, A, acum, dtc, states, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Bm, Cm, acum, dtc, states, D, y, d, s));
 }

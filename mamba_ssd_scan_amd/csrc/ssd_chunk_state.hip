@@ -7,120 +7,229 @@
 // ("Mamba-Family State-Space Model Kernels on a Programmable CGLA", Sec.
 // III-A: the recurrent state links the chunks; Step-3 consumes these states).
 //
-// One 256-thread workgroup (4 wavefronts) per (b, h, c).  The chunk is
-// streamed through LDS in blocks of JB tokens, stored transposed ([P][JB]
-// and [N][JB]) so that each lane reads its reduction slots as one 16-byte LDS
-// load.  The decay weight is folded into X while staging; the weighted X is
-// a computed operand, so with bf16 inputs both operands go to the matrix
-// cores as fp16 (B converts exactly), accumulating in fp32.  Each wavefront
-// owns every fourth 16x16 output tile.
+// One 256-thread workgroup (4 wavefronts) per (b, h, c); each wavefront owns
+// every fourth 16x16 output tile.  The chunk is streamed through LDS in
+// blocks of JB tokens.  With bf16 inputs both tiles are kept row-major
+// ([token][channel], fp16) exactly as they arrive from memory -- every thread
+// converts and stores 16 contiguous bytes -- and the matrix-core operands,
+// whose reduction index is the token, are read with the transposing LDS
+// read.  The decay weight is folded into X on the way in; the weighted X is a
+// computed operand, so both operands go to the matrix cores as fp16 (B
+// converts exactly), accumulating in fp32.  (fp32 inputs keep transposed fp32
+// tiles for the 16x16x4 fp32 path.)  Two blocks of global loads are kept in
+// flight in registers ahead of the block being contracted; LDS is
+// double-buffered with one barrier per block.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-template <typename TIn, int P, int N>
+// Step-0 fused in (FUSE_CUMSUM): one wavefront scans this chunk's dt*A (as the
+// stand-alone cumulative-decay kernel does) and writes dA_cum / dt_c for the
+// later stages, instead of reading them; the other wavefronts start loading.
+template <typename TIn, int P, int N, bool FUSE_CUMSUM>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict__ x,
                                                           const TIn *__restrict__ Bm,
-                                                          const float *__restrict__ acum,
-                                                          const float *__restrict__ dtc,
+                                                          const TIn *__restrict__ dt,
+                                                          const float *__restrict__ A,
+                                                          float *__restrict__ acum,
+                                                          float *__restrict__ dtc,
                                                           float *__restrict__ states, int L, int H,
                                                           int G, int Q, int nc)
 {
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
     constexpr bool F32 = Tr::kF32;
-    constexpr int JB = F32 ? 32 : 64;       // tokens per staged block
-    constexpr int LDX = JB + (F32 ? 4 : 8); // row length of the transposed tiles
+    constexpr int JB = F32 ? 32 : 64;                   // tokens per staged block
+    // bf16 inputs: row-major fp16 tiles; a pitch of (width + 16) halves puts the 16
+    // rows one transposing read touches on distinct bank groups.
+    constexpr int LDXR = P + 16, LDBR = N + 16;
+    constexpr int LDT = JB + 4;                         // fp32 inputs: transposed tiles
+    constexpr int XSZ = F32 ? P * LDT : JB * LDXR;
+    constexpr int BSZ = F32 ? N * LDT : JB * LDBR;
     constexpr int TN = N / 16, NT = (P / 16) * TN;
-    constexpr int TPW = (NT + 3) / 4;       // output tiles per wavefront
-    __shared__ op_t xs[P * LDX];            // (X * w)^T
-    __shared__ op_t bs[N * LDX];            // B^T
+    constexpr int TPW = (NT + 3) / 4;                   // output tiles per wavefront
+    constexpr int XU = (JB / 2) * (P / 8), XPT = (XU + 255) / 256;  // two tokens x 8 channels
+    constexpr int BU = (JB / 2) * (N / 8), BPT = (BU + 255) / 256;
+    __shared__ op_t xs[2][XSZ];
+    __shared__ op_t bs[2][BSZ];
+    __shared__ float ws[256];                           // decay weights w_j of the chunk
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const size_t bhc = ((size_t)b * H + h) * nc + c;
-    const float *ac = acum + bhc * Q;
-    const float *dd = dtc + bhc * Q;
-    const float aend = ac[Q - 1];
     const long tc = (long)c * Q;
+    const int nblk = (Q + JB - 1) / JB;
+
+    struct Stage {
+        Raw8<TIn> x[XPT][2], b[BPT][2];
+    };
+    // Buffer resources over this chunk's valid rows of X and B: loads of rows past
+    // the chunk or the sequence return zeros.
+    const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P, (uint32_t)(((vrows - 1) * H * P + P) * sizeof(TIn)));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(Bm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vrows - 1) * G * N + N) * sizeof(TIn)));
+
+    auto prefetch = [&](Stage &st, int jbk) {
+        const int j0 = jbk * JB;
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int u = tid + k * 256;
+            if (u < XU) {
+                const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) st.x[k][e].load(rx, (uint32_t)((j + e) * H * P + 8 * pg));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int u = tid + k * 256;
+            if (u < BU) {
+                const int jp = u / (N / 8), ng = u % (N / 8), j = j0 + 2 * jp;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) st.b[k][e].load(rb, (uint32_t)((j + e) * G * N + 8 * ng));
+            }
+        }
+    };
+    auto commit = [&](const Stage &st, int buf, int jbk) {
+        const int j0 = jbk * JB;
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int u = tid + k * 256;
+            if (u < XU) {
+                const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
+                const float w0 = j < Q ? ws[j] : 0.f, w1 = j + 1 < Q ? ws[j + 1] : 0.f;
+                if constexpr (F32) {
+                    float v0[8], v1[8];
+                    st.x[k][0].to_f32(v0);
+                    st.x[k][1].to_f32(v1);
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) store_pair(&xs[buf][(8 * pg + kk) * LDT + 2 * jp], v0[kk] * w0, v1[kk] * w1);
+                } else {
+                    *reinterpret_cast<uint4 *>(&xs[buf][(2 * jp) * LDXR + 8 * pg]) = raw8_to_f16x8(st.x[k][0], w0);
+                    *reinterpret_cast<uint4 *>(&xs[buf][(2 * jp + 1) * LDXR + 8 * pg]) = raw8_to_f16x8(st.x[k][1], w1);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int u = tid + k * 256;
+            if (u < BU) {
+                const int jp = u / (N / 8), ng = u % (N / 8);
+                if constexpr (F32) {
+                    float v0[8], v1[8];
+                    st.b[k][0].to_f32(v0);
+                    st.b[k][1].to_f32(v1);
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) store_pair(&bs[buf][(8 * ng + kk) * LDT + 2 * jp], v0[kk], v1[kk]);
+                } else {
+                    *reinterpret_cast<uint4 *>(&bs[buf][(2 * jp) * LDBR + 8 * ng]) = raw8_to_f16x8(st.b[k][0]);
+                    *reinterpret_cast<uint4 *>(&bs[buf][(2 * jp + 1) * LDBR + 8 * ng]) = raw8_to_f16x8(st.b[k][1]);
+                }
+            }
+        }
+    };
 
     f32x4 acc[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) acc[k] = zero4();
 
-    for (int j0 = 0; j0 < Q; j0 += JB) {
-        // ---- stage (X * w)^T: one unit = two consecutive tokens x eight channels
-        constexpr int XG = P / 8;
-        for (int u = tid; u < (JB / 2) * XG; u += 256) {
-            const int jp = u / XG, pg = u % XG;
-            const int j = j0 + 2 * jp;
-            float v0[8], v1[8], w0 = 0.f, w1 = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v0[k] = v1[k] = 0.f;
-            if (j < Q && tc + j < L) {
-                load8(x + (((size_t)b * L + tc + j) * H + h) * P + 8 * pg, v0);
-                w0 = exp_fast(aend - ac[j]) * dd[j];
-            }
-            if (j + 1 < Q && tc + j + 1 < L) {
-                load8(x + (((size_t)b * L + tc + j + 1) * H + h) * P + 8 * pg, v1);
-                w1 = exp_fast(aend - ac[j + 1]) * dd[j + 1];
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                op_t *dst = &xs[(8 * pg + k) * LDX + 2 * jp];
-                if constexpr (F32) {
-                    *reinterpret_cast<float2 *>(dst) = make_float2(v0[k] * w0, v1[k] * w1);
-                } else {
-                    *reinterpret_cast<uint32_t *>(dst) = pack_f16x2(v0[k] * w0, v1[k] * w1);
-                }
-            }
-        }
-        // ---- stage B^T
-        constexpr int BG = N / 8;
-        for (int u = tid; u < (JB / 2) * BG; u += 256) {
-            const int jp = u / BG, ng = u % BG;
-            const int j = j0 + 2 * jp;
-            float v0[8], v1[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v0[k] = v1[k] = 0.f;
-            if (j < Q && tc + j < L) load8(Bm + (((size_t)b * L + tc + j) * G + g) * N + 8 * ng, v0);
-            if (j + 1 < Q && tc + j + 1 < L) load8(Bm + (((size_t)b * L + tc + j + 1) * G + g) * N + 8 * ng, v1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                op_t *dst = &bs[(8 * ng + k) * LDX + 2 * jp];
-                if constexpr (F32) {
-                    *reinterpret_cast<float2 *>(dst) = make_float2(v0[k], v1[k]);
-                } else {
-                    *reinterpret_cast<uint32_t *>(dst) = pack_f16x2(v0[k], v1[k]);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- contraction over this block's tokens, 32 at a time
-        for (int ks = 0; ks < JB && j0 + ks < Q; ks += 32) {
+    auto contract = [&](int buf, int jbk) {
+        for (int ks = 0; ks < JB && jbk * JB + ks < Q; ks += 32) {
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt) {
                 const int t = wave + 4 * tt;
                 if (t < NT) {
                     const int pt = t / TN, nt = t % TN;
-                    const op_t *xa = &xs[(pt * 16 + li) * LDX + ks];
-                    const op_t *ba = &bs[(nt * 16 + li) * LDX + ks];
                     if constexpr (F32) {
+                        const op_t *xa = &xs[buf][(pt * 16 + li) * LDT + ks];
+                        const op_t *ba = &bs[buf][(nt * 16 + li) * LDT + ks];
 #pragma unroll
                         for (int s = 0; s < 8; ++s) acc[tt] = mfma16x16x4_f32(xa[4 * s + lg], ba[4 * s + lg], acc[tt]);
                     } else {
-                        const f16x8 a = *reinterpret_cast<const f16x8 *>(xa + 8 * lg);
-                        const f16x8 bb = *reinterpret_cast<const f16x8 *>(ba + 8 * lg);
+                        // reduction slots of lane group lg: tokens ks + 4 lg + r and ks + 16 + 4 lg + r
+                        const int ox = tr16_offset(lane, ks, pt * 16, LDXR);
+                        const int ob = tr16_offset(lane, ks, nt * 16, LDBR);
+                        const f16x4 a0 = lds_read_tr16(&xs[buf][ox]);
+                        const f16x4 a1 = lds_read_tr16(&xs[buf][ox + 16 * LDXR]);
+                        const f16x4 b0 = lds_read_tr16(&bs[buf][ob]);
+                        const f16x4 b1 = lds_read_tr16(&bs[buf][ob + 16 * LDBR]);
+                        const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        const f16x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
                         acc[tt] = mfma16x16x32_f16(a, bb, acc[tt]);
                     }
                 }
             }
         }
-        __syncthreads();
+    };
+
+    // ---- prologue: blocks 0 and 1 in flight while the decay weights are formed
+    Stage s0, s1;
+    prefetch(s0, 0);
+    if (nblk > 1) prefetch(s1, 1);
+    if constexpr (FUSE_CUMSUM) {
+        if (wave == 0) {
+            // inclusive scan of a_t = dt_t * A_h over the chunk: Q/64 tokens per lane
+            // serially, then a wavefront scan of the lane totals
+            const int per = Q > 64 ? Q / 64 : 1;
+            const float Ah = A[h];
+            float part[4], dts[4], run = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = lane * per + k;
+                float d = 0.f;
+                if (k < per && i < Q && tc + i < L) d = load_in(dt + ((size_t)b * L + tc + i) * H + h);
+                dts[k] = d;
+                run += d * Ah;
+                part[k] = run;
+            }
+            float incl = run;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
+            }
+            float excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = 0.f;
+            const float aend = __shfl(incl, 63, 64);  // total over the chunk (padding adds 0)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = lane * per + k;
+                if (k < per && i < Q) {
+                    const float ac = excl + part[k];
+                    acum[bhc * Q + i] = ac;
+                    dtc[bhc * Q + i] = dts[k];
+                    ws[i] = exp_fast(aend - ac) * dts[k];
+                }
+            }
+        }
+    } else {
+        const float aend = acum[bhc * Q + Q - 1];
+        for (int j = tid; j < Q; j += 256) ws[j] = exp_fast(aend - acum[bhc * Q + j]) * dtc[bhc * Q + j];
+    }
+    __syncthreads();
+    commit(s0, 0, 0);
+    __syncthreads();
+
+    // ---- main loop, unrolled by two so that each register stage has a fixed name:
+    // block k is in LDS buffer k&1; the stage that held block k is refilled with block k+2.
+    for (int jbk = 0; jbk < nblk; jbk += 2) {
+        if (jbk + 2 < nblk) prefetch(s0, jbk + 2);
+        contract(0, jbk);
+        if (jbk + 1 < nblk) {
+            commit(s1, 1, jbk + 1);
+            __syncthreads();
+            if (jbk + 3 < nblk) prefetch(s1, jbk + 3);
+            contract(1, jbk + 1);
+            if (jbk + 2 < nblk) {
+                commit(s0, 0, jbk + 2);
+                __syncthreads();
+            }
+        }
     }
 
     // ---- write S_c [P][N]: lane holds rows p = 16 pt + 4 lg + r of column n = 16 nt + li
@@ -136,29 +245,29 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     }
 }
 
-template <typename TIn, int P>
-static hipError_t launch_cs_n(const void *x, const void *Bm, const float *acum, const float *dtc,
-                              float *states, const Dims &d, hipStream_t s)
+template <typename TIn, int P, bool FUSE>
+static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                              float *dtc, float *states, const Dims &d, hipStream_t s)
 {
     const dim3 grid(d.nc, d.H, d.B);
-    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm);
+    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt);
     switch (d.N) {
-    case 32: chunk_state_kernel<TIn, P, 32><<<grid, 256, 0, s>>>(xx, bb, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
-    case 64: chunk_state_kernel<TIn, P, 64><<<grid, 256, 0, s>>>(xx, bb, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
-    case 128: chunk_state_kernel<TIn, P, 128><<<grid, 256, 0, s>>>(xx, bb, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
+    case 32: chunk_state_kernel<TIn, P, 32, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
+    case 64: chunk_state_kernel<TIn, P, 64, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
+    case 128: chunk_state_kernel<TIn, P, 128, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename TIn>
-static hipError_t launch_cs_t(const void *x, const void *Bm, const float *acum, const float *dtc,
-                              float *states, const Dims &d, hipStream_t s)
+template <typename TIn, bool FUSE>
+static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                              float *dtc, float *states, const Dims &d, hipStream_t s)
 {
     switch (d.P) {
-    case 32: return launch_cs_n<TIn, 32>(x, Bm, acum, dtc, states, d, s);
-    case 64: return launch_cs_n<TIn, 64>(x, Bm, acum, dtc, states, d, s);
-    case 128: return launch_cs_n<TIn, 128>(x, Bm, acum, dtc, states, d, s);
+    case 32: return launch_cs_n<TIn, 32, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
+    case 64: return launch_cs_n<TIn, 64, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
+    case 128: return launch_cs_n<TIn, 128, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -166,8 +275,16 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const float *acum, 
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
                               float *states, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_cs_t<bf16_t>(x, Bm, acum, dtc, states, d, s)
-                  : launch_cs_t<float>(x, Bm, acum, dtc, states, d, s);
+    float *ac = const_cast<float *>(acum), *dc = const_cast<float *>(dtc);  // read-only in this mode
+    return d.bf16 ? launch_cs_t<bf16_t, false>(x, Bm, nullptr, nullptr, ac, dc, states, d, s)
+                  : launch_cs_t<float, false>(x, Bm, nullptr, nullptr, ac, dc, states, d, s);
+}
+
+hipError_t launch_cumsum_chunk_state(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                                     float *dtc, float *states, const Dims &d, hipStream_t s)
+{
+    return d.bf16 ? launch_cs_t<bf16_t, true>(x, Bm, dt, A, acum, dtc, states, d, s)
+                  : launch_cs_t<float, true>(x, Bm, dt, A, acum, dtc, states, d, s);
 }
 
 }  // namespace ssd

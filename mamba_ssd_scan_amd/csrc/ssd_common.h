@@ -97,4 +97,124 @@ template <> struct Traits<float> {
 __device__ __forceinline__ f16 to_op(float v, f16 *) { return static_cast<f16>(v); }
 __device__ __forceinline__ float to_op(float v, float *) { return v; }
 
+// Buffer resource over [base, base + bytes): raw buffer loads take 32-bit byte
+// offsets (one VGPR instead of a 64-bit address) and return zeros at or past
+// `bytes`, which zero-fills ragged chunk tails without branches.  The config
+// word is the gfx9-family raw-buffer setting (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Eight consecutive raw input elements held in registers between a global
+// load and the LDS write that consumes them (software prefetch).
+template <typename TIn> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    uint4 v;
+    __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+    // element offset `e` inside the buffer resource `r`
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e) { v = buf_load16(r, 2u * e); }
+    __device__ __forceinline__ void zero() { v = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void store(bf16_t *dst) const { *reinterpret_cast<uint4 *>(dst) = v; }
+    __device__ __forceinline__ void to_f32(float f[8]) const
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = __uint_as_float(w[k] << 16);
+            f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p)
+    {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e)
+    {
+        a = __builtin_bit_cast(float4, buf_load16(r, 4u * e));
+        b = __builtin_bit_cast(float4, buf_load16(r, 4u * e + 16u));
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void store(float *dst) const
+    {
+        reinterpret_cast<float4 *>(dst)[0] = a;
+        reinterpret_cast<float4 *>(dst)[1] = b;
+    }
+    __device__ __forceinline__ void to_f32(float f[8]) const
+    {
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+};
+
+// Store two fp32 values as an adjacent pair of operand elements (4 or 8 bytes).
+__device__ __forceinline__ void store_pair(f16 *dst, float lo, float hi)
+{
+    *reinterpret_cast<uint32_t *>(dst) = pack_f16x2(lo, hi);
+}
+__device__ __forceinline__ void store_pair(float *dst, float lo, float hi)
+{
+    *reinterpret_cast<float2 *>(dst) = make_float2(lo, hi);
+}
+
+// Eight bf16 bit patterns (as stored) to an fp16 matrix-core operand.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 v)
+{
+    const uint4 u = __builtin_bit_cast(uint4, v);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    f16x8 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        h[2 * k] = static_cast<f16>(__uint_as_float(w[k] << 16));
+        h[2 * k + 1] = static_cast<f16>(__uint_as_float(w[k] & 0xFFFF0000u));
+    }
+    return h;
+}
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives four b16 values: value r is element (i % 4) of the
+// four-element run addressed by lane 4r + i/4 of the same group.  If lane q
+// of group g addresses row k0 + 4g + q/4, column m0 + 4(q % 4) of a row-major
+// [k][m] tile, lane i therefore receives rows k0 + 4g + r of column m0 + i:
+// a matrix-core operand slice whose reduction index runs down the LDS rows,
+// read without storing the tile transposed.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ f16x4 lds_read_tr16(const f16 *p)
+{
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(f16x4, v);
+}
+
+// Address of this lane's run for lds_read_tr16 on a row-major tile of row
+// pitch `ld` elements: rows k0 + 4g + q/4 (g = lane / 16, q = lane % 16),
+// columns m0 + 4 (q % 4).
+__device__ __forceinline__ int tr16_offset(int lane, int k0, int m0, int ld)
+{
+    const int g = lane >> 4, q = lane & 15;
+    return (k0 + 4 * g + (q >> 2)) * ld + m0 + 4 * (q & 3);
+}
+
+// Eight raw inputs converted to fp16 and packed into 16 bytes (one LDS store).
+template <typename TIn>
+__device__ __forceinline__ uint4 raw8_to_f16x8(const Raw8<TIn> &r, float scale = 1.f)
+{
+    float f[8];
+    r.to_f32(f);
+    uint4 w;
+    w.x = pack_f16x2(f[0] * scale, f[1] * scale);
+    w.y = pack_f16x2(f[2] * scale, f[3] * scale);
+    w.z = pack_f16x2(f[4] * scale, f[5] * scale);
+    w.w = pack_f16x2(f[6] * scale, f[7] * scale);
+    return w;
+}
+
 }  // namespace ssd

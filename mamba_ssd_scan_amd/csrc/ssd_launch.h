@@ -17,6 +17,9 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, floa
                                const Dims &d, hipStream_t s);
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
                               float *states, const Dims &d, hipStream_t s);
+// Step-0 fused into Step-2: writes acum/dtc (same values as launch_chunk_cumsum) and states.
+hipError_t launch_cumsum_chunk_state(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                                     float *dtc, float *states, const Dims &d, hipStream_t s);
 hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
 hipError_t launch_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *acum,

@@ -18,7 +18,7 @@
 namespace ssd {
 
 constexpr int kPassThreads = 64;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
     float *__restrict__ states, const float *__restrict__ acum, const float *init,
