@@ -288,6 +288,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=PREFILL_WORKLOAD, choices=[0, 1, 2, 3],
+                    help="prefill workload timed as the step (default 1; the others are for comparison)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -308,8 +310,11 @@ def main():
     torch.cuda.set_device(0)
     ssd.lib()
     flush = Flusher(torch)
-    s = synth.WORKLOADS[PREFILL_WORKLOAD]
-    wname = synth.WORKLOAD_NAMES[PREFILL_WORKLOAD]
+    for _ in range(3):  # load the eviction's reduction kernel before anything is timed
+        flush()
+    torch.cuda.synchronize()
+    s = synth.WORKLOADS[args.workload]
+    wname = synth.WORKLOAD_NAMES[args.workload]
 
     if args.only == "copy":  # plain copy of known size, to scale HBM counters
         src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -325,7 +330,7 @@ def main():
         print(json.dumps(bench_decode(torch, args.decode_steps, flush)))
         return 0
 
-    inp = synth.prefill_inputs(s, synth.SEED_BASE + PREFILL_WORKLOAD)
+    inp = synth.prefill_inputs(s, synth.SEED_BASE + args.workload)
     g = prefill_buffers(torch, s, inp)
     for _ in range(args.warmup):
         run_prefill(g, s)
@@ -395,7 +400,7 @@ def main():
     out = {
         "metric": METRIC, "value": tokens / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us_step / 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": wname, "batch": s.batch, "seqlen": s.seqlen, "nheads": s.nheads,
                    "headdim": s.headdim, "dstate": s.dstate, "ngroups": s.ngroups, "chunk": s.chunk,
                    "cache": "cold (512 MiB eviction before each step, outside the events)",
