@@ -73,7 +73,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int li = lane & 15, lg = lane >> 4;
     const size_t bhc = ((size_t)b * H + h) * nc + c;
     const long tc = (long)c * Q;  // first token of the chunk
@@ -147,7 +148,28 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         }
     };
 
-    // ---- prologue: block 0, decay tables, entering state, C fragments
+    // ---- prologue: C fragments, block 0, decay tables, entering state.  The C loads
+    // go first: the wait for block 0 then covers them on every path, so no wait for
+    // them is left inside the main loop (which would also drain the next prefetch).
+    // C rows of this wavefront's tile: GEMM1^T B operand and off-diagonal A operand
+    bf16x8 cb[F32 ? 1 : KS];
+    float cf[F32 ? KS : 1];
+    {
+        // buffer resource over this chunk's valid rows of C: rows past the sequence (and
+        // the negative offsets of a wavefront without a tile) read as zeros, no branches
+        const int vr = (int)((L - tc) < Q ? (L - tc) : Q);
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(Cm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vr - 1) * G * N + N) * sizeof(TIn)));
+        const uint32_t row = (uint32_t)((ibase + li) * G * N);
+        if constexpr (F32) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                cf[ks] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(4u * (row + ks * 4 + lg)), 0, 0));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+        }
+    }
     prefetch(0);
     for (int i = tid; i < 256 + 32; i += NT) {
         float a = 0.f, d = 0.f, e = 0.f;
@@ -184,25 +206,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 w.z = pack_f16x2(hv[k][1].x, hv[k][1].y);
                 w.w = pack_f16x2(hv[k][1].z, hv[k][1].w);
                 *reinterpret_cast<uint4 *>(&hs[row * LDH + 8 * cg]) = w;
-            }
-        }
-    }
-    // C rows of this wavefront's tile: GEMM1^T B operand and off-diagonal A operand
-    bf16x8 cb[F32 ? 1 : KS];
-    float cf[F32 ? KS : 1];
-    {
-        const long ti = tc + ibase + li;
-        const bool ok = t >= 0 && ti < L;
-        const TIn *crow = Cm + (((size_t)b * L + (ok ? ti : 0)) * G + g) * N;
-        if constexpr (F32) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cf[ks] = ok ? crow[ks * 4 + lg] : 0.f;
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (ok) u = *reinterpret_cast<const uint4 *>(crow + ks * 32 + 8 * lg);
-                cb[ks] = __builtin_bit_cast(bf16x8, u);
             }
         }
     }
@@ -251,20 +254,37 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 if (jb > ibase + 15) break;                 // whole step above the diagonal
                 const bool has1 = jb + 16 <= ibase + 15;    // second 16-column tile not all masked
                 // GEMM1^T: d0 = G^T[jb .. jb+15][rows], d1 = G^T[jb+16 .. jb+31][rows]
+                // (has1 is wave-uniform; testing it outside the k loop keeps each variant
+                // straight-line, so the LDS reads are issued together ahead of the MFMAs)
                 f32x4 d0 = zero4(), d1 = zero4();
+                if constexpr (F32) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if constexpr (F32) {
-                        d0 = mfma16x16x4_f32(bs[buf][(js + li) * LDB + ks * 4 + lg], cf[ks], d0);
-                        if (has1) d1 = mfma16x16x4_f32(bs[buf][(js + 16 + li) * LDB + ks * 4 + lg], cf[ks], d1);
-                    } else {
-                        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&bs[buf][(js + li) * LDB + ks * 32 + 8 * lg]);
-                        d0 = mfma16x16x32_bf16(a0, cb[ks], d0);
-                        if (has1) {
-                            const bf16x8 a1 =
-                                *reinterpret_cast<const bf16x8 *>(&bs[buf][(js + 16 + li) * LDB + ks * 32 + 8 * lg]);
-                            d1 = mfma16x16x32_bf16(a1, cb[ks], d1);
+                    for (int ks = 0; ks < KS; ++ks) d0 = mfma16x16x4_f32(bs[buf][(js + li) * LDB + ks * 4 + lg], cf[ks], d0);
+                    if (has1) {
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks)
+                            d1 = mfma16x16x4_f32(bs[buf][(js + 16 + li) * LDB + ks * 4 + lg], cf[ks], d1);
+                    }
+                } else {
+                    const raw_t *b0 = &bs[buf][(js + li) * LDB + 8 * lg];
+                    if (has1) {
+                        bf16x8 a0[KS], a1[KS];
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
+                            a1[ks] = *reinterpret_cast<const bf16x8 *>(b0 + 16 * LDB + ks * 32);
                         }
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            d0 = mfma16x16x32_bf16(a0[ks], cb[ks], d0);
+                            d1 = mfma16x16x32_bf16(a1[ks], cb[ks], d1);
+                        }
+                    } else {
+                        bf16x8 a0[KS];
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) d0 = mfma16x16x32_bf16(a0[ks], cb[ks], d0);
                     }
                 }
                 // Hadamard: decay exp(a_i - a_j), dt_j and the causal mask, in registers.

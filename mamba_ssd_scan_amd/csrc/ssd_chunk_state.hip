@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int li = lane & 15, lg = lane >> 4;
     const size_t bhc = ((size_t)b * H + h) * nc + c;
     const long tc = (long)c * Q;
