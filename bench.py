@@ -38,7 +38,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_state_kernel": "ssd_chunk_state.hip",
     "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
-    "step_kernel": "ssd_step.hip",
+    "step_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
 }
 
 
@@ -63,12 +63,16 @@ def alg_counts(s: synth.PrefillShape) -> dict:
     st = B * H * P * N * 4
     h0 = st if s.init_state != "zero" else 0
     tri = Q * (Q + 1)                  # 2 flops x Q(Q+1)/2 pairs
+    # C.B^T products as the GEMM1 kernel stores them: per (b, g, chunk), 512 fp32 per
+    # 32-column step of each 16-row tile (the steps on or below the diagonal)
+    cb = B * G * nc * sum(t // 2 + 1 for t in range(Q // 16)) * 512 * 4
     k = {
         "chunk_cumsum_kernel": dict(bytes=dt + chunk_tab, flops=2 * B * L * H),
         "chunk_state_kernel": dict(bytes=x + bc + chunk_tab + states, flops=2 * B * H * L * P * N),
         "state_passing_kernel": dict(bytes=2 * states + B * H * nc * 4 + h0 + st, flops=2 * B * H * nc * P * N),
-        "chunk_scan_kernel": dict(bytes=x + 2 * bc + chunk_tab + states + y,
-                                  flops=B * nc * (G * N * tri + H * P * tri) + 2 * B * H * L * P * N),
+        "chunk_gemm1_kernel": dict(bytes=2 * bc + cb, flops=B * nc * G * N * tri),
+        "chunk_scan_kernel": dict(bytes=x + bc + cb + chunk_tab + states + y,
+                                  flops=B * nc * H * P * tri + 2 * B * H * L * P * N),
     }
     fused_bytes = x + dt + 2 * bc + y + st + h0
     fused_flops = B * nc * (G * N * tri + H * P * tri) + 4 * B * H * L * P * N
@@ -177,6 +181,8 @@ def prefill_buffers(torch, s, inp):
     g["acum"] = torch.empty((s.batch, s.nheads, nc, s.chunk), dtype=torch.float32, device="cuda")
     g["dtc"] = torch.empty_like(g["acum"])
     g["states"] = torch.empty((s.batch, s.nheads, nc, s.headdim, s.dstate), dtype=torch.float32, device="cuda")
+    g["cb"] = torch.empty(ssd.chunk_gemm1_size(s.batch, s.seqlen, s.ngroups, s.chunk) // 4, dtype=torch.float32,
+                          device="cuda")
     return g
 
 
@@ -201,17 +207,22 @@ def stage_fns(torch, g, s):
     def restore_states():  # state passing works in place: restart from the chunk states every launch
         g["states"].copy_(pristine["states"])
 
+    def gemm1():
+        ssd.chunk_gemm1(g["B"], g["C"], chunk=Q, cb=g["cb"])
+
     def scan():
-        ssd.chunk_scan(g["x"], g["B"], g["C"], g["acum"], g["dtc"], g["states"], g["D"], chunk=Q, y=g["y"])
+        ssd.chunk_scan(g["x"], g["C"], g["cb"], g["acum"], g["dtc"], g["states"], g["D"], chunk=Q, y=g["y"])
 
     cumsum()
     cstate()
     torch.cuda.synchronize()
     pristine["states"] = g["states"].clone()
     passing()
+    gemm1()
     torch.cuda.synchronize()
     return {"chunk_cumsum_kernel": (cumsum, None), "chunk_state_kernel": (cstate, None),
-            "state_passing_kernel": (passing, restore_states), "chunk_scan_kernel": (scan, None)}
+            "state_passing_kernel": (passing, restore_states), "chunk_gemm1_kernel": (gemm1, None),
+            "chunk_scan_kernel": (scan, None)}
 
 
 # ---------------------------------------------------------------------------- CPU baseline
@@ -294,7 +305,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
-                                       "chunk_cumsum_kernel", "step", "copy"],
+                                       "chunk_cumsum_kernel", "chunk_gemm1_kernel", "step", "copy"],
                     help="profiling aid: launch only this work --steps times (cold), print nothing else")
     args = ap.parse_args()
 

@@ -71,6 +71,7 @@ int ssd_version(void);
  *   dA_cum  [B, H, nc, Q] fp32   per-chunk inclusive cumsum of dt*A
  *   dt_c    [B, H, nc, Q] fp32   dt regrouped per chunk (0 past seqlen)
  *   states  [B, H, nc, P, N] fp32  chunk states, then entering states
+ *   cb      ssd_chunk_gemm1_size(B, L, G, Q) bytes: the C.B^T products
  * with nc = ceil(seqlen / Q).
  */
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim,
@@ -112,7 +113,8 @@ int ssd_step(float *state, const void *x, const void *dt, const float *A,
              ssd_dtype_t in_dtype, int batch, int nheads, int headdim, int dstate,
              int ngroups, void *hip_stream);
 
-/* ---- Stage entry points (the four kernels ssd_prefill runs, in order) ---- */
+/* ---- Stage entry points (the kernels ssd_prefill runs, in this order:
+ *      chunk_cumsum + chunk_state (fused), state_passing, chunk_gemm1, chunk_scan) ---- */
 
 /*
  * Step-0: per-chunk inclusive cumulative sum of dt*A (wavefront prefix scan).
@@ -146,13 +148,27 @@ int ssd_state_passing(float *states, const float *dA_cum, const float *initial_s
                       int nchunks, int chunk, void *hip_stream);
 
 /*
- * Step-1 + Step-4 + skip: the output of every chunk,
- *   y_i = sum_{j<=i} (C_i . B_j) exp(dA_cum[i] - dA_cum[j]) dt_c[j] x_j      (intra-chunk)
- *       + exp(dA_cum[i]) * H_enter C_i  + D_h x_i                           (off-diagonal, skip)
- *   h_enter [B, H, nc, P, N] fp32: entering states (ssd_state_passing output).
- *   y [B, L, H, P] fp32 (written).
+ * Step-1 GEMM1 ("Mamba-Family State-Space Model Kernels on a Programmable
+ * CGLA", Sec. III-A): the products G_c[i, j] = C_i . B_j of chunk-local
+ * tokens j <= i, once per (batch, group, chunk) -- every head of a group
+ * shares them.
+ *   Bm, Cm [B, L, G, N] in_dtype; cb (written): ssd_chunk_gemm1_size(...)
+ *   bytes, 16-byte aligned, an opaque fp32 layout read by ssd_chunk_scan
+ *   (tile order of the matrix-core accumulators; entries above the diagonal
+ *   are unused).
  */
-int ssd_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *dA_cum,
+size_t ssd_chunk_gemm1_size(int batch, int seqlen, int ngroups, int chunk);
+int ssd_chunk_gemm1(const void *Bm, const void *Cm, float *cb, ssd_dtype_t in_dtype,
+                    int batch, int seqlen, int dstate, int ngroups, int chunk,
+                    void *hip_stream);
+/*
+ * Step-1 mask + GEMM2, Step-4 and skip: the output of every chunk,
+ *   y_i = sum_{j<=i} G_c[i, j] exp(dA_cum[i] - dA_cum[j]) dt_c[j] x_j        (intra-chunk)
+ *       + exp(dA_cum[i]) * H_enter C_i  + D_h x_i                           (off-diagonal, skip)
+ *   cb: ssd_chunk_gemm1 output for the same B/C; h_enter [B, H, nc, P, N]
+ *   fp32: entering states (ssd_state_passing output); y [B, L, H, P] fp32 (written).
+ */
+int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *dA_cum,
                    const float *dt_c, const float *h_enter, const float *D, float *y,
                    ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
                    int dstate, int ngroups, int chunk, void *hip_stream);

@@ -44,10 +44,16 @@ int check_dtype(ssd_dtype_t t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK
 size_t in_size(ssd_dtype_t t) { return t == SSD_BF16 ? 2 : 4; }
 
 struct WsLayout {
-    size_t acum, dtc, states, total;  // byte offsets of each region, then total bytes
+    size_t acum, dtc, states, cb, total;  // byte offsets of each region, then total bytes
 };
 
-WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int chunk)
+// fp32 elements of the GEMM1 output: 512 per 32-column step of every chunk of every group
+size_t gemm1_elems(int batch, int ngroups, int nchunks, int chunk)
+{
+    return (size_t)batch * ngroups * nchunks * ssd::gemm1_steps_per_chunk(chunk) * 512;
+}
+
+WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk)
 {
     const size_t nc = (size_t)(seqlen + chunk - 1) / chunk;
     const size_t bhq = (size_t)batch * nheads * nc * chunk;
@@ -55,7 +61,8 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, i
     w.acum = 0;
     w.dtc = align_up(w.acum + 4 * bhq, kWsAlign);
     w.states = align_up(w.dtc + 4 * bhq, kWsAlign);
-    w.total = align_up(w.states + 4 * (size_t)batch * nheads * nc * headdim * dstate, kWsAlign);
+    w.cb = align_up(w.states + 4 * (size_t)batch * nheads * nc * headdim * dstate, kWsAlign);
+    w.total = align_up(w.cb + 4 * gemm1_elems(batch, ngroups, (int)nc, chunk), kWsAlign);
     return w;
 }
 
@@ -100,13 +107,13 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (1 << 16) | 0; }
+int ssd_version(void) { return (2 << 16) | 0; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
 {
     if (check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true) != SSD_OK) return 0;
-    return ws_layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+    return ws_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk).total;
 }
 
 int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c, ssd_dtype_t in_dtype,
@@ -155,20 +162,38 @@ int ssd_state_passing(float *states, const float *dA_cum, const float *initial_s
     return hip_status(ssd::launch_state_passing(states, dA_cum, initial_state, final_state, d, s));
 }
 
-int ssd_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *dA_cum, const float *dt_c,
+size_t ssd_chunk_gemm1_size(int batch, int seqlen, int ngroups, int chunk)
+{
+    // headdim/dstate/nheads do not enter the size; pass supported placeholders.
+    if (check_shape(batch, seqlen, ngroups, 64, 64, ngroups, chunk, true) != SSD_OK) return 0;
+    return 4 * gemm1_elems(batch, ngroups, (seqlen + chunk - 1) / chunk, chunk);
+}
+
+int ssd_chunk_gemm1(const void *Bm, const void *Cm, float *cb, ssd_dtype_t in_dtype, int batch, int seqlen,
+                    int dstate, int ngroups, int chunk, void *hip_stream)
+{
+    SSD_TRY(check_dtype(in_dtype));
+    SSD_TRY(check_shape(batch, seqlen, ngroups, 64, dstate, ngroups, chunk, true));
+    if (seqlen == 0) return SSD_OK;
+    if (!Bm || !Cm || !cb || !aligned(Bm, 16) || !aligned(Cm, 16) || !aligned(cb, 16)) return SSD_ERR_INVALID_ARG;
+    const ssd::Dims d = make_dims(batch, seqlen, ngroups, 64, dstate, ngroups, chunk, in_dtype);
+    return hip_status(ssd::launch_chunk_gemm1(Bm, Cm, cb, d, (hipStream_t)hip_stream));
+}
+
+int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *dA_cum, const float *dt_c,
                    const float *h_enter, const float *D, float *y, ssd_dtype_t in_dtype, int batch,
                    int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
     SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
     if (seqlen == 0) return SSD_OK;
-    SSD_TRY(check_seq_inputs(x, dt_c, Bm, SSD_F32));
-    if (!Cm || !dA_cum || !h_enter || !y) return SSD_ERR_INVALID_ARG;
-    if (!aligned(Cm, 16) || !aligned(dA_cum, 16) || !aligned(h_enter, 16) || !aligned(y, 16) || !aligned(D, 4))
+    SSD_TRY(check_seq_inputs(x, dt_c, Cm, SSD_F32));
+    if (!cb || !dA_cum || !h_enter || !y) return SSD_ERR_INVALID_ARG;
+    if (!aligned(cb, 16) || !aligned(dA_cum, 16) || !aligned(h_enter, 16) || !aligned(y, 16) || !aligned(D, 4))
         return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
     return hip_status(
-        ssd::launch_chunk_scan(x, Bm, Cm, dA_cum, dt_c, h_enter, D, y, d, (hipStream_t)hip_stream));
+        ssd::launch_chunk_scan(x, Cm, cb, dA_cum, dt_c, h_enter, D, y, d, (hipStream_t)hip_stream));
 }
 
 int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
@@ -189,18 +214,20 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, c
     SSD_TRY(check_seq_inputs(x, dt, Bm, in_dtype));
     if (!A || !Cm || !y || !aligned(A, 4) || !aligned(Cm, 16) || !aligned(y, 16) || !aligned(D, 4))
         return SSD_ERR_INVALID_ARG;
-    const WsLayout w = ws_layout(batch, seqlen, nheads, headdim, dstate, chunk);
+    const WsLayout w = ws_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk);
     if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
     char *ws = static_cast<char *>(workspace);
     float *acum = reinterpret_cast<float *>(ws + w.acum);
     float *dtc = reinterpret_cast<float *>(ws + w.dtc);
     float *states = reinterpret_cast<float *>(ws + w.states);
+    float *cb = reinterpret_cast<float *>(ws + w.cb);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 
     SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state(x, Bm, dt, A, acum, dtc, states, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
-    return hip_status(ssd::launch_chunk_scan(x, Bm, Cm, acum, dtc, states, D, y, d, s));
+    SSD_TRY(hip_status(ssd::launch_chunk_gemm1(Bm, Cm, cb, d, s)));
+    return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, d, s));
 }
 
 int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,

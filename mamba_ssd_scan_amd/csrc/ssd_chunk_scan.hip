@@ -1,84 +1,88 @@
-// ssd_chunk_scan.hip -- Step-1 (intra-chunk) + Step-4 (off-diagonal) + skip.
+// ssd_chunk_scan.hip -- Step-1 (Hadamard mask + GEMM2) + Step-4 (off-diagonal) + skip.
 //
 // For token i of chunk c (chunk-local index), with the chunk's cumulative
-// decay a = dA_cum and the state H_enter entering the chunk:
+// decay a = dA_cum, the state H_enter entering the chunk and the chunk's
+// C.B^T products G (formed once per group by the GEMM1 kernel):
 //
-//   y_i = sum_{j<=i} (C_i . B_j) exp(a_i - a_j) dt_j x_j     Step-1: GEMM1 over N,
-//                                                            Hadamard mask, GEMM2 over j
-//       + exp(a_i) H_enter C_i                               Step-4: off-diagonal
-//       + D_h x_i                                            skip
+//   y_i = sum_{j<=i} G[i, j] exp(a_i - a_j) dt_j x_j     Step-1: Hadamard mask, GEMM2 over j
+//       + exp(a_i) H_enter C_i                           Step-4: off-diagonal
+//       + D_h x_i                                        skip
 //
 // Sources: "Mamba-Family State-Space Model Kernels on a Programmable CGLA",
 // Sec. III-A and IV-B (Step-1 = GEMM1, element-wise mask of R, GEMM2; a
 // fused mask+GEMM2 removes a round trip per chunk) and "Mambalaya: Einsum-
 // Based Fusion Optimizations on State-Space Models", Fig. 2-5 (fusing
-// consecutive Einsums removes the inter-Einsum traffic).  Here GEMM1, the
-// mask, GEMM2, the off-diagonal product and the skip term are fused in one
-// kernel: the score tile never leaves registers.
+// consecutive Einsums removes the inter-Einsum traffic).  Here the mask,
+// GEMM2, the off-diagonal product and the skip term are fused in one kernel:
+// the masked score tile never leaves registers.
 //
-// Work split: one workgroup per (b, h, c) covering the whole chunk, so the
-// entering state and X are read from memory once, and one wavefront per
-// 16-row tile (16 wavefronts for Q = 256).  The four wavefronts that share a
-// SIMD take tiles {s, 7-s, 8+s, 15-s}, which balances the causal triangle
-// across the SIMDs.  Per 32-column step a wavefront computes two 16x16 tiles
-// of G^T = B C^T on the matrix cores (bf16 inputs are exact operands), which
-// leaves every lane holding one row i and four columns j of G per tile -- a
-// row-slice of the GEMM2 A operand once the X operand uses the same column
-// order.  The mask/decay/dt scaling is applied in registers and the result is
-// rounded to fp16 for GEMM2 (bf16 would round the computed scores to 2^-9,
-// too coarse for the error budget).  B and X are streamed through LDS in
-// blocks of JB tokens, both row-major as they arrive from memory; the GEMM2
-// operand, whose reduction index is the token, is read with the transposing
-// LDS read (fp32 inputs store X transposed instead).  The blocks are
-// double-buffered: the global loads of block k+1 are issued into registers
-// before block k is computed and written to the other LDS buffer afterwards,
-// so one barrier per block suffices and memory latency overlaps the matrix
-// work.  Columns above the diagonal are skipped.
+// Work split: one workgroup per (b, h, c) covering the whole chunk, one
+// wavefront per 16-row tile (16 wavefronts for Q = 256); the four wavefronts
+// that share a SIMD take tiles {s, 7-s, 8+s, 15-s}, which balances the causal
+// triangle across the SIMDs.  The prologue stages the chunk's X (fp16,
+// row-major as it arrives) and the entering state (fp16) in LDS and the decay
+// tables, with one barrier; after it every wavefront runs on its own.  Per
+// 32-column step a wavefront loads its slice of G from the GEMM1 output (one
+// coalesced 2 KB read, issued a step ahead), which leaves every lane holding
+// one row i and eight columns j -- a row-slice of the GEMM2 A operand.  The
+// mask/decay/dt scaling is applied in registers and the result is rounded to
+// fp16 for GEMM2 (bf16 would round the computed scores to 2^-9, too coarse
+// for the error budget); the X operand, whose reduction index is the token,
+// is read with the transposing LDS read.  fp32 inputs store X transposed and
+// run the fp32 matrix path.  Columns above the diagonal are skipped.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-template <typename TIn, int P, int N, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
-    const TIn *__restrict__ x, const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
-    const float *__restrict__ acum, const float *__restrict__ dtc, const float *__restrict__ hen,
-    const float *__restrict__ D, float *__restrict__ y, int L, int H, int G, int Q, int nc)
-{
+// LDS plan of one workgroup.  bf16 inputs whose footprint allows it also get a raw
+// staging area that the next item's X, entering state and chunk tables stream into
+// (direct-to-LDS loads: no registers held while the current item is computed).
+template <typename TIn, int P, int N, int NW> struct ScanLds {
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
-    typedef typename Tr::raw_t raw_t;
-    constexpr bool F32 = Tr::kF32;
-    constexpr int JB = F32 ? 32 : 64;        // tokens per staged block
-    constexpr int LDB = N + (F32 ? 4 : 8);   // B rows [JB][N] (raw inputs)
-    // X block: bf16 inputs keep it row-major [JB][P + 16] (fp16) and read the GEMM2
-    // operand with the transposing LDS read; fp32 inputs store it transposed [P][JB + 4].
-    constexpr int LDX = F32 ? JB + 4 : P + 16;
-    constexpr int XSZ = F32 ? P * LDX : JB * LDX;
-    constexpr int LDH = N + 8;               // H_enter rows [P][N] (fp16), bf16 inputs only
-    constexpr int TP = P / 16;
-    constexpr int KS = F32 ? N / 4 : N / 32; // k steps over the state dim
-    constexpr int NT = 64 * NW;              // threads per workgroup
-    constexpr int BU = JB * (N / 8), BPT = (BU + NT - 1) / NT;       // B block: one row x 8 channels
-    constexpr int XR = F32 ? 2 : 1;                                  // X rows per staging unit
-    constexpr int XU = (JB / XR) * (P / 8), XPT = (XU + NT - 1) / NT;
-    constexpr int HU = F32 ? 1 : P * N / 8, HPT = (HU + NT - 1) / NT;  // entering state
-    __shared__ raw_t bs[2][JB * LDB];
-    __shared__ op_t xs[2][XSZ];
-    __shared__ op_t hs[F32 ? 1 : P * LDH];
-    // chunk tables, padded past Q so that the column reads of the last 32-column step
-    // stay inside (padding is never used unmasked): cumulative decay in log2 units, dt,
-    // and exp(a_r - a_j) dt_j with a_r the last column of j's 32-column step
-    __shared__ float acs[256 + 32], dts[256 + 32], ecs[256 + 32];
+    static constexpr bool F32 = Tr::kF32;
+    static constexpr int ROWS = 16 * NW;               // chunk rows held (>= Q)
+    // X: bf16 inputs keep it row-major [ROWS][P + 16] (fp16), read for GEMM2 with the
+    // transposing LDS read; fp32 inputs store it transposed [P][ROWS + 4].
+    static constexpr int LDX = F32 ? ROWS + 4 : P + 16;
+    static constexpr int XSZ = F32 ? P * LDX : ROWS * LDX;
+    static constexpr int LDH = N + 8;                  // H_enter rows [P][N] (fp16), bf16 only
+    static constexpr int HSZ = F32 ? 1 : P * LDH;
+    static constexpr int TAB = ROWS + 32;              // tables padded past the last step
+    static constexpr int base = XSZ * (int)sizeof(op_t) + HSZ * 2 + 3 * TAB * 4;
+    // raw staging: X rows, entering state, dA_cum and dt, and 1 KB that absorbs the
+    // surplus loads of wavefronts with less to stream (every wavefront issues the same count)
+    static constexpr int SX = ROWS * P * 2, SH = P * N * 4, ST = 2 * ROWS * 4, SD = 1024;
+    static constexpr int SALL = SX + SH + ST + SD;
+    static constexpr bool STAGE = !F32 && base + SALL <= 160 * 1024;
+    static constexpr int bytes = base + (STAGE ? SALL : 0);
+};
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int g = h / (H / G);
+template <typename TIn, int P, int N, int NW>
+__global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
+    const TIn *__restrict__ x, const TIn *__restrict__ Cm, const void *__restrict__ cbg,
+    const float *__restrict__ acum, const float *__restrict__ dtc, const float *__restrict__ hen,
+    const float *__restrict__ D, float *__restrict__ y, int L, int H, int G, int Q, int nc, int nitems)
+{
+    typedef ScanLds<TIn, P, N, NW> S;
+    typedef typename S::op_t op_t;
+    constexpr bool F32 = S::F32, STAGE = S::STAGE;
+    constexpr int ROWS = S::ROWS, LDX = S::LDX, LDH = S::LDH;
+    constexpr int TP = P / 16;
+    constexpr int KS = F32 ? N / 4 : N / 32;  // k steps over the state dim
+    constexpr int NT = 64 * NW;               // threads per workgroup (>= S::TAB)
+    constexpr int NSMAX = NW >= 8 ? NW / 2 : 2;  // most 32-column steps of one row tile
+    __shared__ op_t xs[S::XSZ];
+    __shared__ op_t hs[S::HSZ];
+    // chunk tables: cumulative decay in log2 units, dt, and exp(a_r - a_j) dt_j with a_r the
+    // last column of j's 32-column step (zero past the chunk; padding is never used unmasked)
+    __shared__ float acs[S::TAB], dts[S::TAB], ecs[S::TAB];
+    __shared__ __align__(16) unsigned char stg[STAGE ? S::SALL : 16];
+
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int li = lane & 15, lg = lane >> 4;
-    const size_t bhc = ((size_t)b * H + h) * nc + c;
-    const long tc = (long)c * Q;  // first token of the chunk
-    const int nblk = (Q + JB - 1) / JB;
     const int nt = Q >> 4;
     // this wavefront's row tile: the k-th wavefront on SIMD s (wave = 4k + s) takes
     // tile 8(k/2) + s for even k and 8(k/2) + 7 - s for odd k
@@ -90,240 +94,286 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         t = wave < nt ? wave : -1;
     }
     const int ibase = 16 * t;
+    const int ns = t >= 0 ? (ibase + 15) / 32 + 1 : 0;  // 32-column steps up to the diagonal
+    const int spc = (nt & 1) ? ((nt >> 1) + 1) * ((nt >> 1) + 1) : (nt >> 1) * ((nt >> 1) + 1);
+    const int Tt = t < 0 ? 0 : (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
 
-    // Buffer resources over this chunk's valid rows of X and B: loads of rows past
-    // the chunk or the sequence return zeros.
-    const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P, (uint32_t)(((vrows - 1) * H * P + P) * sizeof(TIn)));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(Bm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vrows - 1) * G * N + N) * sizeof(TIn)));
+    // Per-lane addresses of the staging, conversion and store code do not change from
+    // item to item; left alone, the compiler computes them all once and keeps them live
+    // across the item loop, which spills registers.  Adding an opaque zero, produced
+    // afresh in every iteration, makes it recompute them where they are used instead.
+    auto opaque_zero = [] {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        return z;
+    };
 
-    Raw8<TIn> bpre[BPT];
-    Raw8<TIn> xpre[XPT][XR];
-    auto prefetch = [&](int jbk) {
-        const int j0 = jbk * JB;
+    // Item k is chunk c of head h of batch entry b, k = (b H + h) nc + c.
+    struct Item {
+        int c, h, b, g, vrows;
+        size_t bhc;
+        long tc;
+    };
+    auto decode = [&](int item) {
+        Item it;
+        it.c = item % nc;
+        it.h = (item / nc) % H;
+        it.b = item / (nc * H);
+        it.g = it.h / (H / G);
+        it.bhc = ((size_t)it.b * H + it.h) * nc + it.c;
+        it.tc = (long)it.c * Q;
+        it.vrows = (int)((L - it.tc) < Q ? (L - it.tc) : Q);
+        return it;
+    };
+    // buffer resource over the item's valid rows of X: rows past the chunk or the
+    // sequence read as zeros (the masked columns of the last step multiply finite values)
+    auto x_rsrc = [&](const Item &it) {
+        return make_rsrc(x + ((size_t)it.b * L + it.tc) * H * P + (size_t)it.h * P,
+                         (uint32_t)(((it.vrows - 1) * H * P + P) * sizeof(TIn)));
+    };
+
+    // ---- staging (bf16 inputs): direct-to-LDS loads of the raw X rows, the raw fp32
+    // entering state and the item's dA_cum / dt, each wavefront instruction filling 1 KB
+    // (or 256 B for the tables) of the staging area.  Every wavefront issues the same
+    // number of loads; a surplus one reads an empty range into the spare 1 KB.
+    // (with live == false every load reads an empty range: the count stays the same)
+    auto stage_issue = [&](const Item &it, bool live) {
+        if constexpr (STAGE) {
+            const int lane = (tid & 63) + opaque_zero();
+            constexpr int XI = S::SX / 1024, HI = S::SH / 1024, TI = ROWS / 64;
+            unsigned char *spare = stg + S::SX + S::SH + S::ST;
+            const __amdgpu_buffer_rsrc_t rx = live ? x_rsrc(it) : make_rsrc(x, 0u);
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < BU) {
-                const int jr = u / (N / 8), cg = u % (N / 8);
-                bpre[k].load(rb, (uint32_t)((j0 + jr) * G * N + 8 * cg));
+            for (int k = 0; k < (XI + NW - 1) / NW; ++k) {
+                const int wi = k * NW + wave;
+                const int byte = 1024 * wi + 16 * lane, row = byte / (2 * P), col = byte % (2 * P);
+                buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
+                                 (uint32_t)(row * H * P * 2 + col));
             }
-        }
+            const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + it.bhc * P * N, live ? (uint32_t)S::SH : 0u);
 #pragma unroll
-        for (int k = 0; k < XPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < XU) {
-                const int jr = u / (P / 8), cg = u % (P / 8), j = j0 + XR * jr;
-#pragma unroll
-                for (int e = 0; e < XR; ++e) xpre[k][e].load(rx, (uint32_t)((j + e) * H * P + 8 * cg));
+            for (int k = 0; k < (HI + NW - 1) / NW; ++k) {
+                const int wi = k * NW + wave;
+                buf_load_lds16(wi < HI ? rh : make_rsrc(hen, 0u), wi < HI ? stg + S::SX + 1024 * wi : spare,
+                                 (uint32_t)(1024 * wi + 16 * lane));
+            }
+            // tables: wavefronts 0 .. TI-1 stream dA_cum, TI .. 2TI-1 stream dt (zeros past Q)
+            {
+                const bool has = live && wave < 2 * TI;
+                const int tab = has ? wave / TI : 0, wi = has ? wave % TI : 0;
+                const float *src = (tab == 0 ? acum : dtc) + it.bhc * Q;
+                const __amdgpu_buffer_rsrc_t rt = make_rsrc(src, has ? (uint32_t)(Q * 4) : 0u);
+                buf_load_lds4(rt, has ? stg + S::SX + S::SH + tab * ROWS * 4 + 256 * wi : spare,
+                                (uint32_t)(4 * (64 * wi + lane)));
             }
         }
     };
-    auto commit = [&](int buf) {
+    // staged (or, without staging, freshly loaded) item -> the compute layout in LDS
+    auto stage_commit = [&](const Item &it) {
+        const int tid = threadIdx.x + opaque_zero();
+        constexpr int XR = F32 ? 2 : 1;  // X rows per unit
+        constexpr int XU = (ROWS / XR) * (P / 8), XPT = (XU + NT - 1) / NT;
+        constexpr int HU = F32 ? 1 : P * N / 8, HPT = (HU + NT - 1) / NT;
+        float ta = 0.f, tr = 0.f, td = 0.f;
+        const int ir = min(32 * (tid >> 5) + 31, Q - 1);
+        if constexpr (STAGE) {
+            const bf16_t *sx = reinterpret_cast<const bf16_t *>(stg);
+            const float *sh = reinterpret_cast<const float *>(stg + S::SX);
+            const float *st = reinterpret_cast<const float *>(stg + S::SX + S::SH);
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < BU) {
-                const int jr = u / (N / 8), cg = u % (N / 8);
-                bpre[k].store(&bs[buf][jr * LDB + 8 * cg]);
+            for (int k = 0; k < XPT; ++k) {
+                const int u = tid + k * NT;
+                if (u < XU) {
+                    Raw8<bf16_t> r;
+                    r.v = *reinterpret_cast<const uint4 *>(sx + 8 * u);
+                    *reinterpret_cast<uint4 *>(&xs[(u / (P / 8)) * LDX + 8 * (u % (P / 8))]) = raw8_to_f16x8(r);
+                }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < XPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < XU) {
-                const int jr = u / (P / 8), cg = u % (P / 8);
-                if constexpr (F32) {
-                    float v0[8], v1[8];
-                    xpre[k][0].to_f32(v0);
-                    xpre[k][XR - 1].to_f32(v1);
+            for (int k = 0; k < HPT; ++k) {
+                const int u = tid + k * NT;
+                if (u < HU) {
+                    const float4 h0 = *reinterpret_cast<const float4 *>(sh + 8 * u);
+                    const float4 h1 = *reinterpret_cast<const float4 *>(sh + 8 * u + 4);
+                    uint4 w;
+                    w.x = pack_f16x2(h0.x, h0.y);
+                    w.y = pack_f16x2(h0.z, h0.w);
+                    w.z = pack_f16x2(h1.x, h1.y);
+                    w.w = pack_f16x2(h1.z, h1.w);
+                    *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = w;
+                }
+            }
+            if (tid < Q) {
+                ta = st[tid];
+                tr = st[ir];
+                td = st[ROWS + tid];
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rx = x_rsrc(it);
+            Raw8<TIn> px[XPT][XR];
+            float4 ph[HPT][2];
 #pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) store_pair(&xs[buf][(8 * cg + kk) * LDX + 2 * jr], v0[kk], v1[kk]);
-                } else {
-                    *reinterpret_cast<uint4 *>(&xs[buf][jr * LDX + 8 * cg]) = raw8_to_f16x8(xpre[k][0]);
+            for (int k = 0; k < XPT; ++k) {
+                const int u = tid + k * NT;
+                if (u < XU) {
+                    const int jr = u / (P / 8), cg = u % (P / 8);
+#pragma unroll
+                    for (int e = 0; e < XR; ++e) px[k][e].load(rx, (uint32_t)((XR * jr + e) * H * P + 8 * cg));
+                }
+            }
+            if constexpr (!F32) {
+                const float *hp = hen + it.bhc * P * N;
+#pragma unroll
+                for (int k = 0; k < HPT; ++k) {
+                    const int u = tid + k * NT;
+                    if (u < HU) {
+                        ph[k][0] = *reinterpret_cast<const float4 *>(hp + 8 * u);
+                        ph[k][1] = *reinterpret_cast<const float4 *>(hp + 8 * u + 4);
+                    }
+                }
+            }
+            if (tid < Q) {
+                ta = acum[it.bhc * Q + tid];
+                tr = acum[it.bhc * Q + ir];
+                td = dtc[it.bhc * Q + tid];
+            }
+#pragma unroll
+            for (int k = 0; k < XPT; ++k) {
+                const int u = tid + k * NT;
+                if (u < XU) {
+                    const int jr = u / (P / 8), cg = u % (P / 8);
+                    if constexpr (F32) {
+                        float v0[8], v1[8];
+                        px[k][0].to_f32(v0);
+                        px[k][XR - 1].to_f32(v1);
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk) store_pair(&xs[(8 * cg + kk) * LDX + 2 * jr], v0[kk], v1[kk]);
+                    } else {
+                        *reinterpret_cast<uint4 *>(&xs[jr * LDX + 8 * cg]) = raw8_to_f16x8(px[k][0]);
+                    }
+                }
+            }
+            if constexpr (!F32) {
+#pragma unroll
+                for (int k = 0; k < HPT; ++k) {
+                    const int u = tid + k * NT;
+                    if (u < HU) {
+                        uint4 w;
+                        w.x = pack_f16x2(ph[k][0].x, ph[k][0].y);
+                        w.y = pack_f16x2(ph[k][0].z, ph[k][0].w);
+                        w.z = pack_f16x2(ph[k][1].x, ph[k][1].y);
+                        w.w = pack_f16x2(ph[k][1].z, ph[k][1].w);
+                        *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = w;
+                    }
                 }
             }
         }
+        if (tid < S::TAB) {
+            float a = 0.f, d = 0.f, e = 0.f;
+            if (tid < Q) {
+                a = ta * kLog2e;
+                d = td;
+                e = __builtin_amdgcn_exp2f(tr * kLog2e - a) * d;
+            }
+            acs[tid] = a;
+            dts[tid] = d;
+            ecs[tid] = e;
+        }
     };
 
-    // ---- prologue: C fragments, block 0, decay tables, entering state.  The C loads
-    // go first: the wait for block 0 then covers them on every path, so no wait for
-    // them is left inside the main loop (which would also drain the next prefetch).
-    // C rows of this wavefront's tile: GEMM1^T B operand and off-diagonal A operand
+    // ---- per-wavefront operands of an item, held in registers: the C rows of the tile
+    // (off-diagonal A operand) and, for bf16 inputs, all of the tile's fp16 slices of G
     bf16x8 cb[F32 ? 1 : KS];
     float cf[F32 ? KS : 1];
-    {
-        // buffer resource over this chunk's valid rows of C: rows past the sequence (and
-        // the negative offsets of a wavefront without a tile) read as zeros, no branches
-        const int vr = (int)((L - tc) < Q ? (L - tc) : Q);
-        const __amdgpu_buffer_rsrc_t rc =
-            make_rsrc(Cm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vr - 1) * G * N + N) * sizeof(TIn)));
+    f16x8 gs[F32 ? 1 : NSMAX];
+    // The loads are unconditional (a wavefront without a tile reads slice 0 and C rows
+    // past the buffer range, which return zeros): the wait before the next barrier then
+    // knows exactly how many loads follow the staging loads it has to wait for.
+    auto load_tile_operands = [&](const Item &it) {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * G * N + (size_t)it.g * N,
+                                                    (uint32_t)(((it.vrows - 1) * G * N + N) * sizeof(TIn)));
         const uint32_t row = (uint32_t)((ibase + li) * G * N);
         if constexpr (F32) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 cf[ks] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(4u * (row + ks * 4 + lg)), 0, 0));
         } else {
+            const size_t slice0 = (((size_t)it.b * G + it.g) * nc + it.c) * (size_t)spc + Tt;
+            const f16 *gq = static_cast<const f16 *>(cbg) + (slice0 * 64 + lane) * 8;
+            const int slast = ns > 0 ? ns - 1 : 0;
+#pragma unroll
+            for (int s = 0; s < NSMAX; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
         }
-    }
-    prefetch(0);
-    for (int i = tid; i < 256 + 32; i += NT) {
-        float a = 0.f, d = 0.f, e = 0.f;
-        if (i < Q) {
-            const int ir = min(32 * (i >> 5) + 31, Q - 1);
-            a = acum[bhc * Q + i] * kLog2e;
-            d = dtc[bhc * Q + i];
-            e = __builtin_amdgcn_exp2f(acum[bhc * Q + ir] * kLog2e - a) * d;
-        }
-        acs[i] = a;
-        dts[i] = d;
-        ecs[i] = e;
-    }
-    const float *hp = hen + bhc * P * N;
-    if constexpr (!F32) {
-        float4 hv[HPT][2];
-#pragma unroll
-        for (int k = 0; k < HPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < HU) {
-                const int row = u / (N / 8), cg = u % (N / 8);
-                hv[k][0] = *reinterpret_cast<const float4 *>(hp + row * N + 8 * cg);
-                hv[k][1] = *reinterpret_cast<const float4 *>(hp + row * N + 8 * cg + 4);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < HPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < HU) {
-                const int row = u / (N / 8), cg = u % (N / 8);
-                uint4 w;
-                w.x = pack_f16x2(hv[k][0].x, hv[k][0].y);
-                w.y = pack_f16x2(hv[k][0].z, hv[k][0].w);
-                w.z = pack_f16x2(hv[k][1].x, hv[k][1].y);
-                w.w = pack_f16x2(hv[k][1].z, hv[k][1].w);
-                *reinterpret_cast<uint4 *>(&hs[row * LDH + 8 * cg]) = w;
-            }
-        }
-    }
-    const float Dh = D ? D[h] : 0.f;
-    commit(0);
-    __syncthreads();
-    if (nblk > 1) prefetch(1);
+    };
 
+    // y of an item is written at the start of the next one, ahead of that item's staging
+    // loads, so that the wait for those loads never waits for the stores
+    // (buffer stores over the item's valid rows, which drop rows past the sequence and
+    // every store of a wavefront without a tile: the store count is the same for all)
     f32x4 acc[TP];
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
-
-    // ---- Step-4: exp(a_i) * (C_i . H_enter[p, :]) for this wavefront's rows
-    if (t >= 0) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            f16x8 ch;
-            if constexpr (!F32) ch = bf16x8_to_f16x8(cb[ks]);
-#pragma unroll
-            for (int pt = 0; pt < TP; ++pt) {
-                if constexpr (F32) {
-                    acc[pt] = mfma16x16x4_f32(cf[ks], hp[(pt * 16 + li) * N + ks * 4 + lg], acc[pt]);
-                } else {
-                    const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
-                    acc[pt] = mfma16x16x32_f16(ch, hf, acc[pt]);
-                }
-            }
-        }
+    for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();  // (stored, with an empty range, before the first item)
+    auto store_y = [&](const Item &it, bool live) {
+        const int lane = (tid & 63) + opaque_zero(), li = lane & 15, lg = lane >> 4;
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + (((size_t)it.b * L + it.tc) * H + it.h) * P,
+                                                    live && t >= 0 ? (uint32_t)(((it.vrows - 1) * H * P + P) * 4) : 0u);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(acs[ibase + 4 * lg + r]);
+            const int row = ibase + 4 * lg + r;
 #pragma unroll
-            for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= e;
+            for (int pt = 0; pt < TP; ++pt) {
+                // (copied to a scalar first: a bit cast of the vector element itself reads element 0)
+                const float v = acc[pt][r];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, (int)(4u * (uint32_t)(row * H * P + pt * 16 + li)),
+                                                      0, 0);
+            }
         }
-    }
+    };
 
-    // ---- Step-1: stream the causal column blocks
-    const int irow = ibase + li;
-    const float ai = t >= 0 ? acs[irow] : 0.f;
-    for (int jbk = 0; jbk < nblk; ++jbk) {
-        const int buf = jbk & 1;
-        if (t >= 0 && jbk * JB <= ibase + 15) {
+    // Every load and store below is issued unconditionally (empty ranges stand in for
+    // the ones with nothing to do), so that each wait counts exactly the younger
+    // operations it may leave in flight.
+    int item = blockIdx.x;
+    Item cur = decode(item), prev = cur;
+    stage_issue(cur, true);
+    load_tile_operands(cur);
+    for (bool first = true;; first = false) {
+        const float Dh = D ? D[cur.h] : 0.f;
+        __syncthreads();  // the item's staged loads have landed; the previous item's readers are done
+        stage_commit(cur);
+        __syncthreads();
+        store_y(prev, !first);
+        const int next = item + gridDim.x;
+        const bool more = next < nitems;
+        const Item nx = more ? decode(next) : cur;
+        stage_issue(nx, more);
+
+        if (t >= 0) {
 #pragma unroll
-            for (int js = 0; js < JB; js += 32) {
-                const int jb = jbk * JB + js;
-                if (jb > ibase + 15) break;                 // whole step above the diagonal
-                const bool has1 = jb + 16 <= ibase + 15;    // second 16-column tile not all masked
-                // GEMM1^T: d0 = G^T[jb .. jb+15][rows], d1 = G^T[jb+16 .. jb+31][rows]
-                // (has1 is wave-uniform; testing it outside the k loop keeps each variant
-                // straight-line, so the LDS reads are issued together ahead of the MFMAs)
-                f32x4 d0 = zero4(), d1 = zero4();
+            for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
+            // ---- Step-1: the causal 32-column steps of this row tile.  All but the last lie
+            // strictly below the diagonal; the last one holds it (tile t: steps 0 .. t/2).
+            const int irow = ibase + li;
+            const float ai = acs[irow];
+            const size_t slice0 = (((size_t)cur.b * G + cur.g) * nc + cur.c) * (size_t)spc + Tt;
+            const float *gf = static_cast<const float *>(cbg) + (slice0 * 64 + lane) * 8;
+            // Lane holds G[irow][jb + 4 lg + r] (d0) and G[irow][jb + 16 + 4 lg + r] (d1).
+            auto slice = [&](int s, float d0[4], float d1[4]) {
                 if constexpr (F32) {
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) d0 = mfma16x16x4_f32(bs[buf][(js + li) * LDB + ks * 4 + lg], cf[ks], d0);
-                    if (has1) {
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks)
-                            d1 = mfma16x16x4_f32(bs[buf][(js + 16 + li) * LDB + ks * 4 + lg], cf[ks], d1);
-                    }
-                } else {
-                    const raw_t *b0 = &bs[buf][(js + li) * LDB + 8 * lg];
-                    if (has1) {
-                        bf16x8 a0[KS], a1[KS];
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
-                            a1[ks] = *reinterpret_cast<const bf16x8 *>(b0 + 16 * LDB + ks * 32);
-                        }
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            d0 = mfma16x16x32_bf16(a0[ks], cb[ks], d0);
-                            d1 = mfma16x16x32_bf16(a1[ks], cb[ks], d1);
-                        }
-                    } else {
-                        bf16x8 a0[KS];
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) d0 = mfma16x16x32_bf16(a0[ks], cb[ks], d0);
-                    }
+                    const float4 g0 = reinterpret_cast<const float4 *>(gf + (size_t)s * 512)[0];
+                    const float4 g1 = reinterpret_cast<const float4 *>(gf + (size_t)s * 512)[1];
+                    d0[0] = g0.x; d0[1] = g0.y; d0[2] = g0.z; d0[3] = g0.w;
+                    d1[0] = g1.x; d1[1] = g1.y; d1[2] = g1.z; d1[3] = g1.w;
                 }
-                // Hadamard: decay exp(a_i - a_j), dt_j and the causal mask, in registers.
-                // Lane holds G[irow][jb + 4 lg + r] (d0) and G[irow][jb + 16 + 4 lg + r] (d1).
-                float r0[4], r1[4];
-                if (jb + 31 <= ibase) {
-                    // Step strictly below the diagonal: factor the decay through the step's
-                    // last column a_r, exp(a_i - a_j) = exp(a_i - a_r) exp(a_r - a_j).  Both
-                    // factors are <= 1 (a is non-increasing for A <= 0) and any underflow
-                    // drops a term smaller still; exp(a_r - a_j) dt_j is the chunk table.
-                    const float er = __builtin_amdgcn_exp2f(ai - acs[jb + 31]);
-                    const float4 e0 = *reinterpret_cast<const float4 *>(&ecs[jb + 4 * lg]);
-                    const float4 e1 = *reinterpret_cast<const float4 *>(&ecs[jb + 16 + 4 * lg]);
-                    const float ej0[4] = {e0.x, e0.y, e0.z, e0.w}, ej1[4] = {e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        r0[r] = d0[r] * (er * ej0[r]);
-                        r1[r] = d1[r] * (er * ej1[r]);
-                    }
-                } else {
-                    // diagonal step: direct exponentials under the causal mask
-                    const float4 a0v = *reinterpret_cast<const float4 *>(&acs[jb + 4 * lg]);
-                    const float4 t0v = *reinterpret_cast<const float4 *>(&dts[jb + 4 * lg]);
-                    const float4 a1v = *reinterpret_cast<const float4 *>(&acs[jb + 16 + 4 * lg]);
-                    const float4 t1v = *reinterpret_cast<const float4 *>(&dts[jb + 16 + 4 * lg]);
-                    const float aj0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, tj0[4] = {t0v.x, t0v.y, t0v.z, t0v.w};
-                    const float aj1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, tj1[4] = {t1v.x, t1v.y, t1v.z, t1v.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        r0[r] = (jb + 4 * lg + r <= irow) ? d0[r] * __builtin_amdgcn_exp2f(ai - aj0[r]) * tj0[r] : 0.f;
-                        r1[r] = (has1 && jb + 16 + 4 * lg + r <= irow) ? d1[r] * __builtin_amdgcn_exp2f(ai - aj1[r]) * tj1[r]
-                                                                       : 0.f;
-                    }
-                }
-                // GEMM2: k slots of lane group lg are columns {jb+4lg+r, jb+16+4lg+r}
+            };
+            // GEMM2 of one step: k slots of lane group lg are columns {jb+4lg+r, jb+16+4lg+r}
+            auto gemm2 = [&](int jb, bool has1, const float r0[4], const float r1[4]) {
                 if constexpr (F32) {
 #pragma unroll
                     for (int pt = 0; pt < TP; ++pt) {
-                        const op_t *xr = &xs[buf][(pt * 16 + li) * LDX + js + 4 * lg];
+                        const op_t *xr = &xs[(pt * 16 + li) * LDX + jb + 4 * lg];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[pt] = mfma16x16x4_f32(r0[r], xr[r], acc[pt]);
                         if (has1) {
@@ -341,63 +391,151 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
                     for (int pt = 0; pt < TP; ++pt) {
                         // lane li receives X[jb + 4 lg + r][16 pt + li] and X[jb + 16 + 4 lg + r][16 pt + li]
-                        const int ox = tr16_offset(lane, js, pt * 16, LDX);
-                        const f16x4 lo = lds_read_tr16(&xs[buf][ox]);
-                        const f16x4 hi = lds_read_tr16(&xs[buf][ox + 16 * LDX]);
+                        const int ox = tr16_offset(lane, jb, pt * 16, LDX);
+                        const f16x4 lo = lds_read_tr16(&xs[ox]);
+                        const f16x4 hi = lds_read_tr16(&xs[ox + 16 * LDX]);
                         const f16x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                         acc[pt] = mfma16x16x32_f16(a, bx, acc[pt]);
                     }
                 }
+            };
+#pragma unroll
+            for (int s = 0; s + 1 < NSMAX; ++s) {
+                if (s + 1 < ns) {
+                    // Strictly below the diagonal: factor the decay through the step's last
+                    // column a_r, exp(a_i - a_j) = exp(a_i - a_r) exp(a_r - a_j).  Both factors
+                    // are <= 1 (a is non-increasing for A <= 0) and any underflow drops a term
+                    // smaller still; exp(a_r - a_j) dt_j is the chunk table.
+                    const int jb = 32 * s;
+                    float d0[4], d1[4];
+                    if constexpr (F32) {
+                        slice(s, d0, d1);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            d0[r] = static_cast<float>(gs[s][r]);
+                            d1[r] = static_cast<float>(gs[s][4 + r]);
+                        }
+                    }
+                    const float er = __builtin_amdgcn_exp2f(ai - acs[jb + 31]);
+                    const float4 e0 = *reinterpret_cast<const float4 *>(&ecs[jb + 4 * lg]);
+                    const float4 e1 = *reinterpret_cast<const float4 *>(&ecs[jb + 16 + 4 * lg]);
+                    const float ej0[4] = {e0.x, e0.y, e0.z, e0.w}, ej1[4] = {e1.x, e1.y, e1.z, e1.w};
+                    float r0[4], r1[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        r0[r] = d0[r] * (er * ej0[r]);
+                        r1[r] = d1[r] * (er * ej1[r]);
+                    }
+                    gemm2(jb, true, r0, r1);
+                }
             }
-            if (ibase / JB == jbk) {
-                // This block holds the tile's own rows, so the tile is complete: add the skip
-                // term and store it now, while the other wavefronts still compute.
-                if constexpr (!F32) {
-                    // the transposing read hands lane li the values X[ibase + 4 lg + r][16 pt + li],
-                    // exactly the accumulator positions (exact for bf16 inputs in fp16 range)
+            {
+                // the diagonal step: direct exponentials under the causal mask
+                const int sd = ns - 1, jb = 32 * sd;
+                const bool has1 = jb + 16 <= ibase + 15;  // second 16-column half not all masked
+                float d0[4], d1[4];
+                if constexpr (F32) {
+                    slice(sd, d0, d1);
+                } else {
+                    f16x8 gd = gs[0];
+#pragma unroll
+                    for (int s = 1; s < NSMAX; ++s)
+                        if (s == sd) gd = gs[s];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        d0[r] = static_cast<float>(gd[r]);
+                        d1[r] = static_cast<float>(gd[4 + r]);
+                    }
+                }
+                const float4 a0v = *reinterpret_cast<const float4 *>(&acs[jb + 4 * lg]);
+                const float4 t0v = *reinterpret_cast<const float4 *>(&dts[jb + 4 * lg]);
+                const float4 a1v = *reinterpret_cast<const float4 *>(&acs[jb + 16 + 4 * lg]);
+                const float4 t1v = *reinterpret_cast<const float4 *>(&dts[jb + 16 + 4 * lg]);
+                const float aj0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, tj0[4] = {t0v.x, t0v.y, t0v.z, t0v.w};
+                const float aj1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, tj1[4] = {t1v.x, t1v.y, t1v.z, t1v.w};
+                float r0[4], r1[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    r0[r] = (jb + 4 * lg + r <= irow) ? d0[r] * __builtin_amdgcn_exp2f(ai - aj0[r]) * tj0[r] : 0.f;
+                    r1[r] = (has1 && jb + 16 + 4 * lg + r <= irow) ? d1[r] * __builtin_amdgcn_exp2f(ai - aj1[r]) * tj1[r]
+                                                                   : 0.f;
+                }
+                gemm2(jb, has1, r0, r1);
+            }
+
+            // ---- Step-4: exp(a_i) * (C_i . H_enter[p, :]) for this wavefront's rows, in its
+            // own accumulator, added scaled
+            {
+                const float *hp = hen + cur.bhc * P * N;
+                f32x4 off[TP];
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) off[pt] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    f16x8 ch;
+                    if constexpr (!F32) ch = bf16x8_to_f16x8(cb[ks]);
 #pragma unroll
                     for (int pt = 0; pt < TP; ++pt) {
-                        const f16x4 xv = lds_read_tr16(&xs[buf][tr16_offset(lane, ibase - jbk * JB, pt * 16, LDX)]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * static_cast<float>(xv[r]);
+                        if constexpr (F32) {
+                            off[pt] = mfma16x16x4_f32(cf[ks], hp[(pt * 16 + li) * N + ks * 4 + lg], off[pt]);
+                        } else {
+                            const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
+                            off[pt] = mfma16x16x32_f16(ch, hf, off[pt]);
+                        }
                     }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const long tt = tc + ibase + 4 * lg + r;
-                    if (tt < L) {
+                    const float e = __builtin_amdgcn_exp2f(acs[ibase + 4 * lg + r]);
 #pragma unroll
-                        for (int pt = 0; pt < TP; ++pt) {
-                            const size_t idx = (((size_t)b * L + tt) * H + h) * P + pt * 16 + li;
-                            if constexpr (F32)
-                                y[idx] = acc[pt][r] + Dh * load_in(x + idx);
-                            else
-                                y[idx] = acc[pt][r];
-                        }
-                    }
+                    for (int pt = 0; pt < TP; ++pt) acc[pt][r] += e * off[pt][r];
+                }
+            }
+            // ---- skip term
+            if constexpr (F32) {
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * xs[(pt * 16 + li) * LDX + ibase + 4 * lg + r];
+            } else {
+                // the transposing read hands lane li the values X[ibase + 4 lg + r][16 pt + li],
+                // exactly the accumulator positions (exact for bf16 inputs in fp16 range)
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) {
+                    const f16x4 xv = lds_read_tr16(&xs[tr16_offset(lane, ibase, pt * 16, LDX)]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * static_cast<float>(xv[r]);
                 }
             }
         }
-        if (jbk + 1 < nblk) {
-            commit(buf ^ 1);  // the other buffer was last read before the previous barrier
-            __syncthreads();
-            if (jbk + 2 < nblk) prefetch(jbk + 2);
-        }
+        // the next item's tile operands, in flight while its staging completes
+        load_tile_operands(nx);
+        prev = cur;
+        if (!more) break;
+        item = next;
+        cur = nx;
     }
-
+    store_y(prev, true);
 }
 
 template <typename TIn, int P>
-static hipError_t launch_scan_n(const void *x, const void *Bm, const void *Cm, const float *acum,
+static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, const float *acum,
                                 const float *dtc, const float *hen, const float *D, float *y,
-                                const Dims &d, hipStream_t s)
+                                const Dims &d, int ncu, hipStream_t s)
 {
-    const dim3 grid(d.nc, d.H, d.B);
-    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm),
-              *cc = static_cast<const TIn *>(Cm);
-#define SSD_SCAN_LAUNCH(NN, NWV)                                                                      \
-    chunk_scan_kernel<TIn, P, NN, NWV><<<grid, 64 * NWV, 0, s>>>(xx, bb, cc, acum, dtc, hen, D, y, d.L, \
-                                                                 d.H, d.G, d.Q, d.nc)
+    // persistent: enough workgroups for 16 wavefronts per compute unit, each looping over
+    // the (b, h, c) items with stride gridDim.x
+    const int nitems = d.nc * d.H * d.B;
+    const TIn *xx = static_cast<const TIn *>(x), *cc = static_cast<const TIn *>(Cm);
+    // up to 16 wavefronts per compute unit, as many workgroups as the LDS holds
+#define SSD_SCAN_LAUNCH(NN, NWV)                                                                          \
+    do {                                                                                                  \
+        const int fit = (160 * 1024) / ScanLds<TIn, P, NN, NWV>::bytes, per_cu = fit < 16 / NWV ? fit : 16 / NWV; \
+        const int nwg = nitems < ncu * per_cu ? nitems : ncu * per_cu;                                   \
+        chunk_scan_kernel<TIn, P, NN, NWV><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, d.L, \
+                                                                    d.H, d.G, d.Q, d.nc, nitems);        \
+    } while (0)
 #define SSD_SCAN_BY_Q(NN)                                  \
     if (d.Q == 256)                                        \
         SSD_SCAN_LAUNCH(NN, 16);                           \
@@ -418,24 +556,29 @@ static hipError_t launch_scan_n(const void *x, const void *Bm, const void *Cm, c
 }
 
 template <typename TIn>
-static hipError_t launch_scan_t(const void *x, const void *Bm, const void *Cm, const float *acum,
+static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, const float *acum,
                                 const float *dtc, const float *hen, const float *D, float *y,
-                                const Dims &d, hipStream_t s)
+                                const Dims &d, int ncu, hipStream_t s)
 {
     switch (d.P) {
-    case 32: return launch_scan_n<TIn, 32>(x, Bm, Cm, acum, dtc, hen, D, y, d, s);
-    case 64: return launch_scan_n<TIn, 64>(x, Bm, Cm, acum, dtc, hen, D, y, d, s);
-    case 128: return launch_scan_n<TIn, 128>(x, Bm, Cm, acum, dtc, hen, D, y, d, s);
+    case 32: return launch_scan_n<TIn, 32>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
+    case 64: return launch_scan_n<TIn, 64>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
+    case 128: return launch_scan_n<TIn, 128>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *acum,
+hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
                              const float *dtc, const float *h_enter, const float *D, float *y,
                              const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_scan_t<bf16_t>(x, Bm, Cm, acum, dtc, h_enter, D, y, d, s)
-                  : launch_scan_t<float>(x, Bm, Cm, acum, dtc, h_enter, D, y, d, s);
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu <= 0) ncu = 1;
+    return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, d, ncu, s)
+                  : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, d, ncu, s);
 }
 
 }  // namespace ssd

@@ -203,6 +203,20 @@ __device__ __forceinline__ int tr16_offset(int lane, int k0, int m0, int ld)
     return (k0 + 4 * g + (q >> 2)) * ld + m0 + 4 * (q & 3);
 }
 
+// Direct-to-LDS buffer loads (gfx950): every lane reads 16 (or 4) bytes at byte
+// offset `off` of the buffer resource and the wavefront writes them to LDS at
+// `lds + 16 * lane` (or `lds + 4 * lane`) (the LDS address must be wave-uniform).  Out-of-range reads
+// deliver zeros.  The load counts in the wavefront's vector-memory counter like any other.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)off, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, (int)off, 0, 0, 0);
+}
+
 // Eight raw inputs converted to fp16 and packed into 16 bytes (one LDS store).
 template <typename TIn>
 __device__ __forceinline__ uint4 raw8_to_f16x8(const Raw8<TIn> &r, float scale = 1.f)

@@ -22,7 +22,12 @@ hipError_t launch_cumsum_chunk_state(const void *x, const void *Bm, const void *
                                      float *dtc, float *states, const Dims &d, hipStream_t s);
 hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
-hipError_t launch_chunk_scan(const void *x, const void *Bm, const void *Cm, const float *acum,
+// Step-1 GEMM1 once per (batch, group, chunk): cb holds B * G * nc * gemm1_steps_per_chunk(Q)
+// slices of 512 values, fp16 for bf16 inputs and fp32 for fp32 inputs (fragment order, see
+// ssd_chunk_gemm1.hip).
+int gemm1_steps_per_chunk(int q);
+hipError_t launch_chunk_gemm1(const void *Bm, const void *Cm, void *cb, const Dims &d, hipStream_t s);
+hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
                              const float *dtc, const float *h_enter, const float *D, float *y,
                              const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).

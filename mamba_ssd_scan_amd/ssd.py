@@ -19,7 +19,8 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan")
+           "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
+           "ssd_chunk_gemm1", "ssd_chunk_scan")
 
 
 class SsdError(RuntimeError):
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_state.restype = i
     L.ssd_state_passing.argtypes = [vp] * 4 + [i] * 6 + [vp]
     L.ssd_state_passing.restype = i
+    L.ssd_chunk_gemm1_size.argtypes = [i] * 4
+    L.ssd_chunk_gemm1_size.restype = sz
+    L.ssd_chunk_gemm1.argtypes = [vp] * 3 + [i] * 6 + [vp]
+    L.ssd_chunk_gemm1.restype = i
     L.ssd_chunk_scan.argtypes = [vp] * 8 + [i] * 8 + [vp]
     L.ssd_chunk_scan.restype = i
     _lib = L
@@ -221,14 +226,36 @@ def state_passing(states, acum, initial_state=None, *, chunk: int, final_state="
     return final_state
 
 
-def chunk_scan(x, B, C, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stream=None):
+def chunk_gemm1_size(batch, seqlen, ngroups, chunk) -> int:
+    n = lib().ssd_chunk_gemm1_size(batch, seqlen, ngroups, chunk)
+    if n == 0 and seqlen > 0:
+        raise SsdError(SSD_ERR_UNSUPPORTED, "ssd_chunk_gemm1_size")
+    return n
+
+
+def chunk_gemm1(B, C, *, chunk: int, cb=None, stream=None):
+    """C.B^T products of every chunk, once per group (opaque fp32 buffer for chunk_scan)."""
+    torch = _torch()
+    batch, seqlen, ngroups, dstate = B.shape
+    _dev(B, C, cb)
+    if C.dtype != B.dtype:
+        raise TypeError("B and C must share one dtype")
+    if cb is None:
+        cb = torch.empty(max(chunk_gemm1_size(batch, seqlen, ngroups, chunk) // 4, 4), dtype=torch.float32,
+                         device=B.device)
+    _check(lib().ssd_chunk_gemm1(_ptr(B), _ptr(C), _ptr(cb), _dtype_code(B), batch, seqlen, dstate, ngroups, chunk,
+                                 _stream(stream)), "ssd_chunk_gemm1")
+    return cb
+
+
+def chunk_scan(x, C, cb, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stream=None):
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
-    ngroups, dstate = B.shape[2], B.shape[3]
-    _dev(x, B, C, acum, dtc, h_enter, D, y)
+    ngroups, dstate = C.shape[2], C.shape[3]
+    _dev(x, C, cb, acum, dtc, h_enter, D, y)
     if y is None:
         y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
-    _check(lib().ssd_chunk_scan(_ptr(x), _ptr(B), _ptr(C), _ptr(acum), _ptr(dtc), _ptr(h_enter), _ptr(D), _ptr(y),
+    _check(lib().ssd_chunk_scan(_ptr(x), _ptr(C), _ptr(cb), _ptr(acum), _ptr(dtc), _ptr(h_enter), _ptr(D), _ptr(y),
                                 _dtype_code(x), batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
                                 _stream(stream)), "ssd_chunk_scan")
     return y

@@ -23,7 +23,9 @@ A_cum[i] the inclusive sum of a over the chunk's tokens 0..i:
 
 A ragged last chunk simply has fewer tokens.  The intermediates are returned
 in the layouts the GPU library's stage entry points use, with the last chunk
-padded as if by tokens with dt = 0 and x = 0 (A_cum stays constant, dt = 0).
+padded as if by tokens with dt = 0 and x = 0 (A_cum stays constant, dt = 0);
+the GEMM1 products come back as full [Q, Q] matrices per (batch, group,
+chunk), lower triangle only (zero above the diagonal and past the sequence).
 """
 from __future__ import annotations
 
@@ -46,6 +48,7 @@ def chunked(x, dt, A, B, C, D=None, h0=None, *, Q: int):
     states = np.zeros((nb, H, nc, P, N))
     h_enter = np.zeros((nb, H, nc, P, N))
     final = np.zeros((nb, H, P, N))
+    gemm1 = np.zeros((nb, G, nc, Q, Q))
     for b in range(nb):
         for h in range(H):
             g = h // hpg
@@ -67,6 +70,7 @@ def chunked(x, dt, A, B, C, D=None, h0=None, *, Q: int):
                 Lmat = np.where(lower, np.exp(np.where(lower, seg, 0.0)), 0.0)
                 # Step-1: GEMM1 -> Hadamard -> GEMM2
                 G1 = Cc @ Bc.T
+                gemm1[b, g, c, :q, :q] = np.tril(G1)
                 R = G1 * Lmat * dtc[None, :]
                 y_diag = R @ Xc
                 # Step-2
@@ -83,4 +87,4 @@ def chunked(x, dt, A, B, C, D=None, h0=None, *, Q: int):
                     yc = yc + float(D[h]) * Xc
                 y[b, t0:t1, h, :] = yc
             final[b, h] = run
-    return dict(y=y, final=final, acum=acum, dt=dtp, states=states, h_enter=h_enter)
+    return dict(y=y, final=final, acum=acum, dt=dtp, states=states, h_enter=h_enter, gemm1=gemm1)

@@ -34,7 +34,17 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
-    assert ssd.lib().ssd_version() >> 16 == 1
+    assert ssd.lib().ssd_version() >> 16 == 2
+
+
+def gemm1_steps(q):
+    """32-column steps on or below the diagonal of a chunk of q tokens, over its 16-row tiles."""
+    return sum(t // 2 + 1 for t in range(q // 16))
+
+
+def test_gemm1_steps_closed_form():
+    # the count the kernels use in closed form: T(2m) = m(m+1), T(2m+1) = (m+1)^2
+    assert [gemm1_steps(q) for q in (16, 32, 64, 128, 256)] == [1, 2, 6, 20, 72]
 
 
 def test_workspace_size_formula():
@@ -44,8 +54,10 @@ def test_workspace_size_formula():
                                   (2, 1000, 6, 32, 128, 3, 128), (1, 1, 1, 32, 32, 1, 16)]:
         nc = -(-l // q)
         bhq = b * h * nc * q * 4
-        want = al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n)
+        cb = 4 * b * g * nc * gemm1_steps(q) * 512
+        want = al(al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n) + cb)
         assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want
+        assert L.ssd_chunk_gemm1_size(b, l, g, q) == cb
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 1, 48) == 0   # bad chunk
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 48, 128, 1, 64) == 0   # bad headdim
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 5, 64) == 0   # H % G
@@ -103,7 +115,15 @@ def test_stage_entry_points_reject_before_launch():
     assert L.ssd_state_passing(None, P0, None, None, 1, 4, 64, 64, 3, 64, None) == INV
     assert L.ssd_state_passing(P0, P0, None, None, 1, 4, 64, 64, -1, 64, None) == INV
     assert L.ssd_state_passing(P0, P0, P0 + 4, None, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_chunk_gemm1(None, P0, P0, BF, 1, 100, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_gemm1(P0, P0, P0 + 4, BF, 1, 100, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_gemm1(P0, P0, P0, BF, 1, 100, 96, 1, 64, None) == UNS
+    assert L.ssd_chunk_gemm1(P0, P0, P0, BF, 1, 100, 64, 1, 48, None) == UNS
+    assert L.ssd_chunk_gemm1(P0, P0, P0, 7, 1, 100, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_gemm1(None, None, None, BF, 1, 0, 64, 1, 64, None) == 0   # empty sequence: no-op
+    assert L.ssd_chunk_gemm1_size(1, 100, 1, 48) == 0
     assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, None, None, P0, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
+    assert L.ssd_chunk_scan(P0, P0, None, P0, P0, P0, None, P0, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
     assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0 + 4, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
     assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0, F, 1, 100, 4, 64, 64, 3, 64, None) == INV
 

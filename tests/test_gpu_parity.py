@@ -116,16 +116,66 @@ def test_stage_state_passing():
     assert e1 < 1e-5 and e2 < 1e-5
 
 
+def decode_gemm1(cb, B, G, nc, Q):
+    """Unpack the GEMM1 output into [B, G, nc, Q, Q] (NaN where the layout holds nothing).
+
+    Layout: per (b, g, c), row tile t (rows 16t..16t+15) and 32-column step s <= t/2 are
+    numbered t by t; each holds 64 lanes x 8 values, lane l = 16 lg + li carrying
+    G[16t + li][32s + 4lg + r] at r and G[16t + li][32s + 16 + 4lg + r] at 4 + r.
+    """
+    nt = Q // 16
+    steps = [(t, s) for t in range(nt) for s in range(t // 2 + 1)]
+    arr = cb[: B * G * nc * len(steps) * 512].reshape(B, G, nc, len(steps), 64, 8)
+    out = np.full((B, G, nc, Q, Q), np.nan)
+    lane = np.arange(64)
+    li, lg = lane % 16, lane // 16
+    for k, (t, s) in enumerate(steps):
+        for r in range(4):
+            for half in range(2):
+                j = 32 * s + 16 * half + 4 * lg + r
+                ok = j < Q
+                out[:, :, :, 16 * t + li[ok], j[ok]] = arr[:, :, :, k, lane[ok], 4 * half + r]
+    return out
+
+
+@pytest.mark.parametrize("dtype,Q,N,G,L", [("bf16", 256, 128, 1, 700), ("bf16", 64, 64, 2, 1000),
+                                           ("f32", 64, 64, 1, 300), ("bf16", 32, 128, 1, 100),
+                                           ("bf16", 16, 32, 4, 50), ("f32", 128, 32, 2, 129)])
+def test_stage_chunk_gemm1(dtype, Q, N, G, L):
+    """C.B^T of every chunk against the oracle's Step-1 GEMM1, on the causal triangle."""
+    torch = gh.torch()
+    inp, r = _stage_case(dtype=dtype, Q=Q, P=32, N=N, G=G, L=L, H=G)
+    g = gh.upload(inp)
+    cb = ssd.chunk_gemm1(g["B"], g["C"], chunk=Q)
+    torch.cuda.synchronize()
+    nc = -(-L // Q)
+    raw = cb.cpu().numpy()
+    # bf16 inputs: the products are stored as fp16 (the matrix-core operand type downstream)
+    vals = raw.view(np.float16) if dtype == "bf16" else raw
+    got = decode_gemm1(vals.astype(np.float64), inp["x"].shape[0], G, nc, Q)
+    want = r["gemm1"]
+    tok = np.arange(nc)[:, None] * Q + np.arange(Q)[None, :]          # [nc, Q] global token
+    keep = np.tril(np.ones((Q, Q), bool))[None] & (tok < L)[:, :, None]  # j <= i, row in sequence
+    e = np.abs(got - want)[:, :, keep].max() / np.abs(want[:, :, keep]).max()
+    print(f"[chunk_gemm1] {dtype} Q={Q} N={N} G={G} L={L} err={e:.2e}", flush=True)
+    # fp32 accumulation of exact products; bf16 inputs add the fp16 rounding of the stored
+    # value, at most 2^-11 of the element and so of max|G|
+    bound = 2.0 ** -11 if dtype == "bf16" else TOL[dtype] / 20
+    assert np.isfinite(got[:, :, keep]).all() and e < bound
+
+
 @pytest.mark.parametrize("dtype,Q,P,N,G", [("bf16", 256, 64, 128, 1), ("bf16", 64, 64, 64, 2),
                                            ("f32", 64, 64, 64, 1), ("bf16", 32, 128, 128, 1),
-                                           ("bf16", 16, 32, 32, 4)])
+                                           ("bf16", 16, 32, 32, 4), ("bf16", 128, 128, 64, 1),
+                                           ("f32", 256, 32, 128, 1)])
 def test_stage_chunk_scan(dtype, Q, P, N, G):
     torch = gh.torch()
     inp, r = _stage_case(dtype=dtype, Q=Q, P=P, N=N, G=G)
     g = gh.upload(inp)
     f = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()
     for D in (g["D"], None):
-        y = ssd.chunk_scan(g["x"], g["B"], g["C"], f(r["acum"]), f(r["dt"]), f(r["h_enter"]), D, chunk=Q)
+        cb = ssd.chunk_gemm1(g["B"], g["C"], chunk=Q)
+        y = ssd.chunk_scan(g["x"], g["C"], cb, f(r["acum"]), f(r["dt"]), f(r["h_enter"]), D, chunk=Q)
         torch.cuda.synchronize()
         yo = r["y"] if D is not None else chunked.chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None,
                                                           inp["h0"], Q=Q)["y"]
