@@ -63,9 +63,10 @@ def alg_counts(s: synth.PrefillShape) -> dict:
     st = B * H * P * N * 4
     h0 = st if s.init_state != "zero" else 0
     tri = Q * (Q + 1)                  # 2 flops x Q(Q+1)/2 pairs
-    # C.B^T products as the GEMM1 kernel stores them: per (b, g, chunk), 512 fp32 per
-    # 32-column step of each 16-row tile (the steps on or below the diagonal)
-    cb = B * G * nc * sum(t // 2 + 1 for t in range(Q // 16)) * 512 * 4
+    # C.B^T products as the GEMM1 kernel stores them: per (b, g, chunk), 512 values per
+    # 32-column step of each 16-row tile (the steps on or below the diagonal), fp16 for
+    # bf16 inputs and fp32 for fp32 inputs
+    cb = B * G * nc * sum(t // 2 + 1 for t in range(Q // 16)) * 512 * (2 if s.dtype == "bf16" else 4)
     k = {
         "chunk_cumsum_kernel": dict(bytes=dt + chunk_tab, flops=2 * B * L * H),
         "chunk_state_kernel": dict(bytes=x + bc + chunk_tab + states, flops=2 * B * H * L * P * N),
