@@ -224,9 +224,8 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, c
     float *cb = reinterpret_cast<float *>(ws + w.cb);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 
-    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state(x, Bm, dt, A, acum, dtc, states, d, s)));
+    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
-    SSD_TRY(hip_status(ssd::launch_chunk_gemm1(Bm, Cm, cb, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, d, s));
 }
 

@@ -20,6 +20,7 @@
 // flight in registers ahead of the block being contracted; LDS is
 // double-buffered with one barrier per block.
 #include "ssd_common.h"
+#include "ssd_gemm1_body.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -27,15 +28,20 @@ namespace ssd {
 // Step-0 fused in (FUSE_CUMSUM): one wavefront scans this chunk's dt*A (as the
 // stand-alone cumulative-decay kernel does) and writes dA_cum / dt_c for the
 // later stages, instead of reading them; the other wavefronts start loading.
-template <typename TIn, int P, int N, bool FUSE_CUMSUM>
+// Step-1 GEMM1 fused in (GR > 0, chunks of up to GR tokens): the first G rows of
+// the grid (blockIdx.y < G) are GEMM1 workgroups, one per (b, group, chunk), which
+// form C.B^T into `cb` while the chunk-state workgroups (blockIdx.y = G + h) run;
+// they come first in the grid so that they are dispatched first.
+template <typename TIn, int P, int N, bool FUSE_CUMSUM, int GR>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict__ x,
                                                           const TIn *__restrict__ Bm,
                                                           const TIn *__restrict__ dt,
                                                           const float *__restrict__ A,
                                                           float *__restrict__ acum,
                                                           float *__restrict__ dtc,
-                                                          float *__restrict__ states, int L, int H,
-                                                          int G, int Q, int nc)
+                                                          float *__restrict__ states,
+                                                          const TIn *__restrict__ Cm, void *__restrict__ cb,
+                                                          int L, int H, int G, int Q, int nc)
 {
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
@@ -51,11 +57,21 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     constexpr int TPW = (NT + 3) / 4;                   // output tiles per wavefront
     constexpr int XU = (JB / 2) * (P / 8), XPT = (XU + 255) / 256;  // two tokens x 8 channels
     constexpr int BU = (JB / 2) * (N / 8), BPT = (BU + 255) / 256;
-    __shared__ op_t xs[2][XSZ];
-    __shared__ op_t bs[2][BSZ];
-    __shared__ float ws[256];                           // decay weights w_j of the chunk
+    typedef Gemm1Chunk<TIn, N, 4, (GR > 0 ? GR : 64)> G1;
+    constexpr int kStateBytes = 2 * (XSZ + BSZ) * (int)sizeof(op_t) + 256 * 4;
+    constexpr int kBytes = (GR > 0 && G1::kLdsBytes > kStateBytes) ? G1::kLdsBytes : kStateBytes;
+    __shared__ __align__(16) unsigned char smem[kBytes];
+    if constexpr (GR > 0) {
+        if ((int)blockIdx.y < G) {
+            G1::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+            return;
+        }
+    }
+    op_t(*xs)[XSZ] = reinterpret_cast<op_t(*)[XSZ]>(smem);
+    op_t(*bs)[BSZ] = reinterpret_cast<op_t(*)[BSZ]>(smem + 2 * XSZ * sizeof(op_t));
+    float *ws = reinterpret_cast<float *>(smem + 2 * (XSZ + BSZ) * sizeof(op_t));  // decay weights w_j of the chunk
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, h = blockIdx.y - (GR > 0 ? G : 0), b = blockIdx.z;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -246,29 +262,34 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     }
 }
 
-template <typename TIn, int P, bool FUSE>
+template <typename TIn, int P, bool FUSE, int GR>
 static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const Dims &d, hipStream_t s)
+                              float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
 {
-    const dim3 grid(d.nc, d.H, d.B);
-    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt);
+    const dim3 grid(d.nc, d.H + (GR > 0 ? d.G : 0), d.B);
+    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
+              *cc = static_cast<const TIn *>(Cm);
+#define SSD_CS_LAUNCH(NN)                                                                                      \
+    chunk_state_kernel<TIn, P, NN, FUSE, GR><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, d.L, \
+                                                                  d.H, d.G, d.Q, d.nc)
     switch (d.N) {
-    case 32: chunk_state_kernel<TIn, P, 32, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
-    case 64: chunk_state_kernel<TIn, P, 64, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
-    case 128: chunk_state_kernel<TIn, P, 128, FUSE><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, d.L, d.H, d.G, d.Q, d.nc); break;
+    case 32: SSD_CS_LAUNCH(32); break;
+    case 64: SSD_CS_LAUNCH(64); break;
+    case 128: SSD_CS_LAUNCH(128); break;
     default: return hipErrorInvalidValue;
     }
+#undef SSD_CS_LAUNCH
     return hipGetLastError();
 }
 
-template <typename TIn, bool FUSE>
+template <typename TIn, bool FUSE, int GR>
 static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const Dims &d, hipStream_t s)
+                              float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
 {
     switch (d.P) {
-    case 32: return launch_cs_n<TIn, 32, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
-    case 64: return launch_cs_n<TIn, 64, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
-    case 128: return launch_cs_n<TIn, 128, FUSE>(x, Bm, dt, A, acum, dtc, states, d, s);
+    case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    case 64: return launch_cs_n<TIn, 64, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    case 128: return launch_cs_n<TIn, 128, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -277,15 +298,26 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
                               float *states, const Dims &d, hipStream_t s)
 {
     float *ac = const_cast<float *>(acum), *dc = const_cast<float *>(dtc);  // read-only in this mode
-    return d.bf16 ? launch_cs_t<bf16_t, false>(x, Bm, nullptr, nullptr, ac, dc, states, d, s)
-                  : launch_cs_t<float, false>(x, Bm, nullptr, nullptr, ac, dc, states, d, s);
+    return d.bf16 ? launch_cs_t<bf16_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, d, s)
+                  : launch_cs_t<float, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, d, s);
 }
 
-hipError_t launch_cumsum_chunk_state(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                                     float *dtc, float *states, const Dims &d, hipStream_t s)
+template <typename TIn>
+static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                                 float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_cs_t<bf16_t, true>(x, Bm, dt, A, acum, dtc, states, d, s)
-                  : launch_cs_t<float, true>(x, Bm, dt, A, acum, dtc, states, d, s);
+    // GEMM1 workgroups hold a whole chunk of B in LDS: size them by the chunk length
+    if (d.Q > 128) return launch_cs_t<TIn, true, 256>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    if (d.Q > 64) return launch_cs_t<TIn, true, 128>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    return launch_cs_t<TIn, true, 64>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+}
+
+hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
+                                           float *acum, float *dtc, float *states, const void *Cm, void *cb,
+                                           const Dims &d, hipStream_t s)
+{
+    return d.bf16 ? launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s)
+                  : launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
 }
 
 }  // namespace ssd

@@ -17,9 +17,11 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, floa
                                const Dims &d, hipStream_t s);
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
                               float *states, const Dims &d, hipStream_t s);
-// Step-0 fused into Step-2: writes acum/dtc (same values as launch_chunk_cumsum) and states.
-hipError_t launch_cumsum_chunk_state(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                                     float *dtc, float *states, const Dims &d, hipStream_t s);
+// Step-0 and Step-1 GEMM1 fused into the Step-2 launch: writes acum/dtc (same values as
+// launch_chunk_cumsum), states, and the GEMM1 products cb (same as launch_chunk_gemm1).
+hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
+                                           float *acum, float *dtc, float *states, const void *Cm, void *cb,
+                                           const Dims &d, hipStream_t s);
 hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
 // Step-1 GEMM1 once per (batch, group, chunk): cb holds B * G * nc * gemm1_steps_per_chunk(Q)
