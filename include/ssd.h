@@ -101,6 +101,25 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm,
                 int chunk, void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * ssd_prefill with the work adjacent to the SSD core in a Mamba-2 block fused in
+ * ("Mamba-Family State-Space Model Kernels on a Programmable CGLA", Sec. III-A:
+ * the in-projection emits the gate z and the raw step-size channel next to x, B, C):
+ *   dt_bias [H] fp32 or NULL   added to dt before the softplus (0 if NULL)
+ *   dt_softplus                nonzero: the recurrence uses softplus(dt + dt_bias)
+ *                              = log(1 + exp(dt + dt_bias)) as its step size;
+ *                              zero: dt + dt_bias as given (must then be > 0)
+ *   z [B, L, H, P] in_dtype or NULL   output gate: y <- y * z * sigmoid(z), applied
+ *                              to the whole output (skip term included)
+ *   y [B, L, H, P] y_dtype     SSD_F32, or SSD_BF16 (fp32 result rounded to nearest even)
+ * Everything else as ssd_prefill; ssd_prefill is ssd_prefill_ex with NULL, 0, NULL, SSD_F32.
+ */
+int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm,
+                   const void *Cm, const float *D, const float *dt_bias, int dt_softplus,
+                   const void *z, const float *initial_state, float *final_state, void *y,
+                   ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk,
+                   void *workspace, size_t workspace_bytes, void *hip_stream);
+/*
  * One decode token for every (b, h), fused: the state is read once,
  * decayed, updated with the token's input and written back in place, and
  * the output is read off the updated state.
@@ -112,6 +131,15 @@ int ssd_step(float *state, const void *x, const void *dt, const float *A,
              const void *Bm, const void *Cm, const float *D, float *y,
              ssd_dtype_t in_dtype, int batch, int nheads, int headdim, int dstate,
              int ngroups, void *hip_stream);
+/*
+ * ssd_step with the options of ssd_prefill_ex: dt_bias [H] fp32 or NULL,
+ * dt_softplus, z [B, H, P] in_dtype or NULL, y [B, H, P] in y_dtype.
+ */
+int ssd_step_ex(float *state, const void *x, const void *dt, const float *A,
+                const void *Bm, const void *Cm, const float *D, const float *dt_bias,
+                int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
+                ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
+                int ngroups, void *hip_stream);
 
 /* ---- Stage entry points (the kernels ssd_prefill runs, in this order:
  *      chunk_cumsum + chunk_state (fused), state_passing, chunk_gemm1, chunk_scan) ---- */

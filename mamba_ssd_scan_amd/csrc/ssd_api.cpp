@@ -107,7 +107,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (2 << 16) | 0; }
+int ssd_version(void) { return (2 << 16) | 1; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -192,16 +192,20 @@ int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *
     if (!aligned(cb, 16) || !aligned(dA_cum, 16) || !aligned(h_enter, 16) || !aligned(y, 16) || !aligned(D, 4))
         return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
+    const ssd::SsdOpts o = {nullptr, 0, nullptr, 0};
     return hip_status(
-        ssd::launch_chunk_scan(x, Cm, cb, dA_cum, dt_c, h_enter, D, y, d, (hipStream_t)hip_stream));
+        ssd::launch_chunk_scan(x, Cm, cb, dA_cum, dt_c, h_enter, D, y, o, d, (hipStream_t)hip_stream));
 }
 
-int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
-                const float *initial_state, float *final_state, float *y, ssd_dtype_t in_dtype, int batch,
-                int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, void *workspace,
-                size_t workspace_bytes, void *hip_stream)
+int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                   const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                   float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk, void *workspace,
+                   size_t workspace_bytes, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
+    SSD_TRY(check_dtype(y_dtype));
+    if (!aligned(dt_bias, 4) || !aligned(z, in_size(in_dtype))) return SSD_ERR_INVALID_ARG;
     SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)hip_stream;
@@ -224,24 +228,45 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, c
     float *cb = reinterpret_cast<float *>(ws + w.cb);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 
-    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s)));
+    const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
-    return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, d, s));
+    return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, o, d, s));
+}
+
+int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                const float *initial_state, float *final_state, float *y, ssd_dtype_t in_dtype, int batch,
+                int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, void *workspace,
+                size_t workspace_bytes, void *hip_stream)
+{
+    return ssd_prefill_ex(x, dt, A, Bm, Cm, D, nullptr, 0, nullptr, initial_state, final_state, y, in_dtype, SSD_F32,
+                          batch, seqlen, nheads, headdim, dstate, ngroups, chunk, workspace, workspace_bytes,
+                          hip_stream);
+}
+
+int ssd_step_ex(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
+                const float *D, const float *dt_bias, int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
+                ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate, int ngroups, void *hip_stream)
+{
+    SSD_TRY(check_dtype(in_dtype));
+    SSD_TRY(check_dtype(y_dtype));
+    SSD_TRY(check_shape(batch, -1, nheads, headdim, dstate, ngroups, 0, false));
+    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, es) || !aligned(Bm, es) || !aligned(Cm, es) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, in_size(y_dtype)) || !aligned(dt_bias, 4) || !aligned(z, es))
+        return SSD_ERR_INVALID_ARG;
+    const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
+    const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    return hip_status(ssd::launch_step(state, x, dt, A, Bm, Cm, D, y, o, d, (hipStream_t)hip_stream));
 }
 
 int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
              const float *D, float *y, ssd_dtype_t in_dtype, int batch, int nheads, int headdim, int dstate,
              int ngroups, void *hip_stream)
 {
-    SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_shape(batch, -1, nheads, headdim, dstate, ngroups, 0, false));
-    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
-    const size_t es = in_size(in_dtype);
-    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, es) || !aligned(Bm, es) || !aligned(Cm, es) ||
-        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, 4))
-        return SSD_ERR_INVALID_ARG;
-    const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
-    return hip_status(ssd::launch_step(state, x, dt, A, Bm, Cm, D, y, d, (hipStream_t)hip_stream));
+    return ssd_step_ex(state, x, dt, A, Bm, Cm, D, nullptr, 0, nullptr, y, in_dtype, SSD_F32, batch, nheads, headdim,
+                       dstate, ngroups, hip_stream);
 }
 
 }  // extern "C"

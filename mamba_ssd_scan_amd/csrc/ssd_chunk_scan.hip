@@ -59,11 +59,14 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
     static constexpr int bytes = base + (STAGE ? SALL : 0);
 };
 
-template <typename TIn, int P, int N, int NW>
+// OPT: the options of the model-adjacent entry point (z gate, bf16 y) are compiled in;
+// without them the kernel is exactly the plain chunk scan.
+template <typename TIn, int P, int N, int NW, bool OPT>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, const float *__restrict__ hen,
-    const float *__restrict__ D, float *__restrict__ y, int L, int H, int G, int Q, int nc, int nitems)
+    const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int Q, int nc,
+    int nitems)
 {
     typedef ScanLds<TIn, P, N, NW> S;
     typedef typename S::op_t op_t;
@@ -317,8 +320,18 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();  // (stored, with an empty range, before the first item)
     auto store_y = [&](const Item &it, bool live) {
         const int lane = (tid & 63) + opaque_zero(), li = lane & 15, lg = lane >> 4;
-        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + (((size_t)it.b * L + it.tc) * H + it.h) * P,
-                                                    live && t >= 0 ? (uint32_t)(((it.vrows - 1) * H * P + P) * 4) : 0u);
+        const size_t base = (((size_t)it.b * L + it.tc) * H + it.h) * P;
+        const uint32_t es = OPT && opt.y_bf16 ? 2u : 4u;  // y element size
+        const __amdgpu_buffer_rsrc_t ry =
+            make_rsrc(OPT && opt.y_bf16 ? (void *)(static_cast<uint16_t *>(y) + base) : (void *)(static_cast<float *>(y) + base),
+                      live && t >= 0 ? (uint32_t)(((it.vrows - 1) * H * P + P) * es) : 0u);
+        // Both storage types issue the same 16 dword stores with no branch around them or
+        // around their data (both forms cost a few VALU operations): the waits below count
+        // on that number.  bf16: the even lane of each pair of adjacent columns stores both
+        // values (its neighbour's comes through a lane swap); the odd lane's store goes
+        // past the range and is dropped.
+        const bool y16 = OPT && opt.y_bf16;
+        const bool drop = y16 && (li & 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = ibase + 4 * lg + r;
@@ -326,8 +339,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             for (int pt = 0; pt < TP; ++pt) {
                 // (copied to a scalar first: a bit cast of the vector element itself reads element 0)
                 const float v = acc[pt][r];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, (int)(4u * (uint32_t)(row * H * P + pt * 16 + li)),
-                                                      0, 0);
+                uint32_t data = __float_as_uint(v);
+                if constexpr (OPT) data = y16 ? pack_bf16x2(v, swap_adjacent_lanes(v)) : data;
+                const uint32_t e = (uint32_t)(row * H * P + pt * 16 + li);
+                __builtin_amdgcn_raw_buffer_store_b32(data, ry, (int)(drop ? 0x7ffffff0u : es * e), 0, 0);
             }
         }
     };
@@ -509,6 +524,30 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 }
             }
         }
+        // ---- optional output gate: y <- y * z * sigmoid(z), z laid out as x
+        if (OPT && opt.z && t >= 0) {
+            const TIn *zp = static_cast<const TIn *>(opt.z) + ((size_t)cur.b * L + cur.tc) * H * P + (size_t)cur.h * P;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * H * P + P) * sizeof(TIn)));
+            // all of the lane's z values are requested before the first is used
+            uint32_t zr[TP][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) {
+                    const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * H * P + pt * 16 + li);
+                    if constexpr (F32)
+                        zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)(4u * e), 0, 0);
+                    else
+                        zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)(2u * e), 0, 0);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) {
+                    const float zf = F32 ? __uint_as_float(zr[pt][r]) : __uint_as_float(zr[pt][r] << 16);
+                    acc[pt][r] *= silu(zf);
+                }
+        }
         // the next item's tile operands, in flight while its staging completes
         load_tile_operands(nx);
         prev = cur;
@@ -521,8 +560,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 
 template <typename TIn, int P>
 static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, const float *acum,
-                                const float *dtc, const float *hen, const float *D, float *y,
-                                const Dims &d, int ncu, hipStream_t s)
+                                const float *dtc, const float *hen, const float *D, void *y,
+                                const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     // persistent: enough workgroups for 16 wavefronts per compute unit, each looping over
     // the (b, h, c) items with stride gridDim.x
@@ -533,8 +572,12 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
     do {                                                                                                  \
         const int fit = (160 * 1024) / ScanLds<TIn, P, NN, NWV>::bytes, per_cu = fit < 16 / NWV ? fit : 16 / NWV; \
         const int nwg = nitems < ncu * per_cu ? nitems : ncu * per_cu;                                   \
-        chunk_scan_kernel<TIn, P, NN, NWV><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, d.L, \
-                                                                    d.H, d.G, d.Q, d.nc, nitems);        \
+        if (o.z || o.y_bf16)                                                                              \
+            chunk_scan_kernel<TIn, P, NN, NWV, true><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
+                                                                              d.L, d.H, d.G, d.Q, d.nc, nitems); \
+        else                                                                                              \
+            chunk_scan_kernel<TIn, P, NN, NWV, false><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
+                                                                               d.L, d.H, d.G, d.Q, d.nc, nitems); \
     } while (0)
 #define SSD_SCAN_BY_Q(NN)                                  \
     if (d.Q == 256)                                        \
@@ -557,28 +600,28 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
 
 template <typename TIn>
 static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, const float *acum,
-                                const float *dtc, const float *hen, const float *D, float *y,
-                                const Dims &d, int ncu, hipStream_t s)
+                                const float *dtc, const float *hen, const float *D, void *y,
+                                const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     switch (d.P) {
-    case 32: return launch_scan_n<TIn, 32>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
-    case 64: return launch_scan_n<TIn, 64>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
-    case 128: return launch_scan_n<TIn, 128>(x, Cm, cbg, acum, dtc, hen, D, y, d, ncu, s);
+    case 32: return launch_scan_n<TIn, 32>(x, Cm, cbg, acum, dtc, hen, D, y, o, d, ncu, s);
+    case 64: return launch_scan_n<TIn, 64>(x, Cm, cbg, acum, dtc, hen, D, y, o, d, ncu, s);
+    case 128: return launch_scan_n<TIn, 128>(x, Cm, cbg, acum, dtc, hen, D, y, o, d, ncu, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
-                             const float *dtc, const float *h_enter, const float *D, float *y,
-                             const Dims &d, hipStream_t s)
+                             const float *dtc, const float *h_enter, const float *D, void *y,
+                             const SsdOpts &o, const Dims &d, hipStream_t s)
 {
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (ncu <= 0) ncu = 1;
-    return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, d, ncu, s)
-                  : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, d, ncu, s);
+    return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
+                  : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
 }
 
 }  // namespace ssd

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                                                           float *__restrict__ dtc,
                                                           float *__restrict__ states,
                                                           const TIn *__restrict__ Cm, void *__restrict__ cb,
-                                                          int L, int H, int G, int Q, int nc)
+                                                          SsdOpts opt, int L, int H, int G, int Q, int nc)
 {
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
             for (int k = 0; k < 4; ++k) {
                 const int i = lane * per + k;
                 float d = 0.f;
-                if (k < per && i < Q && tc + i < L) d = load_in(dt + ((size_t)b * L + tc + i) * H + h);
+                if (k < per && i < Q && tc + i < L) d = dt_effective(load_in(dt + ((size_t)b * L + tc + i) * H + h), opt, h);
                 dts[k] = d;
                 run += d * Ah;
                 part[k] = run;
@@ -264,14 +264,15 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 
 template <typename TIn, int P, bool FUSE, int GR>
 static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
+                              float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                              hipStream_t s)
 {
     const dim3 grid(d.nc, d.H + (GR > 0 ? d.G : 0), d.B);
     const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
               *cc = static_cast<const TIn *>(Cm);
 #define SSD_CS_LAUNCH(NN)                                                                                      \
-    chunk_state_kernel<TIn, P, NN, FUSE, GR><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, d.L, \
-                                                                  d.H, d.G, d.Q, d.nc)
+    chunk_state_kernel<TIn, P, NN, FUSE, GR><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, o, \
+                                                                  d.L, d.H, d.G, d.Q, d.nc)
     switch (d.N) {
     case 32: SSD_CS_LAUNCH(32); break;
     case 64: SSD_CS_LAUNCH(64); break;
@@ -284,12 +285,13 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
 
 template <typename TIn, bool FUSE, int GR>
 static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
+                              float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                              hipStream_t s)
 {
     switch (d.P) {
-    case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
-    case 64: return launch_cs_n<TIn, 64, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
-    case 128: return launch_cs_n<TIn, 128, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    case 64: return launch_cs_n<TIn, 64, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    case 128: return launch_cs_n<TIn, 128, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -298,26 +300,28 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
                               float *states, const Dims &d, hipStream_t s)
 {
     float *ac = const_cast<float *>(acum), *dc = const_cast<float *>(dtc);  // read-only in this mode
-    return d.bf16 ? launch_cs_t<bf16_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, d, s)
-                  : launch_cs_t<float, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, d, s);
+    const SsdOpts o = {nullptr, 0, nullptr, 0};
+    return d.bf16 ? launch_cs_t<bf16_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s)
+                  : launch_cs_t<float, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s);
 }
 
 template <typename TIn>
 static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                                 float *dtc, float *states, const void *Cm, void *cb, const Dims &d, hipStream_t s)
+                                 float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                                 hipStream_t s)
 {
     // GEMM1 workgroups hold a whole chunk of B in LDS: size them by the chunk length
-    if (d.Q > 128) return launch_cs_t<TIn, true, 256>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
-    if (d.Q > 64) return launch_cs_t<TIn, true, 128>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
-    return launch_cs_t<TIn, true, 64>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    if (d.Q > 128) return launch_cs_t<TIn, true, 256>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    if (d.Q > 64) return launch_cs_t<TIn, true, 128>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    return launch_cs_t<TIn, true, 64>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
 }
 
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
                                            float *acum, float *dtc, float *states, const void *Cm, void *cb,
-                                           const Dims &d, hipStream_t s)
+                                           const SsdOpts &o, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s)
-                  : launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, d, s);
+    return d.bf16 ? launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)
+                  : launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
 }
 
 }  // namespace ssd

@@ -70,6 +70,49 @@ __device__ __forceinline__ f32x4 mfma16x16x4_f32(float a, float b, f32x4 c)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Options of the model-adjacent entry points (all off by default):
+//  - dt_bias / dt_softplus: the step size the recurrence uses is softplus(dt + bias)
+//    instead of the given dt ("Mamba-Family State-Space Model Kernels on a Programmable
+//    CGLA", Sec. III-A: dt comes out of the in-projection as a raw channel);
+//  - z: output gate, y <- y * z * sigmoid(z) (z is the in-projection's gate channel);
+//  - y_bf16: y is stored as bf16 (round to nearest even) instead of fp32.
+struct SsdOpts {
+    const float *dt_bias;
+    int dt_softplus;
+    const void *z;
+    int y_bf16;
+};
+
+// dt as the recurrence uses it, for a token inside the sequence (fp32)
+__device__ __forceinline__ float dt_effective(float d, const SsdOpts &o, int h)
+{
+    if (o.dt_bias) d += o.dt_bias[h];
+    if (o.dt_softplus) d = d > 20.f ? d : log1pf(expf(d));  // log(1 + e^d); past 20 it equals d in fp32
+    return d;
+}
+// z * sigmoid(z), through the hardware base-2 exponential and reciprocal (about 1 ulp
+// each); for z below about -88, exp(-z) overflows to inf and the result is -0
+__device__ __forceinline__ float silu(float v)
+{
+    return v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+// fp32 -> bf16, round to nearest even: gfx950's packed conversion (two values per
+// instruction; the first lands in the low half)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
+
+// the value of the lane next to this one (lanes 2k and 2k+1 swap), through a DPP quad
+// permutation (1, 0, 3, 2): a VALU operation, no LDS round trip
+__device__ __forceinline__ float swap_adjacent_lanes(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, true));
+}
+
 // Pack two fp32 values into one 32-bit word of two fp16 halves (RNE).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "ssd_common.h"
+
 namespace ssd {
 
 struct Dims {
@@ -21,7 +23,7 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
 // launch_chunk_cumsum), states, and the GEMM1 products cb (same as launch_chunk_gemm1).
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
                                            float *acum, float *dtc, float *states, const void *Cm, void *cb,
-                                           const Dims &d, hipStream_t s);
+                                           const SsdOpts &o, const Dims &d, hipStream_t s);
 hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
 // Step-1 GEMM1 once per (batch, group, chunk): cb holds B * G * nc * gemm1_steps_per_chunk(Q)
@@ -30,11 +32,11 @@ hipError_t launch_state_passing(float *states, const float *acum, const float *i
 int gemm1_steps_per_chunk(int q);
 hipError_t launch_chunk_gemm1(const void *Bm, const void *Cm, void *cb, const Dims &d, hipStream_t s);
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
-                             const float *dtc, const float *h_enter, const float *D, float *y,
-                             const Dims &d, hipStream_t s);
+                             const float *dtc, const float *h_enter, const float *D, void *y,
+                             const SsdOpts &o, const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
-                       const void *Cm, const float *D, float *y, const Dims &d, hipStream_t s);
+                       const void *Cm, const float *D, void *y, const SsdOpts &o, const Dims &d, hipStream_t s);
 
 }  // namespace ssd

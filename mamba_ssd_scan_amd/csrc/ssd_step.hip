@@ -7,6 +7,9 @@
 // independent of the sequence length; "Mamba-Family State-Space Model Kernels
 // on a Programmable CGLA", Sec. III-A: the recurrent-state update).
 //
+// Optional model-adjacent work (see SsdOpts): dt = softplus(dt + bias), the z gate
+// and bf16 storage of y.
+//
 // HBM-bound (0.5 flop per byte).  One 256-thread workgroup per (b, h).  A row
 // p of the state (N floats) is covered by N/4 adjacent lanes holding one
 // float4 each, so every access is a 16-byte coalesced load or store; all of
@@ -22,8 +25,8 @@ template <typename TIn, int N>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, const TIn *__restrict__ x,
                                                    const TIn *__restrict__ dt, const float *__restrict__ A,
                                                    const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
-                                                   const float *__restrict__ D, float *__restrict__ y,
-                                                   int H, int G, int P)
+                                                   const float *__restrict__ D, void *__restrict__ y,
+                                                   SsdOpts opt, int H, int G, int P)
 {
     constexpr int NQ = N / 4;          // lanes per state row (8, 16 or 32)
     constexpr int RP = 256 / NQ;       // rows per pass of the workgroup
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
     const int q = threadIdx.x % NQ;
     const int r0 = threadIdx.x / NQ;
 
-    const float dtv = load_in(dt + bh);
+    const float dtv = dt_effective(load_in(dt + bh), opt, h);
     const float r = exp_fast(dtv * A[h]);
     const float Dh = D ? D[h] : 0.f;
     float bv[4], cv[4];
@@ -69,33 +72,40 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
             float part = v.x * cv[0] + v.y * cv[1] + v.z * cv[2] + v.w * cv[3];
 #pragma unroll
             for (int off = NQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-            if (q == 0) y[(size_t)bh * P + p] = part + Dh * xs[k];
+            if (q == 0) {
+                float out = part + Dh * xs[k];
+                if (opt.z) out *= silu(load_in(static_cast<const TIn *>(opt.z) + (size_t)bh * P + p));
+                if (opt.y_bf16)
+                    static_cast<uint16_t *>(y)[(size_t)bh * P + p] = f32_to_bf16_rne(out);
+                else
+                    static_cast<float *>(y)[(size_t)bh * P + p] = out;
+            }
         }
     }
 }
 
 template <typename TIn>
 static hipError_t launch_step_t(float *state, const void *x, const void *dt, const float *A,
-                                const void *Bm, const void *Cm, const float *D, float *y,
-                                const Dims &d, hipStream_t s)
+                                const void *Bm, const void *Cm, const float *D, void *y,
+                                const SsdOpts &o, const Dims &d, hipStream_t s)
 {
     const dim3 grid(d.B * d.H);
     const TIn *xx = static_cast<const TIn *>(x), *dd = static_cast<const TIn *>(dt);
     const TIn *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
     switch (d.N) {
-    case 32: step_kernel<TIn, 32><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
-    case 64: step_kernel<TIn, 64><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
-    case 128: step_kernel<TIn, 128><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, d.H, d.G, d.P); break;
+    case 32: step_kernel<TIn, 32><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
+    case 64: step_kernel<TIn, 64><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
+    case 128: step_kernel<TIn, 128><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
-                       const void *Cm, const float *D, float *y, const Dims &d, hipStream_t s)
+                       const void *Cm, const float *D, void *y, const SsdOpts &o, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_step_t<bf16_t>(state, x, dt, A, Bm, Cm, D, y, d, s)
-                  : launch_step_t<float>(state, x, dt, A, Bm, Cm, D, y, d, s);
+    return d.bf16 ? launch_step_t<bf16_t>(state, x, dt, A, Bm, Cm, D, y, o, d, s)
+                  : launch_step_t<float>(state, x, dt, A, Bm, Cm, D, y, o, d, s);
 }
 
 }  // namespace ssd

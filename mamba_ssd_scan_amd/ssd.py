@@ -19,6 +19,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
+           "ssd_prefill_ex", "ssd_step_ex",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
            "ssd_chunk_gemm1", "ssd_chunk_scan")
 
@@ -52,6 +53,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_prefill.restype = i
     L.ssd_step.argtypes = [vp] * 8 + [i] * 6 + [vp]
     L.ssd_step.restype = i
+    L.ssd_prefill_ex.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [vp, sz, vp]
+    L.ssd_prefill_ex.restype = i
+    L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
+    L.ssd_step_ex.restype = i
     L.ssd_chunk_cumsum.argtypes = [vp] * 4 + [i] * 5 + [vp]
     L.ssd_chunk_cumsum.restype = i
     L.ssd_chunk_state.argtypes = [vp] * 5 + [i] * 8 + [vp]
@@ -167,6 +172,59 @@ def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=N
                              _ptr(final_state), _ptr(y), code, batch, seqlen, nheads, headdim, dstate, ngroups,
                              chunk, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill")
     return y, final_state
+
+
+def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_softplus=False, z=None,
+               y_dtype=None, chunk: int = 256, y=None, final_state="new", workspace=None, stream=None):
+    """ssd_prefill_ex: prefill with dt = softplus(dt + dt_bias) (or dt + dt_bias), the z gate
+    y * z * sigmoid(z), and y stored as float32 or bfloat16 (``y_dtype``, default float32).
+    Returns (y, final_state or None)."""
+    torch = _torch()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    code = _dtype_code(x)
+    for t in (dt, B, C, z):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("x, dt, B, C and z must share one dtype")
+    y_dtype = torch.float32 if y_dtype is None else y_dtype
+    ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+    _dev(x, dt, A, B, C, D, initial_state, y, workspace, dt_bias, z)
+    _f32(A, D, initial_state, dt_bias)
+    if y is None:
+        y = torch.empty((batch, seqlen, nheads, headdim), dtype=y_dtype, device=x.device)
+    elif y.dtype != y_dtype:
+        raise TypeError("y does not have y_dtype")
+    if isinstance(final_state, str):
+        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+    _dev(final_state)
+    _f32(final_state)
+    if workspace is None:
+        workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().ssd_prefill_ex(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+                                int(bool(dt_softplus)), _ptr(z), _ptr(initial_state), _ptr(final_state), _ptr(y),
+                                code, ycode, batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill_ex")
+    return y, final_state
+
+
+def step_ex(state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z=None, y_dtype=None, y=None,
+            stream=None):
+    """ssd_step_ex: one decode token with the options of prefill_ex; ``state`` is updated in place."""
+    torch = _torch()
+    batch, nheads, headdim, dstate = state.shape
+    ngroups = B.shape[1]
+    code = _dtype_code(x)
+    y_dtype = torch.float32 if y_dtype is None else y_dtype
+    ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+    _dev(state, x, dt, A, B, C, D, y, dt_bias, z)
+    _f32(state, A, D, dt_bias)
+    if y is None:
+        y = torch.empty((batch, nheads, headdim), dtype=y_dtype, device=x.device)
+    _check(lib().ssd_step_ex(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+                             int(bool(dt_softplus)), _ptr(z), _ptr(y), code, ycode, batch, nheads, headdim, dstate,
+                             ngroups, _stream(stream)), "ssd_step_ex")
+    return y
 
 
 def step(state, x, dt, A, B, C, D=None, *, y=None, stream=None):

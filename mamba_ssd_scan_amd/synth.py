@@ -193,6 +193,22 @@ def random_prefill(rng: np.random.Generator, batch, seqlen, nheads, headdim, dst
                 D=D, h0=h0, dtype=dtype)
 
 
+def option_inputs(rng: np.random.Generator, inp: dict) -> dict:
+    """Raw in-projection channels for the option entry points, shaped like ``inp``.
+
+    dt_raw ~ N(-3, 1) (the pre-softplus step-size channel, so that the effective
+    step size has the recipe's distribution when dt_bias is small), dt_bias [H] ~
+    N(0, 0.5^2) fp32, z ~ N(0, 1) laid out like x; dt_raw and z in inp's storage dtype.
+    """
+    f = np.float32
+    d = inp["dtype"]
+    H = inp["A"].shape[0]
+    dt_raw = rng.normal(-3.0, 1.0, size=inp["dt"].shape).astype(f)
+    bias = (0.5 * rng.standard_normal((H,))).astype(f)
+    z = rng.standard_normal(inp["x"].shape, dtype=f)
+    return dict(dt_raw=_store(dt_raw, d), dt_bias=bias, z=_store(z, d))
+
+
 def decode_inputs(shape: DecodeShape, seed: int, steps: Optional[int] = None) -> dict:
     """Per-step decode inputs for ``steps`` tokens plus the starting state.
 

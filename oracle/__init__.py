@@ -9,6 +9,8 @@ never imports it, and it never imports the product: the two share no code.
 * ``oracle.chunked``   -- fp64 chunked evaluation in the order of the method's
                           steps (intra-chunk, chunk states, inter-chunk
                           recurrence, off-diagonal output), numpy.
+* ``oracle.gated``     -- the model-adjacent options around the recurrence
+                          (dt = softplus(dt + bias), the z gate), fp64.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against
 closed forms, textbook special cases and invariants; see each module.

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
-    assert ssd.lib().ssd_version() >> 16 == 2
+    assert ssd.lib().ssd_version() >> 16 == 2 and ssd.lib().ssd_version() & 0xffff >= 1
 
 
 def gemm1_steps(q):
@@ -103,6 +103,40 @@ def test_step_rejects_before_launch():
     assert st(nheads=3, ngroups=2) == INV
     assert st(batch=0) == INV
     assert st(x=P0 + 1) == INV
+
+
+def test_option_entry_points_reject_before_launch():
+    L = ssd.lib()
+    base = dict(x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, bias=None, sp=1, z=None, h0=None, hT=None, y=P0, dtype=BF,
+                ydtype=F, batch=1, seqlen=300, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, ws=P0,
+                wsb=1 << 30, stream=None)
+
+    def pf(**kw):
+        a = dict(base, **kw)
+        return L.ssd_prefill_ex(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["bias"], a["sp"], a["z"],
+                                a["h0"], a["hT"], a["y"], a["dtype"], a["ydtype"], a["batch"], a["seqlen"],
+                                a["nheads"], a["headdim"], a["dstate"], a["ngroups"], a["chunk"], a["ws"],
+                                a["wsb"], a["stream"])
+    assert pf(ydtype=5) == INV                 # bad y dtype
+    assert pf(dtype=5) == INV
+    assert pf(bias=P0 + 2) == INV              # misaligned dt_bias
+    assert pf(z=P0 + 1) == INV                 # misaligned z (bf16 needs 2-byte alignment)
+    assert pf(chunk=48) == UNS
+    assert pf(ws=None) == WS
+    assert pf(x=None) == INV
+    assert pf(seqlen=0, y=None) == 0               # empty sequence, no final state: nothing to launch
+    def st(**kw):
+        a = dict(state=P0, x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, bias=None, sp=0, z=None, y=P0, dtype=BF, ydtype=F,
+                 batch=2, nheads=4, headdim=64, dstate=64, ngroups=1, stream=None)
+        a.update(kw)
+        return L.ssd_step_ex(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["bias"], a["sp"],
+                             a["z"], a["y"], a["dtype"], a["ydtype"], a["batch"], a["nheads"], a["headdim"],
+                             a["dstate"], a["ngroups"], a["stream"])
+    assert st(ydtype=9) == INV
+    assert st(y=None) == INV
+    assert st(y=P0 + 2) == INV                 # fp32 y must be 4-byte aligned
+    assert st(z=P0 + 1) == INV
+    assert st(headdim=48) == UNS
 
 
 def test_stage_entry_points_reject_before_launch():
