@@ -278,6 +278,13 @@ def bench_decode(torch, steps, flush):
         ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
 
     us_cold, _ = time_launches(torch, one, min(64, steps), flush=flush)
+    # the same tokens as one HIP graph (ssd_decode_graph): one launch for all of them
+    y_all = torch.empty((steps, s.batch, s.nheads, s.headdim), dtype=torch.float32, device="cuda")
+    graph = ssd.DecodeGraph(state, xs, dts, A, Bs, Cs, D, y=y_all)
+    graph.launch()
+    torch.cuda.synchronize()
+    us_graph = time_back_to_back(torch, graph.launch, 3) / steps
+    graph.close()
     nbytes = decode_bytes_per_step(s)
     traffic = counter_traffic("step_kernel", synth.WORKLOAD_NAMES[DECODE_WORKLOAD])
     return {
@@ -288,9 +295,65 @@ def bench_decode(torch, steps, flush):
         "hbm_frac": nbytes / (us_loop * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "cold_us_per_step": us_cold, "cold_gbps": nbytes / (us_cold * 1e-6) / 1e9,
         "cold_hbm_frac": nbytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "graph_us_per_step": us_graph, "graph_gbps": nbytes / (us_graph * 1e-6) / 1e9,
         "note": "us_per_step: 1024 back-to-back ssd_step launches on one state (the 168 MB state can stay in "
-                "the 256 MiB Infinity Cache between steps); cold: 512 MiB cache eviction before each step",
+                "the 256 MiB Infinity Cache between steps); cold: 512 MiB cache eviction before each step; "
+                "graph: the 1024 tokens as one ssd_decode_graph launch (per-token outputs in their own slots)",
     }
+
+
+def time_back_to_back(torch, fn, n):
+    """Mean duration (us) of ``fn`` over n back-to-back launches between two events (warm caches)."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
+    """Per generated token at a ``context``-token context, batch 1, for the five Mamba-2 shapes:
+    cached decode (the state carried over; ``ntok`` tokens as one decode graph, and as eager
+    ssd_step launches) against full-prefix recomputation (an ssd_prefill over context + 1 tokens,
+    whose last output is the new token's).  Both warm, back to back."""
+    out = {}
+    for name, H in synth.MAMBA2_LADDER.items():
+        s = synth.PrefillShape(1, context + 1, H, 64, 128, 1, 256, "bf16")
+        inp = synth.prefill_inputs(s, synth.SEED_BASE + 100 + H)
+        g = prefill_buffers(torch, s, inp)
+        run_prefill(g, s)
+        torch.cuda.synchronize()
+        us_re = time_back_to_back(torch, lambda: run_prefill(g, s), reps)
+        ds = synth.DecodeShape(1, H, 64, 128, 1, ntok, "bf16")
+        dinp = synth.decode_inputs(ds, synth.SEED_BASE + 200 + H)
+        xs, dts = synth.to_torch(dinp["x"], "bf16"), synth.to_torch(dinp["dt"], "bf16")
+        Bs, Cs = synth.to_torch(dinp["B"], "bf16"), synth.to_torch(dinp["C"], "bf16")
+        state = g["final"].clone()  # the cached state after the prefix
+        graph = ssd.DecodeGraph(state, xs, dts, g["A"], Bs, Cs, g["D"])
+        graph.launch()
+        torch.cuda.synchronize()
+        us_graph = time_back_to_back(torch, graph.launch, max(2, reps // 4)) / ntok
+        graph.close()
+        y1 = torch.empty((1, H, 64), dtype=torch.float32, device="cuda")
+        k = [0]
+
+        def eager():
+            t = k[0] % ntok
+            k[0] += 1
+            ssd.step(state, xs[t], dts[t], g["A"], Bs[t], Cs[t], g["D"], y=y1)
+        eager()
+        torch.cuda.synchronize()
+        us_eager = time_back_to_back(torch, eager, ntok)
+        out[name] = {"nheads": H, "recompute_us": us_re, "cached_graph_us": us_graph, "cached_eager_us": us_eager,
+                     "speedup_graph": us_re / us_graph, "speedup_eager": us_re / us_eager}
+        del g, xs, dts, Bs, Cs, state
+    return {"context": context, "batch": 1, "headdim": 64, "dstate": 128, "chunk": 256, "dtype": "bf16",
+            "tokens_per_graph": ntok, "models": out,
+            "note": "SSD layer core only (one layer, no projections): per-token time of cached decode vs an "
+                    "ssd_prefill over the whole prefix plus the token; warm, back-to-back launches"}
 
 
 # ---------------------------------------------------------------------------- main
@@ -306,7 +369,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
-                                       "chunk_cumsum_kernel", "chunk_gemm1_kernel", "step", "copy"],
+                                       "chunk_cumsum_kernel", "chunk_gemm1_kernel", "step", "cached", "copy"],
                     help="profiling aid: launch only this work --steps times (cold), print nothing else")
     args = ap.parse_args()
 
@@ -340,6 +403,9 @@ def main():
         return 0
     if args.only == "step":
         print(json.dumps(bench_decode(torch, args.decode_steps, flush)))
+        return 0
+    if args.only == "cached":
+        print(json.dumps(bench_cached_vs_recompute(torch)))
         return 0
 
     inp = synth.prefill_inputs(s, synth.SEED_BASE + args.workload)
@@ -424,6 +490,7 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, args.decode_steps, flush)
+        out["cached_vs_recompute"] = bench_cached_vs_recompute(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, inp)
     print(json.dumps(out))

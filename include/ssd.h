@@ -23,6 +23,8 @@
  * - The caller owns all memory.  The library never allocates or frees device
  *   memory and keeps no device state; scratch comes from the caller's
  *   workspace.  No global mutable state: calls are reentrant and thread-safe.
+ *   The one object the library creates is a decode graph, owned by the
+ *   caller through its handle (ssd_decode_graph_create / _destroy).
  * - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
  *   stream) and return after enqueueing; nothing synchronises inside.
  * - Errors are negative return codes, never exceptions.  Every argument is
@@ -140,6 +142,47 @@ int ssd_step_ex(float *state, const void *x, const void *dt, const float *A,
                 int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
                 ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
                 int ngroups, void *hip_stream);
+
+/*
+ * A decode loop of `nsteps` tokens captured once as a HIP graph and replayed
+ * with one launch ("Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching for Inference", abstract: the autoregressive loop is
+ * compiled to run on the device, carrying the cached state from token to
+ * token).  Token t is ssd_step_ex on slot t of step-major buffers
+ *
+ *   x, z [nsteps, B, H, P] in_dtype   dt [nsteps, B, H] in_dtype
+ *   Bm, Cm [nsteps, B, G, N] in_dtype   y [nsteps, B, H, P] y_dtype (written)
+ *
+ * with state [B, H, P, N] fp32 updated in place token after token, and A, D,
+ * dt_bias, dt_softplus as in ssd_step_ex.  The graph holds the pointers, not the
+ * values: the caller may rewrite the inputs and the state between launches, and
+ * keeps every buffer allocated until ssd_decode_graph_destroy.
+ *
+ * ssd_decode_graph_create validates like ssd_step_ex (plus 1 <= nsteps <=
+ * SSD_DECODE_GRAPH_MAX_STEPS), captures the tokens on a private stream of the
+ * current device and stores the handle in *out (NULL on any error).  It
+ * allocates the graph objects (host memory, and the HIP runtime's own kernel
+ * argument storage); nothing is launched.  SSD_ERR_HIP: capture or
+ * instantiation failed.
+ * ssd_decode_graph_launch enqueues the nsteps tokens on hip_stream, after the
+ * work already queued there.  The current device must be the one the handle
+ * was created on (else SSD_ERR_INVALID_ARG).  Launches of one handle write the
+ * same state and y: launches that may overlap in time (different streams with
+ * no ordering between them) race.
+ * ssd_decode_graph_steps returns nsteps (0 for NULL).
+ * ssd_decode_graph_destroy frees the handle (NULL: no-op); call it once no
+ * launch of the handle is pending.
+ */
+#define SSD_DECODE_GRAPH_MAX_STEPS 65536
+typedef struct ssd_decode_graph ssd_decode_graph;
+int ssd_decode_graph_create(ssd_decode_graph **out, int nsteps, float *state, const void *x,
+                            const void *dt, const float *A, const void *Bm, const void *Cm,
+                            const float *D, const float *dt_bias, int dt_softplus,
+                            const void *z, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype,
+                            int batch, int nheads, int headdim, int dstate, int ngroups);
+int ssd_decode_graph_launch(ssd_decode_graph *g, void *hip_stream);
+int ssd_decode_graph_steps(const ssd_decode_graph *g);
+int ssd_decode_graph_destroy(ssd_decode_graph *g);
 
 /* ---- Stage entry points (the kernels ssd_prefill runs, in this order:
  *      chunk_cumsum + chunk_state (fused), state_passing, chunk_gemm1, chunk_scan) ---- */

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <new>
+
 #include "ssd_launch.h"
 
 namespace {
@@ -78,6 +80,23 @@ ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// Argument checks of one decode token (ssd_step_ex and every token of a decode graph).
+int check_step_args(const float *state, const void *x, const void *dt, const float *A, const void *Bm,
+                    const void *Cm, const float *D, const float *dt_bias, const void *z, const void *y,
+                    ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
+                    int ngroups)
+{
+    if (check_dtype(in_dtype) != SSD_OK || check_dtype(y_dtype) != SSD_OK) return SSD_ERR_INVALID_ARG;
+    const int st = check_shape(batch, -1, nheads, headdim, dstate, ngroups, 0, false);
+    if (st != SSD_OK) return st;
+    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, es) || !aligned(Bm, es) || !aligned(Cm, es) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, in_size(y_dtype)) || !aligned(dt_bias, 4) || !aligned(z, es))
+        return SSD_ERR_INVALID_ARG;
+    return SSD_OK;
+}
+
 #define SSD_TRY(expr)                      \
     do {                                   \
         const int _s = (expr);             \
@@ -107,7 +126,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (2 << 16) | 1; }
+int ssd_version(void) { return (2 << 16) | 2; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -248,14 +267,8 @@ int ssd_step_ex(float *state, const void *x, const void *dt, const float *A, con
                 const float *D, const float *dt_bias, int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
                 ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate, int ngroups, void *hip_stream)
 {
-    SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_dtype(y_dtype));
-    SSD_TRY(check_shape(batch, -1, nheads, headdim, dstate, ngroups, 0, false));
-    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
-    const size_t es = in_size(in_dtype);
-    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, es) || !aligned(Bm, es) || !aligned(Cm, es) ||
-        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, in_size(y_dtype)) || !aligned(dt_bias, 4) || !aligned(z, es))
-        return SSD_ERR_INVALID_ARG;
+    SSD_TRY(check_step_args(state, x, dt, A, Bm, Cm, D, dt_bias, z, y, in_dtype, y_dtype, batch, nheads, headdim,
+                            dstate, ngroups));
     const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
     const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
     return hip_status(ssd::launch_step(state, x, dt, A, Bm, Cm, D, y, o, d, (hipStream_t)hip_stream));
@@ -267,6 +280,85 @@ int ssd_step(float *state, const void *x, const void *dt, const float *A, const 
 {
     return ssd_step_ex(state, x, dt, A, Bm, Cm, D, nullptr, 0, nullptr, y, in_dtype, SSD_F32, batch, nheads, headdim,
                        dstate, ngroups, hip_stream);
+}
+
+// ---- decode loop as one HIP graph
+
+struct ssd_decode_graph {
+    hipGraphExec_t exec;
+    int device;
+    int nsteps;
+};
+
+int ssd_decode_graph_create(ssd_decode_graph **out, int nsteps, float *state, const void *x, const void *dt,
+                            const float *A, const void *Bm, const void *Cm, const float *D, const float *dt_bias,
+                            int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype,
+                            int batch, int nheads, int headdim, int dstate, int ngroups)
+{
+    if (!out) return SSD_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (nsteps < 1 || nsteps > SSD_DECODE_GRAPH_MAX_STEPS) return SSD_ERR_INVALID_ARG;
+    SSD_TRY(check_step_args(state, x, dt, A, Bm, Cm, D, dt_bias, z, y, in_dtype, y_dtype, batch, nheads, headdim,
+                            dstate, ngroups));
+    // Byte strides of one token's slot in the step-major buffers.
+    const size_t es = in_size(in_dtype);
+    const size_t sx = (size_t)batch * nheads * headdim * es, sdt = (size_t)batch * nheads * es;
+    const size_t sbc = (size_t)batch * ngroups * dstate * es;
+    const size_t sy = (size_t)batch * nheads * headdim * in_size(y_dtype);
+    const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
+
+    int dev = 0;
+    SSD_TRY(hip_status(hipGetDevice(&dev)));
+    hipStream_t s = nullptr;
+    SSD_TRY(hip_status(hipStreamCreateWithFlags(&s, hipStreamNonBlocking)));
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        hipError_t le = hipSuccess;
+        for (int t = 0; t < nsteps && le == hipSuccess; ++t) {
+            const char *zt = z ? static_cast<const char *>(z) + t * sx : nullptr;
+            const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, zt, y_dtype == SSD_BF16 ? 1 : 0};
+            le = ssd::launch_step(state, static_cast<const char *>(x) + t * sx, static_cast<const char *>(dt) + t * sdt,
+                                  A, static_cast<const char *>(Bm) + t * sbc, static_cast<const char *>(Cm) + t * sbc,
+                                  D, static_cast<char *>(y) + t * sy, o, d, s);
+        }
+        e = hipStreamEndCapture(s, &graph);  // always ends the capture, also after a failed launch
+        if (le != hipSuccess) e = le;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(s);
+    if (e != hipSuccess) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        return SSD_ERR_HIP;
+    }
+    ssd_decode_graph *g = new (std::nothrow) ssd_decode_graph{exec, dev, nsteps};
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        return SSD_ERR_HIP;
+    }
+    *out = g;
+    return SSD_OK;
+}
+
+int ssd_decode_graph_launch(ssd_decode_graph *g, void *hip_stream)
+{
+    if (!g) return SSD_ERR_INVALID_ARG;
+    int dev = -1;
+    SSD_TRY(hip_status(hipGetDevice(&dev)));
+    if (dev != g->device) return SSD_ERR_INVALID_ARG;
+    return hip_status(hipGraphLaunch(g->exec, (hipStream_t)hip_stream));
+}
+
+int ssd_decode_graph_steps(const ssd_decode_graph *g) { return g ? g->nsteps : 0; }
+
+int ssd_decode_graph_destroy(ssd_decode_graph *g)
+{
+    if (!g) return SSD_OK;
+    const hipError_t e = hipGraphExecDestroy(g->exec);
+    delete g;
+    return hip_status(e);
 }
 
 }  // extern "C"

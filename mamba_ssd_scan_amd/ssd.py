@@ -20,6 +20,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
            "ssd_prefill_ex", "ssd_step_ex",
+           "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
            "ssd_chunk_gemm1", "ssd_chunk_scan")
 
@@ -57,6 +58,14 @@ def lib() -> ctypes.CDLL:
     L.ssd_prefill_ex.restype = i
     L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
     L.ssd_step_ex.restype = i
+    L.ssd_decode_graph_create.argtypes = [ctypes.POINTER(vp), i] + [vp] * 8 + [i] + [vp] * 2 + [i] * 7
+    L.ssd_decode_graph_create.restype = i
+    L.ssd_decode_graph_launch.argtypes = [vp, vp]
+    L.ssd_decode_graph_launch.restype = i
+    L.ssd_decode_graph_steps.argtypes = [vp]
+    L.ssd_decode_graph_steps.restype = i
+    L.ssd_decode_graph_destroy.argtypes = [vp]
+    L.ssd_decode_graph_destroy.restype = i
     L.ssd_chunk_cumsum.argtypes = [vp] * 4 + [i] * 5 + [vp]
     L.ssd_chunk_cumsum.restype = i
     L.ssd_chunk_state.argtypes = [vp] * 5 + [i] * 8 + [vp]
@@ -240,6 +249,78 @@ def step(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
     _check(lib().ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), code,
                           batch, nheads, headdim, dstate, ngroups, _stream(stream)), "ssd_step")
     return y
+
+
+class DecodeGraph:
+    """ssd_decode_graph_*: ``nsteps`` decode tokens captured once as a HIP graph.
+
+    Token t runs ssd_step_ex on slot t of the step-major inputs x [T,B,H,P], dt [T,B,H],
+    B/C [T,B,G,N], z [T,B,H,P] and writes y [T,B,H,P]; ``state`` [B,H,P,N] is updated in
+    place token after token.  The graph keeps the buffers' addresses: rewrite their
+    contents between launches, never reallocate them.  The tensors are referenced here
+    so they outlive the graph.
+    """
+
+    def __init__(self, state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z=None, y_dtype=None,
+                 y=None):
+        torch = _torch()
+        self._handle = None
+        nsteps, batch, nheads, headdim = x.shape
+        dstate = state.shape[3]
+        ngroups = B.shape[2]
+        if tuple(state.shape) != (batch, nheads, headdim, dstate):
+            raise ValueError("state must be [B,H,P,N] matching x [T,B,H,P]")
+        if tuple(dt.shape) != (nsteps, batch, nheads) or tuple(B.shape) != (nsteps, batch, ngroups, dstate) \
+                or tuple(C.shape) != tuple(B.shape) or (z is not None and tuple(z.shape) != tuple(x.shape)):
+            raise ValueError("step-major inputs must be x [T,B,H,P], dt [T,B,H], B/C [T,B,G,N], z like x")
+        code = _dtype_code(x)
+        for t in (dt, B, C, z):
+            if t is not None and _dtype_code(t) != code:
+                raise TypeError("x, dt, B, C and z must share one dtype")
+        y_dtype = torch.float32 if y_dtype is None else y_dtype
+        ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+        _dev(state, x, dt, A, B, C, D, y, dt_bias, z)
+        _f32(state, A, D, dt_bias)
+        if y is None:
+            y = torch.empty(tuple(x.shape), dtype=y_dtype, device=x.device)
+        elif tuple(y.shape) != tuple(x.shape) or y.dtype != y_dtype:
+            raise ValueError("y must be [T,B,H,P] of y_dtype")
+        self.y = y
+        self._keep = (state, x, dt, A, B, C, D, dt_bias, z, y)
+        self.device = x.device
+        h = ctypes.c_void_p()
+        with torch.cuda.device(x.device):
+            _check(lib().ssd_decode_graph_create(ctypes.byref(h), nsteps, _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
+                                                 _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), int(bool(dt_softplus)),
+                                                 _ptr(z), _ptr(y), code, ycode, batch, nheads, headdim, dstate,
+                                                 ngroups), "ssd_decode_graph_create")
+        self._handle = h
+        self.nsteps = lib().ssd_decode_graph_steps(h)
+
+    def launch(self, stream=None):
+        """Enqueue the nsteps tokens on ``stream`` (default: the current stream); returns y."""
+        if self._handle is None:
+            raise RuntimeError("decode graph is closed")
+        torch = _torch()
+        with torch.cuda.device(self.device):
+            _check(lib().ssd_decode_graph_launch(self._handle, _stream(stream)), "ssd_decode_graph_launch")
+        return self.y
+
+    def close(self):
+        """Destroy the graph once no launch is pending (synchronises the device first)."""
+        if self._handle is not None:
+            torch = _torch()
+            with torch.cuda.device(self.device):
+                torch.cuda.synchronize()
+                _check(lib().ssd_decode_graph_destroy(self._handle), "ssd_decode_graph_destroy")
+            self._handle = None
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---- stage entry points (for unit tests and per-kernel timing)

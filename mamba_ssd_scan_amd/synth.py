@@ -65,6 +65,13 @@ WORKLOADS = {
     4: DecodeShape(64, 80, 64, 128, 1, 1024, "bf16"),
 }
 
+# Head counts of the five Mamba-2 checkpoints (130M .. 2.7B) on which cached decode is
+# compared with full-prefix recomputation at a 4096-token context ("Compiler-First
+# State Space Duality and Portable O(1) Autoregressive Caching for Inference",
+# abstract).  Every one has headdim 64, d_state 128 and one B/C group per layer;
+# the head count is 2 * d_model / 64.
+MAMBA2_LADDER = {"130m": 24, "370m": 32, "780m": 48, "1.3b": 64, "2.7b": 80}
+
 WORKLOAD_NAMES = {
     0: "tiny-f32-prefill-b1-l256-h4-p64-n64-q64",
     1: "mamba2-130m-prefill-b1-l4096-h24-p64-n128-q256",

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
-    assert ssd.lib().ssd_version() >> 16 == 2 and ssd.lib().ssd_version() & 0xffff >= 1
+    assert ssd.lib().ssd_version() >> 16 == 2 and ssd.lib().ssd_version() & 0xffff >= 2
 
 
 def gemm1_steps(q):
@@ -137,6 +137,38 @@ def test_option_entry_points_reject_before_launch():
     assert st(y=P0 + 2) == INV                 # fp32 y must be 4-byte aligned
     assert st(z=P0 + 1) == INV
     assert st(headdim=48) == UNS
+
+
+def test_decode_graph_rejects_before_capture():
+    """ssd_decode_graph_create validates everything before any HIP call and leaves *out NULL."""
+    import ctypes
+    L = ssd.lib()
+
+    def mk(**kw):
+        a = dict(n=8, state=P0, x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, bias=None, sp=0, z=None, y=P0, dtype=BF,
+                 ydtype=F, batch=2, nheads=4, headdim=64, dstate=64, ngroups=1)
+        a.update(kw)
+        h = ctypes.c_void_p(P0)  # must come back NULL
+        rc = L.ssd_decode_graph_create(ctypes.byref(h), a["n"], a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"],
+                                       a["D"], a["bias"], a["sp"], a["z"], a["y"], a["dtype"], a["ydtype"],
+                                       a["batch"], a["nheads"], a["headdim"], a["dstate"], a["ngroups"])
+        assert h.value is None, "handle must be NULL after a rejected create"
+        return rc
+    assert mk(n=0) == INV
+    assert mk(n=65537) == INV                   # above SSD_DECODE_GRAPH_MAX_STEPS
+    assert mk(state=None) == INV
+    assert mk(state=P0 + 4) == INV              # the state needs 16-byte alignment
+    assert mk(z=P0 + 1) == INV
+    assert mk(ydtype=3) == INV
+    assert mk(headdim=48) == UNS
+    assert mk(nheads=6, ngroups=4) == INV
+    assert L.ssd_decode_graph_create(None, 8, P0, P0, P0, P0, P0, P0, None, None, 0, None, P0, BF, F, 2, 4, 64, 64,
+                                     1) == INV
+    assert L.ssd_decode_graph_launch(None, None) == INV
+    assert L.ssd_decode_graph_steps(None) == 0
+    assert L.ssd_decode_graph_destroy(None) == 0
+    m = re.search(r"#define SSD_DECODE_GRAPH_MAX_STEPS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == 65536
 
 
 def test_stage_entry_points_reject_before_launch():
