@@ -59,7 +59,8 @@ def alg_counts(s: synth.PrefillShape) -> dict:
     bc = B * L * G * N * ib            # one of B or C
     y = B * L * H * P * 4
     chunk_tab = 2 * B * H * nc * Q * 4  # dA_cum + dt regrouped per chunk
-    states = B * H * nc * P * N * 4
+    states = B * H * nc * P * N * ib   # chunk / entering states: fp16 for bf16 inputs, fp32 otherwise
+    hen = states
     st = B * H * P * N * 4
     h0 = st if s.init_state != "zero" else 0
     tri = Q * (Q + 1)                  # 2 flops x Q(Q+1)/2 pairs
@@ -72,7 +73,7 @@ def alg_counts(s: synth.PrefillShape) -> dict:
         "chunk_state_kernel": dict(bytes=x + bc + chunk_tab + states, flops=2 * B * H * L * P * N),
         "state_passing_kernel": dict(bytes=2 * states + B * H * nc * 4 + h0 + st, flops=2 * B * H * nc * P * N),
         "chunk_gemm1_kernel": dict(bytes=2 * bc + cb, flops=B * nc * G * N * tri),
-        "chunk_scan_kernel": dict(bytes=x + bc + cb + chunk_tab + states + y,
+        "chunk_scan_kernel": dict(bytes=x + bc + cb + chunk_tab + hen + y,
                                   flops=B * nc * H * P * tri + 2 * B * H * L * P * N),
     }
     fused_bytes = x + dt + 2 * bc + y + st + h0
@@ -181,7 +182,10 @@ def prefill_buffers(torch, s, inp):
     g["ws"] = ssd.alloc_workspace(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk)
     g["acum"] = torch.empty((s.batch, s.nheads, nc, s.chunk), dtype=torch.float32, device="cuda")
     g["dtc"] = torch.empty_like(g["acum"])
-    g["states"] = torch.empty((s.batch, s.nheads, nc, s.headdim, s.dstate), dtype=torch.float32, device="cuda")
+    # chunk states, then (in place) entering states: fp16 for bf16 inputs, fp32 otherwise
+    g["states"] = torch.empty((s.batch, s.nheads, nc, s.headdim, s.dstate),
+                              dtype=torch.float16 if s.dtype == "bf16" else torch.float32, device="cuda")
+    g["hen"] = g["states"]
     g["cb"] = torch.empty(ssd.chunk_gemm1_size(s.batch, s.seqlen, s.ngroups, s.chunk) // 4, dtype=torch.float32,
                           device="cuda")
     return g
@@ -193,6 +197,7 @@ def run_prefill(g, s):
 
 
 def stage_fns(torch, g, s):
+    """The launches of the prefill for this input type, each callable on its own."""
     Q = s.chunk
     pristine = {}
 
@@ -212,7 +217,7 @@ def stage_fns(torch, g, s):
         ssd.chunk_gemm1(g["B"], g["C"], chunk=Q, cb=g["cb"])
 
     def scan():
-        ssd.chunk_scan(g["x"], g["C"], g["cb"], g["acum"], g["dtc"], g["states"], g["D"], chunk=Q, y=g["y"])
+        ssd.chunk_scan(g["x"], g["C"], g["cb"], g["acum"], g["dtc"], g["hen"], g["D"], chunk=Q, y=g["y"])
 
     cumsum()
     cstate()

@@ -72,7 +72,8 @@ int ssd_version(void);
  * invalid/unsupported shapes.  Layout (each region 256-byte aligned):
  *   dA_cum  [B, H, nc, Q] fp32   per-chunk inclusive cumsum of dt*A
  *   dt_c    [B, H, nc, Q] fp32   dt regrouped per chunk (0 past seqlen)
- *   states  [B, H, nc, P, N] fp32  chunk states, then entering states
+ *   states  [B, H, nc, P, N] x 4 bytes: the chunk states, then the entering
+ *           states (fp16 for bf16 inputs -- half the region -- fp32 for fp32 inputs)
  *   cb      ssd_chunk_gemm1_size(B, L, G, Q) bytes: the C.B^T products
  * with nc = ceil(seqlen / Q).
  */
@@ -184,8 +185,9 @@ int ssd_decode_graph_launch(ssd_decode_graph *g, void *hip_stream);
 int ssd_decode_graph_steps(const ssd_decode_graph *g);
 int ssd_decode_graph_destroy(ssd_decode_graph *g);
 
-/* ---- Stage entry points (the kernels ssd_prefill runs, in this order:
- *      chunk_cumsum + chunk_state (fused), state_passing, chunk_gemm1, chunk_scan) ---- */
+/* ---- Stage entry points (the kernels ssd_prefill runs, in this order: chunk_cumsum +
+ *      chunk_state + chunk_gemm1 in one launch, state_passing, chunk_scan).  The chunk
+ *      and entering states between them are fp16 for bf16 inputs and fp32 for fp32 inputs. ---- */
 
 /*
  * Step-0: per-chunk inclusive cumulative sum of dt*A (wavefront prefix scan).
@@ -201,10 +203,11 @@ int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c,
  * Step-2: chunk states, the state each chunk alone leaves from a zero start:
  *   states[b,h,c] = sum_j exp(dA_cum[c][Q-1] - dA_cum[c][j]) * dt_c[c][j] * x_j B_j^T
  *   x [B, L, H, P], Bm [B, L, G, N] in_dtype; dA_cum, dt_c as written by
- *   ssd_chunk_cumsum; states [B, H, nc, P, N] fp32 (written).
+ *   ssd_chunk_cumsum; states [B, H, nc, P, N] (written): fp32 accumulation, stored
+ *   fp32 for fp32 inputs and rounded once to fp16 for bf16 inputs.
  */
 int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const float *dt_c,
-                    float *states, ssd_dtype_t in_dtype, int batch, int seqlen,
+                    void *states, ssd_dtype_t in_dtype, int batch, int seqlen,
                     int nheads, int headdim, int dstate, int ngroups, int chunk,
                     void *hip_stream);
 
@@ -213,10 +216,13 @@ int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const fl
  *   run = initial_state (or 0); for c: tmp = states[c]; states[c] = run;
  *   run = exp(dA_cum[c][Q-1]) * run + tmp.   final_state = run (if non-NULL;
  *   may alias initial_state).  On return states[c] holds the state entering chunk c.
+ *   states [B, H, nc, P, N]: fp16 when in_dtype is SSD_BF16, fp32 when SSD_F32 (the
+ *   type ssd_chunk_state writes for that input type); the carry `run` is fp32 and
+ *   each entering state is rounded once when stored.
  */
-int ssd_state_passing(float *states, const float *dA_cum, const float *initial_state,
-                      float *final_state, int batch, int nheads, int headdim, int dstate,
-                      int nchunks, int chunk, void *hip_stream);
+int ssd_state_passing(void *states, const float *dA_cum, const float *initial_state,
+                      float *final_state, ssd_dtype_t in_dtype, int batch, int nheads,
+                      int headdim, int dstate, int nchunks, int chunk, void *hip_stream);
 
 /*
  * Step-1 GEMM1 ("Mamba-Family State-Space Model Kernels on a Programmable
@@ -236,11 +242,12 @@ int ssd_chunk_gemm1(const void *Bm, const void *Cm, float *cb, ssd_dtype_t in_dt
  * Step-1 mask + GEMM2, Step-4 and skip: the output of every chunk,
  *   y_i = sum_{j<=i} G_c[i, j] exp(dA_cum[i] - dA_cum[j]) dt_c[j] x_j        (intra-chunk)
  *       + exp(dA_cum[i]) * H_enter C_i  + D_h x_i                           (off-diagonal, skip)
- *   cb: ssd_chunk_gemm1 output for the same B/C; h_enter [B, H, nc, P, N]
- *   fp32: entering states (ssd_state_passing output); y [B, L, H, P] fp32 (written).
+ *   cb: ssd_chunk_gemm1 output for the same B/C; h_enter [B, H, nc, P, N]: the
+ *   entering states (ssd_state_passing output), fp16 for bf16 inputs and fp32 for
+ *   fp32 inputs; y [B, L, H, P] fp32 (written).
  */
 int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *dA_cum,
-                   const float *dt_c, const float *h_enter, const float *D, float *y,
+                   const float *dt_c, const void *h_enter, const float *D, float *y,
                    ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
                    int dstate, int ngroups, int chunk, void *hip_stream);
 

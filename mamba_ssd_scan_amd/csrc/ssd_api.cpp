@@ -126,7 +126,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (2 << 16) | 2; }
+int ssd_version(void) { return (3 << 16) | 0; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -149,7 +149,7 @@ int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c,
     return hip_status(ssd::launch_chunk_cumsum(dt, A, dA_cum, dt_c, d, (hipStream_t)hip_stream));
 }
 
-int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const float *dt_c, float *states,
+int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const float *dt_c, void *states,
                     ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim, int dstate,
                     int ngroups, int chunk, void *hip_stream)
 {
@@ -162,14 +162,15 @@ int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const fl
     return hip_status(ssd::launch_chunk_state(x, Bm, dA_cum, dt_c, states, d, (hipStream_t)hip_stream));
 }
 
-int ssd_state_passing(float *states, const float *dA_cum, const float *initial_state, float *final_state,
-                      int batch, int nheads, int headdim, int dstate, int nchunks, int chunk,
-                      void *hip_stream)
+int ssd_state_passing(void *states, const float *dA_cum, const float *initial_state, float *final_state,
+                      ssd_dtype_t in_dtype, int batch, int nheads, int headdim, int dstate, int nchunks,
+                      int chunk, void *hip_stream)
 {
+    SSD_TRY(check_dtype(in_dtype));
     if (nchunks < 0) return SSD_ERR_INVALID_ARG;
     SSD_TRY(check_shape(batch, nchunks, nheads, headdim, dstate, 1, chunk, true));
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
-    const ssd::Dims d = make_dims(batch, nchunks * chunk, nheads, headdim, dstate, 1, chunk, SSD_F32);
+    const ssd::Dims d = make_dims(batch, nchunks * chunk, nheads, headdim, dstate, 1, chunk, in_dtype);
     hipStream_t s = (hipStream_t)hip_stream;
     if (nchunks == 0) {
         if (final_state)
@@ -200,7 +201,7 @@ int ssd_chunk_gemm1(const void *Bm, const void *Cm, float *cb, ssd_dtype_t in_dt
 }
 
 int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *dA_cum, const float *dt_c,
-                   const float *h_enter, const float *D, float *y, ssd_dtype_t in_dtype, int batch,
+                   const void *h_enter, const float *D, float *y, ssd_dtype_t in_dtype, int batch,
                    int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
@@ -243,7 +244,7 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
     char *ws = static_cast<char *>(workspace);
     float *acum = reinterpret_cast<float *>(ws + w.acum);
     float *dtc = reinterpret_cast<float *>(ws + w.dtc);
-    float *states = reinterpret_cast<float *>(ws + w.states);
+    void *states = ws + w.states;
     float *cb = reinterpret_cast<float *>(ws + w.cb);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 

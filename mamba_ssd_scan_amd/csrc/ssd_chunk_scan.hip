@@ -51,9 +51,9 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
     static constexpr int HSZ = F32 ? 1 : P * LDH;
     static constexpr int TAB = ROWS + 32;              // tables padded past the last step
     static constexpr int base = XSZ * (int)sizeof(op_t) + HSZ * 2 + 3 * TAB * 4;
-    // raw staging: X rows, entering state, dA_cum and dt, and 1 KB that absorbs the
+    // raw staging: X rows, fp16 entering state, dA_cum and dt, and 1 KB that absorbs the
     // surplus loads of wavefronts with less to stream (every wavefront issues the same count)
-    static constexpr int SX = ROWS * P * 2, SH = P * N * 4, ST = 2 * ROWS * 4, SD = 1024;
+    static constexpr int SX = ROWS * P * 2, SH = P * N * 2, ST = 2 * ROWS * 4, SD = 1024;
     static constexpr int SALL = SX + SH + ST + SD;
     static constexpr bool STAGE = !F32 && base + SALL <= 160 * 1024;
     static constexpr int bytes = base + (STAGE ? SALL : 0);
@@ -64,7 +64,7 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
 template <typename TIn, int P, int N, int NW, bool OPT>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ Cm, const void *__restrict__ cbg,
-    const float *__restrict__ acum, const float *__restrict__ dtc, const float *__restrict__ hen,
+    const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
     const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int Q, int nc,
     int nitems)
 {
@@ -153,6 +153,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
                                  (uint32_t)(row * H * P * 2 + col));
             }
+            const f16 *hen = static_cast<const f16 *>(henv);
             const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + it.bhc * P * N, live ? (uint32_t)S::SH : 0u);
 #pragma unroll
             for (int k = 0; k < (HI + NW - 1) / NW; ++k) {
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         const int ir = min(32 * (tid >> 5) + 31, Q - 1);
         if constexpr (STAGE) {
             const bf16_t *sx = reinterpret_cast<const bf16_t *>(stg);
-            const float *sh = reinterpret_cast<const float *>(stg + S::SX);
+            const f16 *sh = reinterpret_cast<const f16 *>(stg + S::SX);
             const float *st = reinterpret_cast<const float *>(stg + S::SX + S::SH);
 #pragma unroll
             for (int k = 0; k < XPT; ++k) {
@@ -195,16 +196,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
             for (int k = 0; k < HPT; ++k) {
                 const int u = tid + k * NT;
-                if (u < HU) {
-                    const float4 h0 = *reinterpret_cast<const float4 *>(sh + 8 * u);
-                    const float4 h1 = *reinterpret_cast<const float4 *>(sh + 8 * u + 4);
-                    uint4 w;
-                    w.x = pack_f16x2(h0.x, h0.y);
-                    w.y = pack_f16x2(h0.z, h0.w);
-                    w.z = pack_f16x2(h1.x, h1.y);
-                    w.w = pack_f16x2(h1.z, h1.w);
-                    *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = w;
-                }
+                if (u < HU)
+                    *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) =
+                        *reinterpret_cast<const uint4 *>(sh + 8 * u);
             }
             if (tid < Q) {
                 ta = st[tid];
@@ -214,7 +208,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         } else {
             const __amdgpu_buffer_rsrc_t rx = x_rsrc(it);
             Raw8<TIn> px[XPT][XR];
-            float4 ph[HPT][2];
+            uint4 ph[HPT];
 #pragma unroll
             for (int k = 0; k < XPT; ++k) {
                 const int u = tid + k * NT;
@@ -225,14 +219,11 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 }
             }
             if constexpr (!F32) {
-                const float *hp = hen + it.bhc * P * N;
+                const f16 *hp = static_cast<const f16 *>(henv) + it.bhc * P * N;
 #pragma unroll
                 for (int k = 0; k < HPT; ++k) {
                     const int u = tid + k * NT;
-                    if (u < HU) {
-                        ph[k][0] = *reinterpret_cast<const float4 *>(hp + 8 * u);
-                        ph[k][1] = *reinterpret_cast<const float4 *>(hp + 8 * u + 4);
-                    }
+                    if (u < HU) ph[k] = *reinterpret_cast<const uint4 *>(hp + 8 * u);
                 }
             }
             if (tid < Q) {
@@ -260,14 +251,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
                 for (int k = 0; k < HPT; ++k) {
                     const int u = tid + k * NT;
-                    if (u < HU) {
-                        uint4 w;
-                        w.x = pack_f16x2(ph[k][0].x, ph[k][0].y);
-                        w.y = pack_f16x2(ph[k][0].z, ph[k][0].w);
-                        w.z = pack_f16x2(ph[k][1].x, ph[k][1].y);
-                        w.w = pack_f16x2(ph[k][1].z, ph[k][1].w);
-                        *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = w;
-                    }
+                    if (u < HU) *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = ph[k];
                 }
             }
         }
@@ -482,7 +466,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             // ---- Step-4: exp(a_i) * (C_i . H_enter[p, :]) for this wavefront's rows, in its
             // own accumulator, added scaled
             {
-                const float *hp = hen + cur.bhc * P * N;
+                const float *hp = static_cast<const float *>(henv) + cur.bhc * P * N;  // fp32 inputs only
                 f32x4 off[TP];
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) off[pt] = zero4();
@@ -560,7 +544,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 
 template <typename TIn, int P>
 static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, const float *acum,
-                                const float *dtc, const float *hen, const float *D, void *y,
+                                const float *dtc, const void *hen, const float *D, void *y,
                                 const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     // persistent: enough workgroups for 16 wavefronts per compute unit, each looping over
@@ -600,7 +584,7 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
 
 template <typename TIn>
 static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, const float *acum,
-                                const float *dtc, const float *hen, const float *D, void *y,
+                                const float *dtc, const void *hen, const float *D, void *y,
                                 const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     switch (d.P) {
@@ -612,7 +596,7 @@ static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, 
 }
 
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
-                             const float *dtc, const float *h_enter, const float *D, void *y,
+                             const float *dtc, const void *h_enter, const float *D, void *y,
                              const SsdOpts &o, const Dims &d, hipStream_t s)
 {
     int dev = 0, ncu = 0;

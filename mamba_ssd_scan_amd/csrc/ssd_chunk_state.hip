@@ -19,6 +19,11 @@
 // tiles for the 16x16x4 fp32 path.)  Two blocks of global loads are kept in
 // flight in registers ahead of the block being contracted; LDS is
 // double-buffered with one barrier per block.
+//
+// With bf16 inputs S_c is stored in fp16 (fp32 accumulation, one rounding at
+// the end): the chunk states and the entering states made from them travel
+// between the kernels at half the bytes, and the chunk-scan kernel feeds the
+// entering state to the matrix cores in fp16 anyway.
 #include "ssd_common.h"
 #include "ssd_gemm1_body.h"
 #include "ssd_launch.h"
@@ -39,7 +44,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                                                           const float *__restrict__ A,
                                                           float *__restrict__ acum,
                                                           float *__restrict__ dtc,
-                                                          float *__restrict__ states,
+                                                          void *__restrict__ states,
                                                           const TIn *__restrict__ Cm, void *__restrict__ cb,
                                                           SsdOpts opt, int L, int H, int G, int Q, int nc)
 {
@@ -162,11 +167,13 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                 const int t = wave + 4 * tt;
                 if (t < NT) {
                     const int pt = t / TN, nt = t % TN;
+                    // S^T tiles: the B rows are the A operand, so a lane's accumulator holds
+                    // four consecutive state columns n of one row p (contiguous stores)
                     if constexpr (F32) {
                         const op_t *xa = &xs[buf][(pt * 16 + li) * LDT + ks];
                         const op_t *ba = &bs[buf][(nt * 16 + li) * LDT + ks];
 #pragma unroll
-                        for (int s = 0; s < 8; ++s) acc[tt] = mfma16x16x4_f32(xa[4 * s + lg], ba[4 * s + lg], acc[tt]);
+                        for (int s = 0; s < 8; ++s) acc[tt] = mfma16x16x4_f32(ba[4 * s + lg], xa[4 * s + lg], acc[tt]);
                     } else {
                         // reduction slots of lane group lg: tokens ks + 4 lg + r and ks + 16 + 4 lg + r
                         const int ox = tr16_offset(lane, ks, pt * 16, LDXR);
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                         const f16x4 b1 = lds_read_tr16(&bs[buf][ob + 16 * LDBR]);
                         const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
                         const f16x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                        acc[tt] = mfma16x16x32_f16(a, bb, acc[tt]);
+                        acc[tt] = mfma16x16x32_f16(bb, a, acc[tt]);
                     }
                 }
             }
@@ -249,22 +256,30 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
         }
     }
 
-    // ---- write S_c [P][N]: lane holds rows p = 16 pt + 4 lg + r of column n = 16 nt + li
-    float *out = states + bhc * P * N;
+    // ---- write S_c [P][N] (fp32, or fp16 for bf16 inputs): lane holds columns
+    // n = 16 nt + 4 lg + r of row p = 16 pt + li
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int t = wave + 4 * tt;
         if (t < NT) {
             const int pt = t / TN, nt = t % TN;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[(size_t)(pt * 16 + 4 * lg + r) * N + nt * 16 + li] = acc[tt][r];
+            const size_t e = bhc * P * N + (size_t)(pt * 16 + li) * N + nt * 16 + 4 * lg;
+            if constexpr (F32) {
+                *reinterpret_cast<float4 *>(static_cast<float *>(states) + e) =
+                    make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+            } else {
+                uint2 v;
+                v.x = pack_f16x2(acc[tt][0], acc[tt][1]);
+                v.y = pack_f16x2(acc[tt][2], acc[tt][3]);
+                *reinterpret_cast<uint2 *>(static_cast<f16 *>(states) + e) = v;
+            }
         }
     }
 }
 
 template <typename TIn, int P, bool FUSE, int GR>
 static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                              float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                               hipStream_t s)
 {
     const dim3 grid(d.nc, d.H + (GR > 0 ? d.G : 0), d.B);
@@ -285,7 +300,7 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
 
 template <typename TIn, bool FUSE, int GR>
 static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                              float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                              float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                               hipStream_t s)
 {
     switch (d.P) {
@@ -297,7 +312,7 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, con
 }
 
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
-                              float *states, const Dims &d, hipStream_t s)
+                              void *states, const Dims &d, hipStream_t s)
 {
     float *ac = const_cast<float *>(acum), *dc = const_cast<float *>(dtc);  // read-only in this mode
     const SsdOpts o = {nullptr, 0, nullptr, 0};
@@ -307,7 +322,7 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
 
 template <typename TIn>
 static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
-                                 float *dtc, float *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
+                                 float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                                  hipStream_t s)
 {
     // GEMM1 workgroups hold a whole chunk of B in LDS: size them by the chunk length
@@ -317,7 +332,7 @@ static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, 
 }
 
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
-                                           float *acum, float *dtc, float *states, const void *Cm, void *cb,
+                                           float *acum, float *dtc, void *states, const void *Cm, void *cb,
                                            const SsdOpts &o, const Dims &d, hipStream_t s)
 {
     return d.bf16 ? launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)

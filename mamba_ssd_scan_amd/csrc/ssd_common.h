@@ -83,12 +83,17 @@ struct SsdOpts {
     int y_bf16;
 };
 
-// dt as the recurrence uses it, for a token inside the sequence (fp32)
+// dt as the recurrence uses it, for a token inside the sequence (fp32), with the head's
+// bias already read
+__device__ __forceinline__ float dt_effective_b(float d, float bias, int softplus)
+{
+    d += bias;
+    if (softplus) d = d > 20.f ? d : log1pf(expf(d));  // log(1 + e^d); past 20 it equals d in fp32
+    return d;
+}
 __device__ __forceinline__ float dt_effective(float d, const SsdOpts &o, int h)
 {
-    if (o.dt_bias) d += o.dt_bias[h];
-    if (o.dt_softplus) d = d > 20.f ? d : log1pf(expf(d));  // log(1 + e^d); past 20 it equals d in fp32
-    return d;
+    return dt_effective_b(d, o.dt_bias ? o.dt_bias[h] : 0.f, o.dt_softplus);
 }
 // z * sigmoid(z), through the hardware base-2 exponential and reciprocal (about 1 ulp
 // each); for z below about -88, exp(-z) overflows to inf and the result is -0

@@ -17,22 +17,25 @@ struct Dims {
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, float *dtc,
                                const Dims &d, hipStream_t s);
+// states: [B, H, nc, P, N], fp16 for bf16 inputs (d.bf16), fp32 otherwise; likewise below.
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
-                              float *states, const Dims &d, hipStream_t s);
+                              void *states, const Dims &d, hipStream_t s);
 // Step-0 and Step-1 GEMM1 fused into the Step-2 launch: writes acum/dtc (same values as
 // launch_chunk_cumsum), states, and the GEMM1 products cb (same as launch_chunk_gemm1).
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
-                                           float *acum, float *dtc, float *states, const void *Cm, void *cb,
+                                           float *acum, float *dtc, void *states, const void *Cm, void *cb,
                                            const SsdOpts &o, const Dims &d, hipStream_t s);
-hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
+hipError_t launch_state_passing(void *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
 // Step-1 GEMM1 once per (batch, group, chunk): cb holds B * G * nc * gemm1_steps_per_chunk(Q)
 // slices of 512 values, fp16 for bf16 inputs and fp32 for fp32 inputs (fragment order, see
 // ssd_chunk_gemm1.hip).
 int gemm1_steps_per_chunk(int q);
 hipError_t launch_chunk_gemm1(const void *Bm, const void *Cm, void *cb, const Dims &d, hipStream_t s);
+// h_enter: entering states [B, H, nc, P, N], fp16 for bf16 inputs (the off-diagonal
+// operand precision), fp32 for fp32 inputs.
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
-                             const float *dtc, const float *h_enter, const float *D, void *y,
+                             const float *dtc, const void *h_enter, const float *D, void *y,
                              const SsdOpts &o, const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);

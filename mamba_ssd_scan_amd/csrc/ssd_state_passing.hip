@@ -7,9 +7,10 @@
 // the per-chunk update of the [P, N] state is a per-head scalar scale plus an
 // add, not a dense matrix-vector product).
 //
-// HBM-bound: each thread owns four consecutive fp32 state elements of one
-// (b, h) and walks the chunks in order, reading S_c and writing the entering
-// state in place (16-byte coalesced accesses).  The loads of the next kUnroll
+// HBM-bound: each thread owns four consecutive state elements of one (b, h)
+// and walks the chunks in order, reading S_c and writing the entering state in
+// place (16-byte coalesced accesses for fp32 states, 8-byte for the fp16 states
+// of bf16 inputs; the carry itself is fp32).  The loads of the next kUnroll
 // chunks are issued before any of their results is needed, so many loads are
 // in flight per thread while the dependent scale-add chain runs.
 #include "ssd_common.h"
@@ -20,16 +21,34 @@ namespace ssd {
 constexpr int kPassThreads = 64;
 constexpr int kUnroll = 16;
 
+// Four consecutive stored state elements <-> fp32 (the carry is always fp32).
+__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const f16 *p)
+{
+    const f16x4 v = *reinterpret_cast<const f16x4 *>(p);
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+__device__ __forceinline__ void store4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+__device__ __forceinline__ void store4(f16 *p, float4 v)
+{
+    uint2 u;
+    u.x = pack_f16x2(v.x, v.y);
+    u.y = pack_f16x2(v.z, v.w);
+    *reinterpret_cast<uint2 *>(p) = u;
+}
+
+// T: element type of the chunk / entering states in memory (fp32, or fp16 for bf16 inputs)
+template <typename T>
 __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
-    float *__restrict__ states, const float *__restrict__ acum, const float *init,
+    T *__restrict__ states, const float *__restrict__ acum, const float *init,
     float *fin, int H, int nc, int Q, int PN4)
 {
-    const int e = blockIdx.x * kPassThreads + threadIdx.x;  // float4 index inside one [P, N] state
+    const int e = blockIdx.x * kPassThreads + threadIdx.x;  // group of 4 elements inside one [P, N] state
     const int h = blockIdx.y, b = blockIdx.z;
     if (e >= PN4) return;
     const size_t bh = (size_t)b * H + h;
     float4 run = init ? reinterpret_cast<const float4 *>(init)[bh * PN4 + e] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 *st = reinterpret_cast<float4 *>(states) + bh * nc * (size_t)PN4 + e;
+    T *st = states + (bh * nc * (size_t)PN4 + e) * 4;
     const float *ac = acum + bh * nc * (size_t)Q + (Q - 1);
 
     int c = 0;
@@ -38,12 +57,12 @@ __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
         float dec[kUnroll];
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            s[k] = st[(size_t)(c + k) * PN4];
+            s[k] = load4(st + (size_t)(c + k) * PN4 * 4);
             dec[k] = ac[(size_t)(c + k) * Q];
         }
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            st[(size_t)(c + k) * PN4] = run;
+            store4(st + (size_t)(c + k) * PN4 * 4, run);
             const float r = exp_fast(dec[k]);
             run.x = fmaf(r, run.x, s[k].x);
             run.y = fmaf(r, run.y, s[k].y);
@@ -52,8 +71,8 @@ __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
         }
     }
     for (; c < nc; ++c) {
-        const float4 s = st[(size_t)c * PN4];
-        st[(size_t)c * PN4] = run;
+        const float4 s = load4(st + (size_t)c * PN4 * 4);
+        store4(st + (size_t)c * PN4 * 4, run);
         const float r = exp_fast(ac[(size_t)c * Q]);
         run.x = fmaf(r, run.x, s.x);
         run.y = fmaf(r, run.y, s.y);
@@ -63,12 +82,17 @@ __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
     if (fin) reinterpret_cast<float4 *>(fin)[bh * PN4 + e] = run;
 }
 
-hipError_t launch_state_passing(float *states, const float *acum, const float *init, float *fin,
+hipError_t launch_state_passing(void *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s)
 {
     const int PN4 = d.P * d.N / 4;
     dim3 grid((PN4 + kPassThreads - 1) / kPassThreads, d.H, d.B);
-    state_passing_kernel<<<grid, kPassThreads, 0, s>>>(states, acum, init, fin, d.H, d.nc, d.Q, PN4);
+    if (d.bf16)
+        state_passing_kernel<f16><<<grid, kPassThreads, 0, s>>>(static_cast<f16 *>(states), acum, init, fin, d.H,
+                                                               d.nc, d.Q, PN4);
+    else
+        state_passing_kernel<float><<<grid, kPassThreads, 0, s>>>(static_cast<float *>(states), acum, init, fin,
+                                                                 d.H, d.nc, d.Q, PN4);
     return hipGetLastError();
 }
 

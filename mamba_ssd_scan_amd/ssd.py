@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_cumsum.restype = i
     L.ssd_chunk_state.argtypes = [vp] * 5 + [i] * 8 + [vp]
     L.ssd_chunk_state.restype = i
-    L.ssd_state_passing.argtypes = [vp] * 4 + [i] * 6 + [vp]
+    L.ssd_state_passing.argtypes = [vp] * 4 + [i] * 7 + [vp]
     L.ssd_state_passing.restype = i
     L.ssd_chunk_gemm1_size.argtypes = [i] * 4
     L.ssd_chunk_gemm1_size.restype = sz
@@ -340,28 +340,43 @@ def chunk_cumsum(dt, A, *, chunk: int, acum=None, dtc=None, stream=None):
     return acum, dtc
 
 
+def _state_dtype(x):
+    """Element type of the chunk / entering states for inputs like ``x``."""
+    torch = _torch()
+    return torch.float16 if x.dtype == torch.bfloat16 else torch.float32
+
+
 def chunk_state(x, B, acum, dtc, *, chunk: int, states=None, stream=None):
+    """Chunk states [B,H,nc,P,N]: float16 for bfloat16 inputs, float32 for float32 inputs."""
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
     nc = nchunks(seqlen, chunk)
     _dev(x, B, acum, dtc, states)
     if states is None:
-        states = torch.empty((batch, nheads, nc, headdim, dstate), dtype=torch.float32, device=x.device)
+        states = torch.empty((batch, nheads, nc, headdim, dstate), dtype=_state_dtype(x), device=x.device)
+    elif states.dtype != _state_dtype(x):
+        raise TypeError(f"states must be {_state_dtype(x)} for {x.dtype} inputs")
     _check(lib().ssd_chunk_state(_ptr(x), _ptr(B), _ptr(acum), _ptr(dtc), _ptr(states), _dtype_code(x), batch, seqlen,
                                  nheads, headdim, dstate, ngroups, chunk, _stream(stream)), "ssd_chunk_state")
     return states
 
 
 def state_passing(states, acum, initial_state=None, *, chunk: int, final_state="new", stream=None):
-    """In place: ``states`` [B,H,nc,P,N] becomes the entering states.  Returns final_state."""
+    """In place: ``states`` [B,H,nc,P,N] (float16 or float32) becomes the entering states.  Returns final_state."""
     torch = _torch()
     batch, nheads, nc, headdim, dstate = states.shape
     _dev(states, acum, initial_state)
+    if states.dtype == torch.float16:
+        code = SSD_BF16
+    elif states.dtype == torch.float32:
+        code = SSD_F32
+    else:
+        raise TypeError("states must be float16 (bfloat16 inputs) or float32 (float32 inputs)")
     if isinstance(final_state, str):
         final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=states.device)
-    _check(lib().ssd_state_passing(_ptr(states), _ptr(acum), _ptr(initial_state), _ptr(final_state), batch, nheads,
-                                   headdim, dstate, nc, chunk, _stream(stream)), "ssd_state_passing")
+    _check(lib().ssd_state_passing(_ptr(states), _ptr(acum), _ptr(initial_state), _ptr(final_state), code, batch,
+                                   nheads, headdim, dstate, nc, chunk, _stream(stream)), "ssd_state_passing")
     return final_state
 
 
@@ -388,10 +403,14 @@ def chunk_gemm1(B, C, *, chunk: int, cb=None, stream=None):
 
 
 def chunk_scan(x, C, cb, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stream=None):
+    """``h_enter`` [B,H,nc,P,N]: float16 for bfloat16 inputs, float32 for float32 inputs."""
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = C.shape[2], C.shape[3]
     _dev(x, C, cb, acum, dtc, h_enter, D, y)
+    want = torch.float16 if x.dtype == torch.bfloat16 else torch.float32
+    if h_enter.dtype != want:
+        raise TypeError(f"h_enter must be {want} for {x.dtype} inputs")
     if y is None:
         y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
     _check(lib().ssd_chunk_scan(_ptr(x), _ptr(C), _ptr(cb), _ptr(acum), _ptr(dtc), _ptr(h_enter), _ptr(D), _ptr(y),

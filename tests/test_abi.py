@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
-    assert ssd.lib().ssd_version() >> 16 == 2 and ssd.lib().ssd_version() & 0xffff >= 2
+    assert ssd.lib().ssd_version() >> 16 == 3
 
 
 def gemm1_steps(q):
@@ -178,9 +178,10 @@ def test_stage_entry_points_reject_before_launch():
     assert L.ssd_chunk_cumsum(P0, P0, P0 + 4, P0, BF, 1, 100, 4, 64, None) == INV
     assert L.ssd_chunk_state(P0, P0, P0, P0, None, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
     assert L.ssd_chunk_state(P0, P0, P0, P0, P0, BF, 1, 100, 4, 64, 96, 1, 64, None) == UNS
-    assert L.ssd_state_passing(None, P0, None, None, 1, 4, 64, 64, 3, 64, None) == INV
-    assert L.ssd_state_passing(P0, P0, None, None, 1, 4, 64, 64, -1, 64, None) == INV
-    assert L.ssd_state_passing(P0, P0, P0 + 4, None, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_state_passing(None, P0, None, None, BF, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_state_passing(P0, P0, None, None, BF, 1, 4, 64, 64, -1, 64, None) == INV
+    assert L.ssd_state_passing(P0, P0, P0 + 4, None, F, 1, 4, 64, 64, 3, 64, None) == INV
+    assert L.ssd_state_passing(P0, P0, None, None, 7, 1, 4, 64, 64, 3, 64, None) == INV   # bad state dtype
     assert L.ssd_chunk_gemm1(None, P0, P0, BF, 1, 100, 64, 1, 64, None) == INV
     assert L.ssd_chunk_gemm1(P0, P0, P0 + 4, BF, 1, 100, 64, 1, 64, None) == INV
     assert L.ssd_chunk_gemm1(P0, P0, P0, BF, 1, 100, 96, 1, 64, None) == UNS
