@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
     constexpr bool F32 = Tr::kF32;
-    constexpr int JB = F32 ? 32 : 64;                   // tokens per staged block
+    constexpr int JB = 32;                              // tokens per staged block
     // bf16 inputs: row-major fp16 tiles; a pitch of (width + 16) halves puts the 16
     // rows one transposing read touches on distinct bank groups.
     constexpr int LDXR = P + 16, LDBR = N + 16;

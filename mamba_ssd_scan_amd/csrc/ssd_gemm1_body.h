@@ -17,7 +17,10 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
     static constexpr int LDB = N + (F32 ? 4 : 8);  // row pitch: 16 rows read together hit distinct banks
     static constexpr int KS = F32 ? N / 4 : N / 32;
     static constexpr int NT = 64 * NWAVES;
-    static constexpr int kLdsBytes = ROWS * LDB * (int)sizeof(raw_t);
+    // B rows are held in LDS 128 at a time: a 32-column step reads rows 32s .. 32s+31, so
+    // every step lies in one pass and each output slice is still formed once.
+    static constexpr int PASS_ROWS = ROWS < 128 ? ROWS : 128;
+    static constexpr int kLdsBytes = PASS_ROWS * LDB * (int)sizeof(raw_t);
     static constexpr int TPW = NWAVES == 4 ? 4 : 1;  // row tiles per wavefront
 
     // row tile of slot k of wavefront w (-1: none), for nt 16-row tiles
@@ -70,35 +73,52 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
         const int t0 = tile_of(wave, 0, nt);
         if (t0 >= 0) load_c(t0);
 
-        // B rows of the whole chunk -> LDS (rows past the chunk or the sequence read as
-        // zeros); a fixed trip count keeps every load in flight before the first store
-        constexpr int BU = ROWS * (N / 8), BPT = (BU + NT - 1) / NT;
-        Raw8<TIn> bv[BPT];
+        const int spc = (nt & 1) ? ((nt >> 1) + 1) * ((nt >> 1) + 1) : (nt >> 1) * ((nt >> 1) + 1);
+        const size_t chunk0 = (((size_t)b * G + g) * nc + c) * (size_t)spc;  // the chunk's first slice
+        const int npass = (16 * nt + PASS_ROWS - 1) / PASS_ROWS;  // 1 or 2
+        // B rows of both passes are requested at once (rows past the chunk or the sequence
+        // read as zeros; a fixed trip count keeps every load in flight): the second pass's
+        // rows wait in registers while the first pass computes.
+        constexpr int BU = PASS_ROWS * (N / 8), BPT = (BU + NT - 1) / NT;
+        constexpr int NPASS_MAX = ROWS > 128 ? 2 : 1;
+        Raw8<TIn> bv[NPASS_MAX][BPT];
+#pragma unroll
+        for (int q = 0; q < NPASS_MAX; ++q)
+#pragma unroll
+            for (int k = 0; k < BPT; ++k) {
+                const int u = tid + k * NT;
+                if (u < BU) {
+                    if (q < npass)
+                        bv[q][k].load(rb, (uint32_t)((q * PASS_ROWS + u / (N / 8)) * G * N + 8 * (u % (N / 8))));
+                    else
+                        bv[q][k].zero();
+                }
+            }
+#pragma unroll
+        for (int pass = 0; pass < NPASS_MAX; ++pass) {
+        if (pass >= npass) break;
+        const int r0 = pass * PASS_ROWS;  // first B row held in LDS during this pass
+        if (pass > 0) __syncthreads();    // the previous pass's readers are done with the rows
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
             const int u = tid + k * NT;
-            if (u < BU) bv[k].load(rb, (uint32_t)((u / (N / 8)) * G * N + 8 * (u % (N / 8))));
-        }
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int u = tid + k * NT;
-            if (u < BU) bv[k].store(&bs[(u / (N / 8)) * LDB + 8 * (u % (N / 8))]);
+            if (u < BU) bv[pass][k].store(&bs[(u / (N / 8)) * LDB + 8 * (u % (N / 8))]);
         }
         __syncthreads();
 
-        const int spc = (nt & 1) ? ((nt >> 1) + 1) * ((nt >> 1) + 1) : (nt >> 1) * ((nt >> 1) + 1);
-        const size_t chunk0 = (((size_t)b * G + g) * nc + c) * (size_t)spc;  // the chunk's first slice
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int t = tile_of(wave, k, nt);
             if (t < 0) continue;
-            if (k > 0) load_c(t);
+            if (k > 0 || pass > 0) load_c(t);
             const int ibase = 16 * t;
             const int Tt = (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
             const int ns = (ibase + 15) / 32 + 1;
-            for (int s = 0; s < ns; ++s) {
-                const int jb = 32 * s;
-                const bool has1 = jb + 16 <= ibase + 15;  // second 16-column half not entirely above the diagonal
+            // this pass's steps of the tile: columns 32 s in [r0, r0 + PASS_ROWS)
+            const int s_lo = r0 / 32, s_hi = min(ns, (r0 + PASS_ROWS) / 32);
+            for (int s = s_lo; s < s_hi; ++s) {
+                const int jb = 32 * s - r0;  // LDS row of the step's first column
+                const bool has1 = 32 * s + 16 <= ibase + 15;  // second 16-column half not entirely above the diagonal
                 f32x4 d0 = zero4(), d1 = zero4();
                 if constexpr (F32) {
 #pragma unroll
@@ -144,6 +164,7 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
                 }
             }
         }
+        }  // pass
     }
 };
 
