@@ -37,7 +37,10 @@ namespace ssd {
 // the grid (blockIdx.y < G) are GEMM1 workgroups, one per (b, group, chunk), which
 // form C.B^T into `cb` while the chunk-state workgroups (blockIdx.y = G + h) run;
 // they come first in the grid so that they are dispatched first.
-template <typename TIn, int P, int N, bool FUSE_CUMSUM, int GR>
+// JBT: tokens per staged block.  32 keeps LDS small enough for four workgroups per
+// CU (grids with many workgroups); 64 halves the barriers when the whole grid is
+// resident at once anyway (two workgroups per CU).
+template <typename TIn, int P, int N, bool FUSE_CUMSUM, int GR, int JBT>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict__ x,
                                                           const TIn *__restrict__ Bm,
                                                           const TIn *__restrict__ dt,
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
     constexpr bool F32 = Tr::kF32;
-    constexpr int JB = 32;                              // tokens per staged block
+    constexpr int JB = Traits<TIn>::kF32 ? 32 : JBT;   // tokens per staged block
     // bf16 inputs: row-major fp16 tiles; a pitch of (width + 16) halves puts the 16
     // rows one transposing read touches on distinct bank groups.
     constexpr int LDXR = P + 16, LDBR = N + 16;
@@ -280,20 +283,26 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 template <typename TIn, int P, bool FUSE, int GR>
 static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
                               float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
-                              hipStream_t s)
+                              bool big, hipStream_t s)
 {
     const dim3 grid(d.nc, d.H + (GR > 0 ? d.G : 0), d.B);
     const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
               *cc = static_cast<const TIn *>(Cm);
-#define SSD_CS_LAUNCH(NN)                                                                                      \
-    chunk_state_kernel<TIn, P, NN, FUSE, GR><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, o, \
-                                                                  d.L, d.H, d.G, d.Q, d.nc)
+#define SSD_CS_LAUNCH(NN, JJ)                                                                                      \
+    chunk_state_kernel<TIn, P, NN, FUSE, GR, JJ><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, o, \
+                                                                      d.L, d.H, d.G, d.Q, d.nc)
+#define SSD_CS_BY_JB(NN)          \
+    if (big || sizeof(TIn) == 4)  \
+        SSD_CS_LAUNCH(NN, 32);    \
+    else                          \
+        SSD_CS_LAUNCH(NN, 64)
     switch (d.N) {
-    case 32: SSD_CS_LAUNCH(32); break;
-    case 64: SSD_CS_LAUNCH(64); break;
-    case 128: SSD_CS_LAUNCH(128); break;
+    case 32: SSD_CS_BY_JB(32); break;
+    case 64: SSD_CS_BY_JB(64); break;
+    case 128: SSD_CS_BY_JB(128); break;
     default: return hipErrorInvalidValue;
     }
+#undef SSD_CS_BY_JB
 #undef SSD_CS_LAUNCH
     return hipGetLastError();
 }
@@ -303,10 +312,18 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, con
                               float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                               hipStream_t s)
 {
+    // More workgroups than two per compute unit: the smaller staged blocks (more resident
+    // workgroups) pay off; otherwise the larger ones (fewer barriers).
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long nwg = (long)d.nc * (d.H + (GR > 0 ? d.G : 0)) * d.B;
+    const bool big = nwg > 2L * (ncu > 0 ? ncu : 1);
     switch (d.P) {
-    case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
-    case 64: return launch_cs_n<TIn, 64, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
-    case 128: return launch_cs_n<TIn, 128, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, big, s);
+    case 64: return launch_cs_n<TIn, 64, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, big, s);
+    case 128: return launch_cs_n<TIn, 128, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, big, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -325,7 +342,7 @@ static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, 
                                  float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                                  hipStream_t s)
 {
-    // GEMM1 workgroups hold a whole chunk of B in LDS: size them by the chunk length
+    // GEMM1 workgroups hold up to 128 rows of the chunk's B in LDS: size them by the chunk length
     if (d.Q > 128) return launch_cs_t<TIn, true, 256>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     if (d.Q > 64) return launch_cs_t<TIn, true, 128>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     return launch_cs_t<TIn, true, 64>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
