@@ -32,6 +32,7 @@ int check_shape(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     if (!supported_dim(headdim) || !supported_dim(dstate)) return SSD_ERR_UNSUPPORTED;
     if (need_chunk && !supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
     if (batch > 65535 || nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y/z limits
+    if (need_chunk && (long long)nheads + 4LL * ngroups > 65535) return SSD_ERR_UNSUPPORTED;  // chunk-state grid y
     if ((long long)batch * nheads > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     // One chunk of x or B/C is addressed with 32-bit byte offsets inside the kernels.
     if (need_chunk && (long long)chunk * 4 * ((long long)nheads * headdim > (long long)ngroups * dstate

@@ -33,10 +33,11 @@ namespace ssd {
 // Step-0 fused in (FUSE_CUMSUM): one wavefront scans this chunk's dt*A (as the
 // stand-alone cumulative-decay kernel does) and writes dA_cum / dt_c for the
 // later stages, instead of reading them; the other wavefronts start loading.
-// Step-1 GEMM1 fused in (GR > 0, chunks of up to GR tokens): the first G rows of
-// the grid (blockIdx.y < G) are GEMM1 workgroups, one per (b, group, chunk), which
-// form C.B^T into `cb` while the chunk-state workgroups (blockIdx.y = G + h) run;
-// they come first in the grid so that they are dispatched first.
+// Step-1 GEMM1 fused in (GR > 0, chunks of up to GR tokens): the first 4G rows of
+// the grid (blockIdx.y < 4G) are GEMM1 workgroups, four per (b, group, chunk), each
+// forming a balanced quarter of the chunk's row tiles of C.B^T into `cb`, while the
+// chunk-state workgroups (blockIdx.y = 4G + h) run; they come first in the grid so
+// that they are dispatched first.
 // JBT: tokens per staged block.  32 keeps LDS small enough for four workgroups per
 // CU (grids with many workgroups); 64 halves the barriers when the whole grid is
 // resident at once anyway (two workgroups per CU).
@@ -70,8 +71,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     constexpr int kBytes = (GR > 0 && G1::kLdsBytes > kStateBytes) ? G1::kLdsBytes : kStateBytes;
     __shared__ __align__(16) unsigned char smem[kBytes];
     if constexpr (GR > 0) {
-        if ((int)blockIdx.y < G) {
-            G1::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+        if ((int)blockIdx.y < 4 * G) {
+            G1::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y >> 2, blockIdx.z, smem, blockIdx.y & 3);
             return;
         }
     }
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     op_t(*bs)[BSZ] = reinterpret_cast<op_t(*)[BSZ]>(smem + 2 * XSZ * sizeof(op_t));
     float *ws = reinterpret_cast<float *>(smem + 2 * (XSZ + BSZ) * sizeof(op_t));  // decay weights w_j of the chunk
 
-    const int c = blockIdx.x, h = blockIdx.y - (GR > 0 ? G : 0), b = blockIdx.z;
+    const int c = blockIdx.x, h = blockIdx.y - (GR > 0 ? 4 * G : 0), b = blockIdx.z;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -285,7 +286,7 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
                               float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                               bool big, hipStream_t s)
 {
-    const dim3 grid(d.nc, d.H + (GR > 0 ? d.G : 0), d.B);
+    const dim3 grid(d.nc, d.H + (GR > 0 ? 4 * d.G : 0), d.B);
     const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
               *cc = static_cast<const TIn *>(Cm);
 #define SSD_CS_LAUNCH(NN, JJ)                                                                                      \
@@ -318,7 +319,7 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, con
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const long nwg = (long)d.nc * (d.H + (GR > 0 ? d.G : 0)) * d.B;
+    const long nwg = (long)d.nc * (d.H + (GR > 0 ? 4 * d.G : 0)) * d.B;
     const bool big = nwg > 2L * (ncu > 0 ? ncu : 1);
     switch (d.P) {
     case 32: return launch_cs_n<TIn, 32, FUSE, GR>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, big, s);

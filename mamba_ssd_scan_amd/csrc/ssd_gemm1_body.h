@@ -39,9 +39,13 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
         }
     }
 
+    // part < 0: this workgroup forms every row tile of the chunk.  part = 0..3 (four
+    // wavefronts only): one of four workgroups sharing the chunk; wavefront w forms row
+    // tile tile_of(part, w) alone, so the four workgroups take the balanced tile sets
+    // {p, 7-p, 8+p, 15-p} and no wavefront walks more than one tile.
     static __device__ __forceinline__ void run(const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
                                                void *__restrict__ cb, int L, int G, int Q, int nc, int c, int g,
-                                               int b, unsigned char *smem)
+                                               int b, unsigned char *smem, int part = -1)
     {
         raw_t *bs = reinterpret_cast<raw_t *>(smem);
         const int tid = threadIdx.x, lane = tid & 63;
@@ -70,7 +74,8 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
                 for (int ks = 0; ks < KS; ++ks) cbf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
             }
         };
-        const int t0 = tile_of(wave, 0, nt);
+        auto tile = [&](int k) { return part < 0 ? tile_of(wave, k, nt) : (k == 0 ? tile_of(part, wave, nt) : -1); };
+        const int t0 = tile(0);
         if (t0 >= 0) load_c(t0);
 
         const int spc = (nt & 1) ? ((nt >> 1) + 1) * ((nt >> 1) + 1) : (nt >> 1) * ((nt >> 1) + 1);
@@ -108,7 +113,7 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
 
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            const int t = tile_of(wave, k, nt);
+            const int t = tile(k);
             if (t < 0) continue;
             if (k > 0 || pass > 0) load_c(t);
             const int ibase = 16 * t;
