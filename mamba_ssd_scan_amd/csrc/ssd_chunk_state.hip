@@ -56,6 +56,9 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     typedef typename Tr::op_t op_t;
     constexpr bool F32 = Tr::kF32;
     constexpr int JB = Traits<TIn>::kF32 ? 32 : JBT;   // tokens per staged block
+    // one-round grids (64-token blocks): every block of the chunk prefetched at once
+    constexpr bool ALLPF = !Traits<TIn>::kF32 && JBT == 64;
+    constexpr int NBMAX = 256 / JB;                    // blocks of the longest chunk
     // bf16 inputs: row-major fp16 tiles; a pitch of (width + 16) halves puts the 16
     // rows one transposing read touches on distinct bank groups.
     constexpr int LDXR = P + 16, LDBR = N + 16;
@@ -100,24 +103,27 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(Bm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vrows - 1) * G * N + N) * sizeof(TIn)));
 
-    auto prefetch = [&](Stage &st, int jbk) {
-        const int j0 = jbk * JB;
+    // (live == false: a block past the chunk; its loads read an empty range)
+    auto prefetch = [&](Stage &st, int jbk, bool live = true) {
+        const int j0 = live ? jbk * JB : 0;
+        const __amdgpu_buffer_rsrc_t bx = live ? rx : make_rsrc(x, 0u);
+        const __amdgpu_buffer_rsrc_t bb = live ? rb : make_rsrc(Bm, 0u);
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int u = tid + k * 256;
-            if (u < XU) {
+            if (XU % 256 == 0 || u < XU) {  // (true at compile time when every thread has a unit)
                 const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) st.x[k][e].load(rx, (uint32_t)((j + e) * H * P + 8 * pg));
+                for (int e = 0; e < 2; ++e) st.x[k][e].load(bx, (uint32_t)((j + e) * H * P + 8 * pg));
             }
         }
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
             const int u = tid + k * 256;
-            if (u < BU) {
+            if (BU % 256 == 0 || u < BU) {
                 const int jp = u / (N / 8), ng = u % (N / 8), j = j0 + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) st.b[k][e].load(rb, (uint32_t)((j + e) * G * N + 8 * ng));
+                for (int e = 0; e < 2; ++e) st.b[k][e].load(bb, (uint32_t)((j + e) * G * N + 8 * ng));
             }
         }
     };
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int u = tid + k * 256;
-            if (u < XU) {
+            if (XU % 256 == 0 || u < XU) {  // (true at compile time when every thread has a unit)
                 const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
                 const float w0 = j < Q ? ws[j] : 0.f, w1 = j + 1 < Q ? ws[j + 1] : 0.f;
                 if constexpr (F32) {
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
             const int u = tid + k * 256;
-            if (u < BU) {
+            if (BU % 256 == 0 || u < BU) {
                 const int jp = u / (N / 8), ng = u % (N / 8);
                 if constexpr (F32) {
                     float v0[8], v1[8];
@@ -195,67 +201,138 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
         }
     };
 
-    // ---- prologue: blocks 0 and 1 in flight while the decay weights are formed
-    Stage s0, s1;
-    prefetch(s0, 0);
-    if (nblk > 1) prefetch(s1, 1);
+    // ---- prologue.  The step sizes (or the tables) are requested first, so that waiting
+    // for them never waits for the block loads issued after them.
+    const int per = Q > 64 ? Q / 64 : 1;
+    unsigned short dtraw[4];  // FUSE_CUMSUM, wavefront 0: raw bf16 step sizes, Q/64 per lane
+    float dtf[4];             // (fp32 inputs)
+    float tac = 0.f, tdt = 0.f, tend = 0.f;  // !FUSE_CUMSUM: this thread's table entries
+    const float dbias = (FUSE_CUMSUM && opt.dt_bias) ? opt.dt_bias[h] : 0.f;  // read before the block loads
     if constexpr (FUSE_CUMSUM) {
         if (wave == 0) {
-            // inclusive scan of a_t = dt_t * A_h over the chunk: Q/64 tokens per lane
-            // serially, then a wavefront scan of the lane totals
-            const int per = Q > 64 ? Q / 64 : 1;
-            const float Ah = A[h];
-            float part[4], dts[4], run = 0.f;
+            const long vq = (L - tc) < Q ? (L - tc) : Q;
+            const __amdgpu_buffer_rsrc_t rd =
+                make_rsrc(dt + ((size_t)b * L + tc) * H + h, (uint32_t)(((vq - 1) * H + 1) * sizeof(TIn)));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int i = lane * per + k;
-                float d = 0.f;
-                if (k < per && i < Q && tc + i < L) d = dt_effective(load_in(dt + ((size_t)b * L + tc + i) * H + h), opt, h);
-                dts[k] = d;
-                run += d * Ah;
-                part[k] = run;
+                // (for k >= per this reads a neighbour's token, or zero past the range: unused,
+                // but a select here would become a branch, and a branch hides the load count)
+                const uint32_t off = (uint32_t)((lane * per + k) * H * sizeof(TIn));
+                if constexpr (F32)
+                    dtf[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)off, 0, 0));
+                else
+                    dtraw[k] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)off, 0, 0);
             }
-            float incl = run;
+        }
+    } else {
+        tend = acum[bhc * Q + Q - 1];
+        if (tid < Q) {
+            tac = acum[bhc * Q + tid];
+            tdt = dtc[bhc * Q + tid];
+        }
+    }
+    // An empty asm statement that reads and rewrites a value: it keeps in program order
+    // (after the block loads) the first instruction that consumes a loaded value, so the
+    // wait for that load is placed here and not right after the load itself.
+    auto pin = [](uint32_t v) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    auto pin16 = [](unsigned short v) {  // (before the widening, which is itself an instruction)
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    // Step-0 (fused) or the decay weights from the tables, into ws
+    auto form_weights = [&]() {
+        if constexpr (FUSE_CUMSUM) {
+            if (wave == 0) {
+                // inclusive scan of a_t = dt_t * A_h over the chunk: Q/64 tokens per lane
+                // serially, then a wavefront scan of the lane totals
+                const float Ah = A[h];
+                float part[4], dts[4], run = 0.f;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float v = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += v;
+                for (int k = 0; k < 4; ++k) {
+                    const int i = lane * per + k;
+                    float d = 0.f;
+                    const float raw = F32 ? __uint_as_float(pin(__float_as_uint(dtf[k])))
+                                          : __uint_as_float((uint32_t)pin16(dtraw[k]) << 16);
+                    if (k < per && i < Q && tc + i < L) d = dt_effective_b(raw, dbias, opt.dt_softplus);
+                    dts[k] = d;
+                    run += d * Ah;
+                    part[k] = run;
+                }
+                float incl = run;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float v = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += v;
+                }
+                float excl = __shfl_up(incl, 1, 64);
+                if (lane == 0) excl = 0.f;
+                const float aend = __shfl(incl, 63, 64);  // total over the chunk (padding adds 0)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int i = lane * per + k;
+                    if (k < per && i < Q) {
+                        const float ac = excl + part[k];
+                        acum[bhc * Q + i] = ac;
+                        dtc[bhc * Q + i] = dts[k];
+                        ws[i] = exp_fast(aend - ac) * dts[k];
+                    }
+                }
             }
-            float excl = __shfl_up(incl, 1, 64);
-            if (lane == 0) excl = 0.f;
-            const float aend = __shfl(incl, 63, 64);  // total over the chunk (padding adds 0)
+        } else {
+            if (tid < Q)
+                ws[tid] = exp_fast(__uint_as_float(pin(__float_as_uint(tend))) - __uint_as_float(pin(__float_as_uint(tac)))) *
+                          __uint_as_float(pin(__float_as_uint(tdt)));
+        }
+    };
+
+    if constexpr (ALLPF) {
+        // The whole chunk is requested at once (all blocks in registers), then contracted
+        // block by block with no further waits for memory: for grids that fit the GPU in
+        // one round, where each workgroup does exactly one chunk.
+        Stage sa[NBMAX];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = lane * per + k;
-                if (k < per && i < Q) {
-                    const float ac = excl + part[k];
-                    acum[bhc * Q + i] = ac;
-                    dtc[bhc * Q + i] = dts[k];
-                    ws[i] = exp_fast(aend - ac) * dts[k];
+        for (int k = 0; k < NBMAX; ++k) prefetch(sa[k], k, k < nblk);
+        form_weights();
+        __syncthreads();
+        commit(sa[0], 0, 0);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NBMAX; ++k) {
+            if (k < nblk) {
+                contract(k & 1, k);
+                if (k + 1 < NBMAX && k + 1 < nblk) {
+                    commit(sa[k + 1], (k + 1) & 1, k + 1);
+                    __syncthreads();
                 }
             }
         }
     } else {
-        const float aend = acum[bhc * Q + Q - 1];
-        for (int j = tid; j < Q; j += 256) ws[j] = exp_fast(aend - acum[bhc * Q + j]) * dtc[bhc * Q + j];
-    }
-    __syncthreads();
-    commit(s0, 0, 0);
-    __syncthreads();
+        // blocks 0 and 1 in flight while the decay weights are formed
+        Stage s0, s1;
+        prefetch(s0, 0);
+        if (nblk > 1) prefetch(s1, 1);
+        form_weights();
+        __syncthreads();
+        commit(s0, 0, 0);
+        __syncthreads();
 
-    // ---- main loop, unrolled by two so that each register stage has a fixed name:
-    // block k is in LDS buffer k&1; the stage that held block k is refilled with block k+2.
-    for (int jbk = 0; jbk < nblk; jbk += 2) {
-        if (jbk + 2 < nblk) prefetch(s0, jbk + 2);
-        contract(0, jbk);
-        if (jbk + 1 < nblk) {
-            commit(s1, 1, jbk + 1);
-            __syncthreads();
-            if (jbk + 3 < nblk) prefetch(s1, jbk + 3);
-            contract(1, jbk + 1);
-            if (jbk + 2 < nblk) {
-                commit(s0, 0, jbk + 2);
+        // main loop, unrolled by two so that each register stage has a fixed name:
+        // block k is in LDS buffer k&1; the stage that held block k is refilled with block k+2.
+        for (int jbk = 0; jbk < nblk; jbk += 2) {
+            if (jbk + 2 < nblk) prefetch(s0, jbk + 2);
+            contract(0, jbk);
+            if (jbk + 1 < nblk) {
+                commit(s1, 1, jbk + 1);
                 __syncthreads();
+                if (jbk + 3 < nblk) prefetch(s1, jbk + 3);
+                contract(1, jbk + 1);
+                if (jbk + 2 < nblk) {
+                    commit(s0, 0, jbk + 2);
+                    __syncthreads();
+                }
             }
         }
     }
