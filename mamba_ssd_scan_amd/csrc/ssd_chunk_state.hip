@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     constexpr int LDT = JB + 4;                         // fp32 inputs: transposed tiles
     constexpr int XSZ = F32 ? P * LDT : JB * LDXR;
     constexpr int BSZ = F32 ? N * LDT : JB * LDBR;
-    constexpr int TN = N / 16, NT = (P / 16) * TN;
+    constexpr int TP = P / 16, TN = N / 16, NT = TP * TN;
     constexpr int TPW = (NT + 3) / 4;                   // output tiles per wavefront
     constexpr int XU = (JB / 2) * (P / 8), XPT = (XU + 255) / 256;  // two tokens x 8 channels
     constexpr int BU = (JB / 2) * (N / 8), BPT = (BU + 255) / 256;
@@ -172,6 +172,39 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
 
     auto contract = [&](int buf, int jbk) {
         for (int ks = 0; ks < JB && jbk * JB + ks < Q; ks += 32) {
+            if constexpr (!F32) {
+                // The wavefront's tiles t = wave + 4 tt share operands: with TN >= 4 they are
+                // the state-column tiles wave + 4 j (j < TN / 4) crossed with every channel
+                // tile; with TN = 2, one state-column tile crossed with TPW channel tiles.
+                // Each distinct operand is read from LDS once per 32-token step.
+                // Reduction slots of lane group lg: tokens ks + 4 lg + r and ks + 16 + 4 lg + r.
+                constexpr int NB = TN >= 4 ? TN / 4 : 1, NX = TN >= 4 ? TP : TPW;
+                f16x8 bo[NB], xo[NX];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int nt = TN >= 4 ? wave + 4 * j : wave % TN;
+                    const int ob = tr16_offset(lane, ks, nt * 16, LDBR);
+                    const f16x4 b0 = lds_read_tr16(&bs[buf][ob]);
+                    const f16x4 b1 = lds_read_tr16(&bs[buf][ob + 16 * LDBR]);
+                    bo[j] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                }
+#pragma unroll
+                for (int q = 0; q < NX; ++q) {
+                    const int pt = TN >= 4 ? q : wave / TN + (4 / TN) * q;
+                    const int ox = tr16_offset(lane, ks, pt * 16, LDXR);
+                    const f16x4 a0 = lds_read_tr16(&xs[buf][ox]);
+                    const f16x4 a1 = lds_read_tr16(&xs[buf][ox + 16 * LDXR]);
+                    xo[q] = f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                }
+                // S^T tiles: the B rows are the A operand, so a lane's accumulator holds
+                // four consecutive state columns n of one row p (contiguous stores)
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    const int j = TN >= 4 ? tt % NB : 0, q = TN >= 4 ? tt / NB : tt;
+                    acc[tt] = mfma16x16x32_f16(bo[j], xo[q], acc[tt]);
+                }
+                continue;
+            }
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt) {
                 const int t = wave + 4 * tt;
