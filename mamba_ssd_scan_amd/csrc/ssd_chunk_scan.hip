@@ -604,6 +604,7 @@ hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, cons
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (ncu <= 0) ncu = 1;
+    if (chunk_scan_small_fits(d, ncu)) return launch_chunk_scan_small(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, s);
     return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
                   : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
 }

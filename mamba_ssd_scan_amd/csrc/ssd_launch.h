@@ -37,6 +37,12 @@ hipError_t launch_chunk_gemm1(const void *Bm, const void *Cm, void *cb, const Di
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
                              const float *dtc, const void *h_enter, const float *D, void *y,
                              const SsdOpts &o, const Dims &d, hipStream_t s);
+// The chunk scan for problems whose items all fit at once (one item per workgroup, two
+// workgroups per compute unit): bf16 inputs, Q = 256, P = 64, items <= 2 * ncu.
+bool chunk_scan_small_fits(const Dims &d, int ncu);
+hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
+                                   const float *dtc, const void *h_enter, const float *D, void *y,
+                                   const SsdOpts &o, const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
