@@ -39,7 +39,19 @@ KERNEL_SOURCES = {
     "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_state_kernel": "ssd_chunk_state.hip",
     "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
     "step_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
+    "chunk_scan_small_kernel": "ssd_chunk_scan_small.hip",
 }
+
+
+def scan_kernel_name(s) -> str:
+    """The chunk-scan kernel the library launches for this shape: the one-round kernel when
+    every (b, h, chunk) item fits at two per compute unit (bf16, 256-token chunks, P = 64),
+    else the persistent one (the same rule as the library's launcher)."""
+    import torch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    nitems = s.batch * s.nheads * -(-s.seqlen // s.chunk)
+    small = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and nitems <= 2 * ncu
+    return "chunk_scan_small_kernel" if small else "chunk_scan_kernel"
 
 
 # ---------------------------------------------------------------------------- algorithmic work
@@ -76,6 +88,7 @@ def alg_counts(s: synth.PrefillShape) -> dict:
         "chunk_scan_kernel": dict(bytes=x + bc + cb + chunk_tab + hen + y,
                                   flops=B * nc * H * P * tri + 2 * B * H * L * P * N),
     }
+    k["chunk_scan_small_kernel"] = k["chunk_scan_kernel"]
     fused_bytes = x + dt + 2 * bc + y + st + h0
     fused_flops = B * nc * (G * N * tri + H * P * tri) + 4 * B * H * L * P * N
     return dict(kernels=k, fused_bytes=fused_bytes, fused_flops=fused_flops)
@@ -238,7 +251,7 @@ def stage_fns(torch, g, s):
     torch.cuda.synchronize()
     return {"chunk_cumsum_kernel": (cumsum, None), "chunk_state_kernel": (cstate, None),
             "state_passing_kernel": (passing, restore_states), "chunk_gemm1_kernel": (gemm1, None),
-            "chunk_scan_kernel": (scan, None)}
+            scan_kernel_name(s): (scan, None)}
 
 
 # ---------------------------------------------------------------------------- CPU baseline
@@ -384,7 +397,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
-                                       "chunk_cumsum_kernel", "chunk_gemm1_kernel", "step", "cached", "copy"],
+                                       "chunk_cumsum_kernel", "chunk_gemm1_kernel", "chunk_scan_small_kernel",
+                                       "step", "cached", "copy"],
                     help="profiling aid: launch only this work --steps times (cold), print nothing else")
     args = ap.parse_args()
 
