@@ -43,20 +43,35 @@ KERNEL_SOURCES = {
 }
 
 
-def scan_kernel_name(s) -> str:
+def scan_kernel_name(s, ncu=None) -> str:
     """The chunk-scan kernel the library launches for this shape: the one-round kernel when
     every (b, h, chunk) item fits at two per compute unit (bf16, 256-token chunks, P = 64),
-    else the persistent one (the same rule as the library's launcher)."""
-    import torch
-    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    else the persistent one (the same rule as the library's launcher).  ncu: compute units
+    (default: the current device's)."""
+    if ncu is None:
+        import torch
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
     nitems = s.batch * s.nheads * -(-s.seqlen // s.chunk)
     small = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and nitems <= 2 * ncu
     return "chunk_scan_small_kernel" if small else "chunk_scan_kernel"
 
 
+def passing_in_scan(s, ncu=None) -> bool:
+    """Whether ssd_prefill runs Step-3 inside the one-round chunk scan (two launches): the
+    one-round kernel's shapes with at most 16 chunks (the same rule as the library)."""
+    return scan_kernel_name(s, ncu) == "chunk_scan_small_kernel" and -(-s.seqlen // s.chunk) <= 16
+
+
+def step_kernels(s) -> list:
+    """The kernels one ssd_prefill launches, in order."""
+    if passing_in_scan(s):
+        return ["chunk_state_kernel", "chunk_scan_small_kernel"]
+    return ["chunk_state_kernel", "state_passing_kernel", scan_kernel_name(s)]
+
+
 # ---------------------------------------------------------------------------- algorithmic work
 
-def alg_counts(s: synth.PrefillShape) -> dict:
+def alg_counts(s: synth.PrefillShape, ncu=None) -> dict:
     """Algorithmic bytes and flops per launch of each prefill kernel.
 
     Bytes: every tensor a kernel must read or write, once.  Flops: the
@@ -89,6 +104,11 @@ def alg_counts(s: synth.PrefillShape) -> dict:
                                   flops=B * nc * H * P * tri + 2 * B * H * L * P * N),
     }
     k["chunk_scan_small_kernel"] = k["chunk_scan_kernel"]
+    if passing_in_scan(s, ncu):
+        # Step-3 inside the chunk scan: the chunk states, the initial and the final state
+        # instead of the entering states (which it writes and reads back itself)
+        k["chunk_scan_small_kernel"] = dict(bytes=x + bc + cb + chunk_tab + states + h0 + st + y,
+                                            flops=k["chunk_scan_kernel"]["flops"] + 2 * B * H * nc * P * N)
     fused_bytes = x + dt + 2 * bc + y + st + h0
     fused_flops = B * nc * (G * N * tri + H * P * tri) + 4 * B * H * L * P * N
     return dict(kernels=k, fused_bytes=fused_bytes, fused_flops=fused_flops)
@@ -242,6 +262,14 @@ def stage_fns(torch, g, s):
     def scan():
         ssd.chunk_scan(g["x"], g["C"], g["cb"], g["acum"], g["dtc"], g["hen"], g["D"], chunk=Q, y=g["y"])
 
+    def scan_passing():
+        ssd.chunk_scan_passing(g["x"], g["C"], g["cb"], g["acum"], g["dtc"], g["states"], g["sync"], g["D"],
+                               g["h0"], chunk=Q, y=g["y"], final_state=g["final"])
+
+    def restore_states_and_counters():  # Step-3 in the scan works in place on zeroed counters
+        g["states"].copy_(pristine["states"])
+        g["sync"].zero_()
+
     cumsum()
     cstate()
     torch.cuda.synchronize()
@@ -249,9 +277,13 @@ def stage_fns(torch, g, s):
     passing()
     gemm1()
     torch.cuda.synchronize()
-    return {"chunk_cumsum_kernel": (cumsum, None), "chunk_state_kernel": (cstate, None),
-            "state_passing_kernel": (passing, restore_states), "chunk_gemm1_kernel": (gemm1, None),
-            scan_kernel_name(s): (scan, None)}
+    out = {"chunk_cumsum_kernel": (cumsum, None), "chunk_state_kernel": (cstate, None),
+           "state_passing_kernel": (passing, restore_states), "chunk_gemm1_kernel": (gemm1, None),
+           scan_kernel_name(s): (scan, None)}
+    if passing_in_scan(s):
+        g["sync"] = ssd.alloc_sync(s.batch, s.nheads)
+        out["chunk_scan_small_kernel"] = (scan_passing, restore_states_and_counters)
+    return out
 
 
 # ---------------------------------------------------------------------------- CPU baseline
@@ -479,7 +511,7 @@ def main():
         kb, kf = counts["kernels"][name]["bytes"], counts["kernels"][name]["flops"]
         kernels[name] = {"us": us, "us_min": us_min, "alg_bytes": kb, "alg_flops": kf,
                          "gbps": kb / (us * 1e-6) / 1e9, "tflops": kf / (us * 1e-6) / 1e12}
-    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    dom = max(step_kernels(s), key=lambda k: kernels[k]["us"])  # the step's longest launch
     d = kernels[dom]
     intensity = d["alg_flops"] / d["alg_bytes"]
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -490,7 +522,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": d["tflops"] / MFMA_BF16_PEAK_TFLOPS}
-    roof.update({"traffic": counter_traffic(dom, wname), "kernel": dom, "us_per_launch": d["us"],
+    roof.update({"traffic": counter_traffic(dom, wname), "kernel": dom,
+                 "variant": ("with Step-3 (ssd_chunk_scan_passing)" if dom == "chunk_scan_small_kernel"
+                             and passing_in_scan(s) else "as launched by the stage entry point"),
+                 "us_per_launch": d["us"],
                  "alg_bytes_per_launch": d["alg_bytes"], "alg_flops_per_launch": d["alg_flops"],
                  "intensity_flop_per_byte": intensity})
 
@@ -516,6 +551,7 @@ def main():
         "roofline": roof,
         "prefill": prefill,
         "kernels": kernels,
+        "step_launches": step_kernels(s),
         "timed_wall_s": wall,
     }
     if not args.no_decode:

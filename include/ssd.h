@@ -75,6 +75,7 @@ int ssd_version(void);
  *   states  [B, H, nc, P, N] x 4 bytes: the chunk states, then the entering
  *           states (fp16 for bf16 inputs -- half the region -- fp32 for fp32 inputs)
  *   cb      ssd_chunk_gemm1_size(B, L, G, Q) bytes: the C.B^T products
+ *   sync    [B, H] uint32 counters, one per 256 bytes, of the two-launch path below
  * with nc = ceil(seqlen / Q).
  */
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim,
@@ -84,6 +85,15 @@ size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim
  * Chunked prefill over a whole sequence (Step-1 intra-chunk output, chunk
  * states, Step-3 inter-chunk state passing, off-diagonal output; see the
  * stage entry points below, which it runs in order on `hip_stream`).
+ * When every (b, h, chunk) item fits the device at once (bf16 inputs, Q = 256,
+ * P = 64, nc <= 16, B*H*nc <= 2 x compute units) it runs two launches instead: the chunk
+ * scan walks Step-3 itself, each workgroup for its share of its head's state,
+ * and waits for the head's other workgroups.  That wait relies on all of them
+ * being resident together: a kernel on another stream that holds compute units
+ * indefinitely while this one starts could delay it (the wait is bounded; past
+ * the bound the result is not valid).  Results equal the staged path's bit for bit;
+ * SSD_PREFILL_STAGED=1 in the environment (read on every call) forces the staged
+ * path, for comparisons.
  *
  *   x   [B, L, H, P] in_dtype       dt [B, L, H] in_dtype (used as given:
  *   A   [H] fp32                          positive step sizes, no softplus)
@@ -250,6 +260,28 @@ int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *
                    const float *dt_c, const void *h_enter, const float *D, float *y,
                    ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
                    int dstate, int ngroups, int chunk, void *hip_stream);
+
+/*
+ * Step-3 and the chunk scan in one launch, for problems whose (b, h, chunk)
+ * items all fit the device at once (the two-launch ssd_prefill path):
+ * bf16 inputs, Q = 256, P = 64, nc <= 16 and B*H*nc <= 2 x compute units;
+ * any other shape returns SSD_ERR_UNSUPPORTED.  The result equals
+ * ssd_state_passing followed by ssd_chunk_scan bit for bit.
+ *   states [B, H, nc, P, N] fp16: the chunk states (ssd_chunk_state output) on
+ *          entry, the entering states on exit
+ *   initial_state / final_state: as in ssd_state_passing (NULL allowed)
+ *   sync   B*H*64 uint32 (256 bytes per (b, h)), ZERO on entry; each (b, h)
+ *          counter holds nc on exit.  The launch's workgroups of one (b, h) wait
+ *          for each other through it, which needs them resident together: a
+ *          kernel on another stream that holds compute units indefinitely could
+ *          delay the wait (it is bounded; past the bound y is not valid).
+ *   Other arguments as ssd_chunk_scan; y [B, L, H, P] fp32 (written).
+ */
+int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const float *dA_cum,
+                           const float *dt_c, void *states, const float *initial_state,
+                           float *final_state, const float *D, float *y, unsigned *sync,
+                           ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
+                           int dstate, int ngroups, int chunk, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -7,12 +7,21 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <new>
 
 #include "ssd_launch.h"
 
 namespace {
+
+// SSD_PREFILL_STAGED=1 in the environment: always the three-launch path (for comparisons)
+bool staged_forced()
+{
+    const char *e = getenv("SSD_PREFILL_STAGED");
+    return e && e[0] == '1';
+}
+
 
 constexpr size_t kWsAlign = 256;
 
@@ -47,7 +56,7 @@ int check_dtype(ssd_dtype_t t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK
 size_t in_size(ssd_dtype_t t) { return t == SSD_BF16 ? 2 : 4; }
 
 struct WsLayout {
-    size_t acum, dtc, states, cb, total;  // byte offsets of each region, then total bytes
+    size_t acum, dtc, states, cb, sync, total;  // byte offsets of each region, then total bytes
 };
 
 // fp32 elements of the GEMM1 output: 512 per 32-column step of every chunk of every group
@@ -65,7 +74,8 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, i
     w.dtc = align_up(w.acum + 4 * bhq, kWsAlign);
     w.states = align_up(w.dtc + 4 * bhq, kWsAlign);
     w.cb = align_up(w.states + 4 * (size_t)batch * nheads * nc * headdim * dstate, kWsAlign);
-    w.total = align_up(w.cb + 4 * gemm1_elems(batch, ngroups, (int)nc, chunk), kWsAlign);
+    w.sync = align_up(w.cb + 4 * gemm1_elems(batch, ngroups, (int)nc, chunk), kWsAlign);
+    w.total = align_up(w.sync + 4 * (size_t)batch * nheads * ssd::kSyncStride, kWsAlign);  // a counter per (b, h)
     return w;
 }
 
@@ -127,7 +137,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (3 << 16) | 0; }
+int ssd_version(void) { return (3 << 16) | 1; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -218,6 +228,30 @@ int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *
         ssd::launch_chunk_scan(x, Cm, cb, dA_cum, dt_c, h_enter, D, y, o, d, (hipStream_t)hip_stream));
 }
 
+int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const float *dA_cum, const float *dt_c,
+                           void *states, const float *initial_state, float *final_state, const float *D, float *y,
+                           unsigned *sync, ssd_dtype_t in_dtype, int batch, int seqlen, int nheads, int headdim,
+                           int dstate, int ngroups, int chunk, void *hip_stream)
+{
+    SSD_TRY(check_dtype(in_dtype));
+    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
+    if (seqlen == 0) return SSD_OK;
+    SSD_TRY(check_seq_inputs(x, dt_c, Cm, SSD_F32));
+    if (!cb || !dA_cum || !states || !y || !sync) return SSD_ERR_INVALID_ARG;
+    if (!aligned(cb, 16) || !aligned(dA_cum, 16) || !aligned(states, 16) || !aligned(y, 16) || !aligned(D, 4) ||
+        !aligned(sync, 16) || !aligned(initial_state, 16) || !aligned(final_state, 16))
+        return SSD_ERR_INVALID_ARG;
+    const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
+    if (!ssd::chunk_scan_small_pass_shape(d)) return SSD_ERR_UNSUPPORTED;
+    int ncu = 0;
+    SSD_TRY(hip_status(ssd::device_cu_count(&ncu)));
+    if (!ssd::chunk_scan_small_pass_fits(d, ncu)) return SSD_ERR_UNSUPPORTED;
+    ssd::SsdOpts o = {nullptr, 0, nullptr, 0};
+    o.sync = sync;
+    return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, dA_cum, dt_c, states, initial_state, final_state, D, y,
+                                                   o, d, (hipStream_t)hip_stream));
+}
+
 int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
                    const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
                    float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
@@ -249,7 +283,16 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
     float *cb = reinterpret_cast<float *>(ws + w.cb);
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
 
-    const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    int ncu = 0;
+    SSD_TRY(hip_status(ssd::device_cu_count(&ncu)));
+    if (ssd::chunk_scan_small_pass_fits(d, ncu) && !staged_forced()) {
+        // every (b, h, chunk) item is resident at once: Step-3 runs inside the chunk scan
+        o.sync = reinterpret_cast<unsigned *>(ws + w.sync);
+        SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
+        return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, acum, dtc, states, initial_state, final_state, D, y,
+                                                       o, d, s));
+    }
     SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, o, d, s));

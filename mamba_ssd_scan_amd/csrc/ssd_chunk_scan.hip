@@ -595,16 +595,29 @@ static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, 
     }
 }
 
+hipError_t device_cu_count(int *ncu)
+{
+    int dev = 0;
+    *ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (*ncu <= 0) *ncu = 1;
+    return e;
+}
+
 hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, const float *acum,
                              const float *dtc, const void *h_enter, const float *D, void *y,
                              const SsdOpts &o, const Dims &d, hipStream_t s)
 {
-    int dev = 0, ncu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int ncu = 0;
+    const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
-    if (ncu <= 0) ncu = 1;
-    if (chunk_scan_small_fits(d, ncu)) return launch_chunk_scan_small(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, s);
+    if (chunk_scan_small_fits(d, ncu)) {
+        SsdOpts po = o;
+        po.sync = nullptr;  // entering states given
+        return launch_chunk_scan_small(x, Cm, cb, acum, dtc, const_cast<void *>(h_enter), nullptr, nullptr, D, y, po,
+                                       d, s);
+    }
     return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
                   : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
 }

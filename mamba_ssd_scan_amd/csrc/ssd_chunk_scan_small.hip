@@ -14,16 +14,37 @@
 // Chunks of 256 tokens, bf16 inputs (fp16 matrix-core operands, fp32 accumulation),
 // fp16 entering states.  Wavefront w forms tiles w and 15 - w: the two wavefronts of a
 // SIMD (w and w + 4) then hold tiles {s, 15-s, s+4, 11-s}, 18 32-column steps per SIMD.
+//
+// With every item resident at once, the launch can also run Step-3 (same paper, Sec. IV-C:
+// the entering state of chunk c+1 is that of chunk c decayed by the chunk's total decay
+// plus the chunk's own state): the workgroups of one (b, h) split the P*N state elements
+// between them, each walks the chunk recurrence for its share over all chunks, and each
+// reads back its own chunk's entering state once all of them have counted themselves done.
+// That replaces the separate state-passing launch (its read and write of every state, and
+// a launch) with one extra read of the chunk's state per workgroup, taken after the first
+// tile's steps, by which time the head's other workgroups are done.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-template <int P, int N, bool OPT>
+// Cache-policy bit of buffer loads and stores: coherent across the whole device (the
+// per-XCD L2 caches are not coherent with each other; such accesses go through to memory).
+constexpr int kDeviceCoherent = 16;
+constexpr unsigned kSpinLimit = 1u << 22;  // bound of the wait for a head's other chunks
+
+// PNC = 0: hen holds the entering states [B, H, nc, P, N] (fp16).
+// PNC > 0 (nc <= PNC): hen holds the chunk states; Step-3 runs inside this launch.  The
+// workgroup of chunk c walks the chunk recurrence for its 1/nc share of the P*N state elements
+// of its (b, h), writing every chunk's entering state over its chunk state (and the final
+// state to fin), then counts itself done in sync[b, h] (zeroed by the chunk-state launch) and
+// waits until all nc workgroups of the head are; all items are resident at once, so the wait
+// ends.
+template <int P, int N, bool OPT, int PNC>
 __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves per SIMD: <= 128 VGPRs
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
-    const float *__restrict__ acum, const float *__restrict__ dtc, const f16 *__restrict__ hen,
-    const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int nc)
+    const float *__restrict__ acum, const float *__restrict__ dtc, f16 *hen, const float *init, float *fin,
+    unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int nc)
 {
     constexpr int Q = 256, ROWS = 256, NT = 512, NSMAX = 8;
     constexpr int TP = P / 16, KS = N / 32;
@@ -43,6 +64,61 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
     const float Dh = D ? D[h] : 0.f;
 
+    // ---- Step-3 operands first (PNC > 0): word q = w0 + tid (two state elements) of each
+    // chunk's state, the chunks' total decays and the initial state.  Every load is issued
+    // unconditionally (slots past nc or past the share read past a buffer range: zeros), so
+    // that the waits for them and for the loads issued after them stay exact.
+    constexpr bool PASS = PNC > 0;
+    constexpr int PN2 = P * N / 2;  // 32-bit words (two fp16 elements) of one state
+    constexpr int PS = PASS ? PNC : 1;
+    const size_t bh = (size_t)b * H + h;
+    const int share = (PN2 + nc - 1) / nc, w0 = c * share, nw = min(share, PN2 - w0);
+    __amdgpu_buffer_rsrc_t rp = make_rsrc(hen, 0u), ri = rp, rf = rp;
+    uint32_t pv[PS], pi0 = 0u, pi1 = 0u;
+    float pdec[PS];
+    auto pass_load = [&](int q) {  // chunk states and initial state of word w0 + q
+        const bool act = q < nw;
+#pragma unroll
+        for (int k = 0; k < PS; ++k) {
+            const uint32_t off = (k < nc && act) ? 4u * (uint32_t)(k * PN2 + w0 + q) : 0x80000000u;
+            pv[k] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)off, 0, 0);
+        }
+        const uint32_t oi = act ? 8u * (uint32_t)(w0 + q) : 0x80000000u;
+        pi0 = __builtin_amdgcn_raw_buffer_load_b32(ri, (int)oi, 0, 0);
+        pi1 = __builtin_amdgcn_raw_buffer_load_b32(ri, (int)(oi + 4u), 0, 0);
+    };
+    // The recurrence over the chunk slots (a slot past nc is the identity step), storing each
+    // chunk's entering state (device-coherent) and the final state; q past the share stores
+    // nothing (past the ranges).
+    auto pass_run = [&](int q) {
+        const bool act = q < nw;
+        float r0 = __uint_as_float(pi0), r1 = __uint_as_float(pi1);
+#pragma unroll
+        for (int k = 0; k < PS; ++k) {
+            const uint32_t off = (k < nc && act) ? 4u * (uint32_t)(k * PN2 + w0 + q) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(pack_f16x2(r0, r1), rp, (int)off, 0, kDeviceCoherent);
+            const float r = k < nc ? exp_fast(pdec[k]) : 1.f;
+            const f16x2 sv = __builtin_bit_cast(f16x2, pv[k]);
+            r0 = fmaf(r, r0, static_cast<float>(sv[0]));
+            r1 = fmaf(r, r1, static_cast<float>(sv[1]));
+            // fp32 carry, converted by the next store (the standalone Step-3 kernel's
+            // rounding): no multiply-add that rounds straight to fp16
+            asm volatile("" : "+v"(r0), "+v"(r1));
+        }
+        const uint32_t of = act ? 8u * (uint32_t)(w0 + q) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r0), rf, (int)of, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r1), rf, (int)(of + 4u), 0, 0);
+    };
+    if constexpr (PASS) {
+        rp = make_rsrc(hen + bh * nc * P * N, (uint32_t)(nc * PN2 * 4));
+        ri = make_rsrc(init ? init + bh * P * N : nullptr, init ? (uint32_t)(PN2 * 8) : 0u);
+        rf = make_rsrc(fin ? fin + bh * P * N : nullptr, fin ? (uint32_t)(PN2 * 8) : 0u);
+        const float *ac = acum + bh * nc * Q + (Q - 1);
+#pragma unroll
+        for (int k = 0; k < PS; ++k) pdec[k] = ac[(size_t)min(k, nc - 1) * Q];
+        pass_load(tid);
+    }
+
     // ---- the item's X rows (fp16), entering state and decay tables into LDS
     {
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P,
@@ -57,10 +133,12 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             px[k].load(rx, (uint32_t)((u / (P / 8)) * H * P + 8 * (u % (P / 8))));
         }
         const f16 *hp = hen + bhc * P * N;
+        if constexpr (!PASS) {
 #pragma unroll
-        for (int k = 0; k < HPT; ++k) {
-            const int u = tid + k * NT;
-            if (HU % NT == 0 || u < HU) ph[k] = *reinterpret_cast<const uint4 *>(hp + 8 * u);
+            for (int k = 0; k < HPT; ++k) {
+                const int u = tid + k * NT;
+                if (HU % NT == 0 || u < HU) ph[k] = *reinterpret_cast<const uint4 *>(hp + 8 * u);
+            }
         }
         // tables: dA_cum in log2 units, dt, and exp(a_r - a_j) dt_j with a_r the last column
         // of the 32-column step holding j
@@ -76,10 +154,21 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             const int u = tid + k * NT;
             *reinterpret_cast<uint4 *>(&xs[(u / (P / 8)) * LDX + 8 * (u % (P / 8))]) = raw8_to_f16x8(px[k]);
         }
+        if constexpr (PASS) {
+            // Step-3 for this workgroup's share: the first word per thread (loaded above),
+            // then, when the share is longer than the workgroup, the rest in turn
+            pass_run(tid);
+            for (int q = tid + NT; q < share; q += NT) {
+                pass_load(q);
+                pass_run(q);
+            }
+        } else {
 #pragma unroll
-        for (int k = 0; k < HPT; ++k) {
-            const int u = tid + k * NT;
-            if (HU % NT == 0 || u < HU) *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = ph[k];
+            for (int k = 0; k < HPT; ++k) {
+                const int u = tid + k * NT;
+                if (HU % NT == 0 || u < HU)
+                    *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = ph[k];
+            }
         }
         if (tid < TAB) {
             float a = 0.f, d = 0.f, e = 0.f;
@@ -93,7 +182,22 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             ecs[tid] = e;
         }
     }
-    __syncthreads();
+    constexpr int HU = P * N / 8, HPT = (HU + NT - 1) / NT;  // uint4 words of the entering state
+    uint4 hv[HPT];
+    if constexpr (PASS) {
+        // The entering-state stores are device-coherent (they write through the XCD's L2);
+        // once every wavefront's stores have completed the workgroup counts itself done, and
+        // the entering state is read back with device-coherent loads issued only after the
+        // count reached nc.  (No L2 write-back or invalidation is needed: nothing else this
+        // kernel exchanges between workgroups.)
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's stores are done
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(sync + ((size_t)b * H + h) * kSyncStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        __syncthreads();
+    }
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)b * L + tc) * G * N + (size_t)g * N,
                                                 (uint32_t)(((vrows - 1) * G * N + N) * 2));
@@ -184,6 +288,31 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             }
             gemm2(jb, r0, r1);
         }
+        if (PASS && k == 0) {
+            // The entering state, once, before the first off-diagonal (the first tile's steps
+            // gave the head's other workgroups time to count in): wait for all nc counts, read
+            // it through to memory (written by other workgroups; words past the state read past
+            // the range: zeros, not stored), and put it into LDS (rows p, padded).
+            if (tid == 0) {
+                const unsigned *cnt = sync + ((size_t)b * H + h) * kSyncStride;
+                for (unsigned it = 0; it < kSpinLimit; ++it) {
+                    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)nc) break;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+            }
+            __syncthreads();
+            const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + bhc * P * N, (uint32_t)(P * N * 2));
+#pragma unroll
+            for (int kk = 0; kk < HPT; ++kk)
+                hv[kk] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)(16u * (tid + kk * NT)), 0, kDeviceCoherent));
+#pragma unroll
+            for (int kk = 0; kk < HPT; ++kk) {
+                const int u = tid + kk * NT;  // uint4 index: elements 8u .. 8u + 7
+                if (HU % NT == 0 || u < HU) *reinterpret_cast<uint4 *>(&hs[(u / (N / 8)) * LDH + 8 * (u % (N / 8))]) = hv[kk];
+            }
+            __syncthreads();
+        }
         // ---- Step-4: exp(a_i) * (C_i . H_enter[p, :]), then the skip term (the C rows are
         // loaded only now, so that they do not hold registers through the steps)
         {
@@ -254,26 +383,38 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 
 // Whether the one-round kernel takes this problem: bf16 inputs, chunks of 256 tokens,
 // supported P, and no more items than two per compute unit.
+bool chunk_scan_small_shape(const Dims &d) { return d.bf16 && d.Q == 256 && d.P == 64; }
 bool chunk_scan_small_fits(const Dims &d, int ncu)
 {
-    return d.bf16 && d.Q == 256 && d.P == 64 && (long)d.nc * d.H * d.B <= 2L * ncu;
+    return chunk_scan_small_shape(d) && (long)d.nc * d.H * d.B <= 2L * ncu;
 }
 
+// Whether the one-round kernel can also run Step-3 itself: at most 16 chunks per sequence
+// (a thread keeps one state word of every chunk in registers).
+bool chunk_scan_small_pass_shape(const Dims &d) { return chunk_scan_small_shape(d) && d.nc <= 16; }
+bool chunk_scan_small_pass_fits(const Dims &d, int ncu) { return chunk_scan_small_pass_shape(d) && chunk_scan_small_fits(d, ncu); }
+
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
-                                   const float *dtc, const void *h_enter, const float *D, void *y,
-                                   const SsdOpts &o, const Dims &d, hipStream_t s)
+                                   const float *dtc, void *h, const float *init, float *fin, const float *D,
+                                   void *y, const SsdOpts &o, const Dims &d, hipStream_t s)
 {
+    if (o.sync && d.nc > 16) return hipErrorInvalidValue;
     const unsigned nitems = (unsigned)(d.nc * d.H * d.B);
     const bf16_t *xx = static_cast<const bf16_t *>(x), *cc = static_cast<const bf16_t *>(Cm);
-    const f16 *hh = static_cast<const f16 *>(h_enter);
-#define SSD_SMALL_LAUNCH(NN)                                                                                   \
-    do {                                                                                                       \
-        if (o.z || o.y_bf16)                                                                                   \
-            chunk_scan_small_kernel<64, NN, true><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, D, y, o, d.L, \
-                                                                         d.H, d.G, d.nc);                      \
-        else                                                                                                   \
-            chunk_scan_small_kernel<64, NN, false><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, D, y, o,     \
-                                                                          d.L, d.H, d.G, d.nc);                \
+    f16 *hh = static_cast<f16 *>(h);
+#define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                        \
+    chunk_scan_small_kernel<64, NN, OO, PP><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, init, fin, o.sync, \
+                                                                    D, y, o, d.L, d.H, d.G, d.nc)
+#define SSD_SMALL_LAUNCH2(NN, PP)                                                                            \
+    do {                                                                                                     \
+        if (o.z || o.y_bf16) SSD_SMALL_LAUNCH3(NN, true, PP);                                                \
+        else SSD_SMALL_LAUNCH3(NN, false, PP);                                                               \
+    } while (0)
+#define SSD_SMALL_LAUNCH(NN)                                                                                 \
+    do {                                                                                                     \
+        if (!o.sync) SSD_SMALL_LAUNCH2(NN, 0);                                                               \
+        else if (d.nc <= 8) SSD_SMALL_LAUNCH2(NN, 8);                                                        \
+        else SSD_SMALL_LAUNCH2(NN, 16);                                                                      \
     } while (0)
     switch (d.N) {
     case 32: SSD_SMALL_LAUNCH(32); break;
@@ -282,6 +423,8 @@ hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb
     default: return hipErrorInvalidValue;
     }
 #undef SSD_SMALL_LAUNCH
+#undef SSD_SMALL_LAUNCH2
+#undef SSD_SMALL_LAUNCH3
     return hipGetLastError();
 }
 

@@ -91,6 +91,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     const size_t bhc = ((size_t)b * H + h) * nc + c;
     const long tc = (long)c * Q;
     const int nblk = (Q + JB - 1) / JB;
+    // the head's completion counter of a chunk scan that runs Step-3 itself starts at zero
+    if (FUSE_CUMSUM && opt.sync && c == 0 && tid == 0) opt.sync[((size_t)b * H + h) * kSyncStride] = 0u;
 
     struct Stage {
         Raw8<TIn> x[XPT][2], b[BPT][2];

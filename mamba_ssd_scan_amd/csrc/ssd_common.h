@@ -81,7 +81,10 @@ struct SsdOpts {
     int dt_softplus;
     const void *z;
     int y_bf16;
+    unsigned *sync;  // per-(b, h) counters of a launch that runs Step-3 inside the chunk scan
 };
+// One counter per 256 bytes, so that the heads' counters sit in different lines.
+constexpr int kSyncStride = 64;
 
 // dt as the recurrence uses it, for a token inside the sequence (fp32), with the head's
 // bias already read

@@ -39,10 +39,17 @@ hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, cons
                              const SsdOpts &o, const Dims &d, hipStream_t s);
 // The chunk scan for problems whose items all fit at once (one item per workgroup, two
 // workgroups per compute unit): bf16 inputs, Q = 256, P = 64, items <= 2 * ncu.
+// o.sync == nullptr: h holds the entering states (fp16).  o.sync != nullptr: h holds the
+// chunk states (fp16) and Step-3 runs inside the launch (entering states written over h,
+// final state to fin, initial state from init); o.sync holds B*H counters that the
+// chunk-state launch zeroed (launch_cumsum_chunk_state_gemm1 with the same o.sync).
 bool chunk_scan_small_fits(const Dims &d, int ncu);
+bool chunk_scan_small_pass_fits(const Dims &d, int ncu);  // ... and o.sync may be set (nc <= 16)
+bool chunk_scan_small_pass_shape(const Dims &d);          // the part of it that needs no device query
+hipError_t device_cu_count(int *ncu);  // compute units of the current device
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
-                                   const float *dtc, const void *h_enter, const float *D, void *y,
-                                   const SsdOpts &o, const Dims &d, hipStream_t s);
+                                   const float *dtc, void *h, const float *init, float *fin, const float *D,
+                                   void *y, const SsdOpts &o, const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,

@@ -37,6 +37,15 @@ __device__ __forceinline__ void store4(f16 *p, float4 v)
     *reinterpret_cast<uint2 *>(p) = u;
 }
 
+// The carry is rounded to fp32 by every step and only then to the stored type: an empty
+// asm statement over the fresh carry keeps the compiler from fusing the step's
+// multiply-add with the next store's conversion into one instruction that rounds
+// straight to fp16 (the chunk scan's own Step-3 stores exactly these values).
+__device__ __forceinline__ void carry_fp32(float4 &v)
+{
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 // T: element type of the chunk / entering states in memory (fp32, or fp16 for bf16 inputs)
 template <typename T>
 __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
@@ -68,6 +77,7 @@ __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
             run.y = fmaf(r, run.y, s[k].y);
             run.z = fmaf(r, run.z, s[k].z);
             run.w = fmaf(r, run.w, s[k].w);
+            carry_fp32(run);
         }
     }
     for (; c < nc; ++c) {
@@ -78,6 +88,7 @@ __global__ __launch_bounds__(kPassThreads) void state_passing_kernel(
         run.y = fmaf(r, run.y, s.y);
         run.z = fmaf(r, run.z, s.z);
         run.w = fmaf(r, run.w, s.w);
+        carry_fp32(run);
     }
     if (fin) reinterpret_cast<float4 *>(fin)[bh * PN4 + e] = run;
 }

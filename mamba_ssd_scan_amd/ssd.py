@@ -22,7 +22,7 @@ EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ss
            "ssd_prefill_ex", "ssd_step_ex",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
-           "ssd_chunk_gemm1", "ssd_chunk_scan")
+           "ssd_chunk_gemm1", "ssd_chunk_scan", "ssd_chunk_scan_passing")
 
 
 class SsdError(RuntimeError):
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_gemm1.restype = i
     L.ssd_chunk_scan.argtypes = [vp] * 8 + [i] * 8 + [vp]
     L.ssd_chunk_scan.restype = i
+    L.ssd_chunk_scan_passing.argtypes = [vp] * 11 + [i] * 8 + [vp]
+    L.ssd_chunk_scan_passing.restype = i
     _lib = L
     return L
 
@@ -417,3 +419,42 @@ def chunk_scan(x, C, cb, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stre
                                 _dtype_code(x), batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
                                 _stream(stream)), "ssd_chunk_scan")
     return y
+
+
+SYNC_WORDS_PER_HEAD = 64  # ssd_chunk_scan_passing: one uint32 counter per 256 bytes
+
+
+def alloc_sync(batch, nheads, device="cuda"):
+    """Zeroed counters for ssd_chunk_scan_passing (zero them again before every call)."""
+    torch = _torch()
+    return torch.zeros(batch * nheads * SYNC_WORDS_PER_HEAD, dtype=torch.int32, device=device)
+
+
+def chunk_scan_passing(x, C, cb, acum, dtc, states, sync, D=None, initial_state=None, *, chunk: int, y=None,
+                       final_state="new", stream=None):
+    """ssd_chunk_scan_passing: Step-3 and the chunk scan in one launch (one-round bf16 problems).
+
+    ``states`` float16 [B,H,nc,P,N]: chunk states in, entering states out.  ``sync``: zeroed
+    counters (alloc_sync).  Returns (y fp32, final_state or None); raises SsdError with
+    SSD_ERR_UNSUPPORTED for shapes that do not take this path.
+    """
+    torch = _torch()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = C.shape[2], C.shape[3]
+    _dev(x, C, cb, acum, dtc, states, sync, D, initial_state, y)
+    _f32(D, initial_state, y)
+    if states.dtype != torch.float16:
+        raise TypeError("states must be float16 (bfloat16 inputs)")
+    if sync.numel() * sync.element_size() < batch * nheads * SYNC_WORDS_PER_HEAD * 4:
+        raise ValueError("sync is smaller than batch * nheads * 256 bytes")
+    if y is None:
+        y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
+    if isinstance(final_state, str):
+        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+    _dev(final_state)
+    _f32(final_state)
+    _check(lib().ssd_chunk_scan_passing(_ptr(x), _ptr(C), _ptr(cb), _ptr(acum), _ptr(dtc), _ptr(states),
+                                        _ptr(initial_state), _ptr(final_state), _ptr(D), _ptr(y), _ptr(sync),
+                                        _dtype_code(x), batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                        _stream(stream)), "ssd_chunk_scan_passing")
+    return y, final_state

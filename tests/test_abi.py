@@ -55,7 +55,7 @@ def test_workspace_size_formula():
         nc = -(-l // q)
         bhq = b * h * nc * q * 4
         cb = 4 * b * g * nc * gemm1_steps(q) * 512
-        want = al(al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n) + cb)
+        want = al(al(al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n) + cb) + 256 * b * h)
         assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want
         assert L.ssd_chunk_gemm1_size(b, l, g, q) == cb
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 1, 48) == 0   # bad chunk
@@ -193,6 +193,17 @@ def test_stage_entry_points_reject_before_launch():
     assert L.ssd_chunk_scan(P0, P0, None, P0, P0, P0, None, P0, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
     assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0 + 4, BF, 1, 100, 4, 64, 64, 1, 64, None) == INV
     assert L.ssd_chunk_scan(P0, P0, P0, P0, P0, P0, None, P0, F, 1, 100, 4, 64, 64, 3, 64, None) == INV
+    # ssd_chunk_scan_passing(x, C, cb, acum, dtc, states, init, final, D, y, sync, dtype, B, L, H, P, N, G, Q, s)
+    sp = lambda *a: L.ssd_chunk_scan_passing(*a)
+    assert sp(P0, P0, P0, P0, P0, None, None, None, None, P0, P0, BF, 1, 4096, 24, 64, 128, 1, 256, None) == INV
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, None, BF, 1, 4096, 24, 64, 128, 1, 256, None) == INV
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, P0 + 4, BF, 1, 4096, 24, 64, 128, 1, 256, None) == INV
+    assert sp(P0, P0, P0, P0, P0, P0, P0 + 8, None, None, P0, P0, BF, 1, 4096, 24, 64, 128, 1, 256, None) == INV
+    # shapes the one-round path does not take: fp32, another chunk length or headdim, > 16 chunks
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, P0, F, 1, 4096, 24, 64, 128, 1, 256, None) == UNS
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, P0, BF, 1, 4096, 24, 64, 128, 1, 128, None) == UNS
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, P0, BF, 1, 4096, 24, 32, 128, 1, 256, None) == UNS
+    assert sp(P0, P0, P0, P0, P0, P0, None, None, None, P0, P0, BF, 1, 4097, 24, 64, 128, 1, 256, None) == UNS
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():

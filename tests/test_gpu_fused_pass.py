@@ -1,0 +1,155 @@
+"""GPU tests of the prefill whose chunk scan runs the chunk recurrence itself.
+
+When every (b, h, chunk) item of a bf16 problem with 256-token chunks and
+headdim 64 fits the GPU at once, ssd_prefill runs two launches: chunk state,
+then the chunk scan with the inter-chunk recurrence (Step-3) inside it, each
+workgroup walking the recurrence for its share of the head's state and waiting
+for the head's other chunks.  The recurrence's arithmetic is the standalone
+state-passing kernel's, so the two-launch prefill must equal the three-launch
+one (SSD_PREFILL_STAGED=1) bit for bit, and the fp64 oracle within the bf16
+bar.  Every case runs twice on one workspace with different inputs: the
+per-head counters must start from zero on every call.
+"""
+from __future__ import annotations
+
+import os
+import numpy as np
+import pytest
+
+from mamba_ssd_scan_amd import ssd, synth
+from tests import gpu_helpers as gh
+from tests.util import TOL, rel_err
+
+pytestmark = pytest.mark.gpu
+
+Q = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.lib()
+
+
+def _fits(B, L, H):
+    """Whether the library takes the one-round path: items <= 2 per compute unit."""
+    torch = gh.torch()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    return B * H * ssd.nchunks(L, Q) <= 2 * ncu
+
+
+def _prefill(g, final, ws, staged):
+    """ssd_prefill on the two-launch path, or on the three-launch one (staged)."""
+    if staged:
+        os.environ["SSD_PREFILL_STAGED"] = "1"
+    try:
+        return ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=Q,
+                           final_state="new" if final else None, workspace=ws)
+    finally:
+        os.environ.pop("SSD_PREFILL_STAGED", None)
+
+
+# (B, L, H, N, G, with initial state, with final state, dt mode)
+CASES = [
+    (1, 4096, 24, 128, 1, True, True, "softplus"),   # the 130M layer at 4096 tokens: 16 chunks x 24 heads
+    (2, 700, 8, 64, 2, True, True, "weak"),          # 3 chunks, ragged last chunk, long memory
+    (1, 256, 4, 32, 1, False, True, "softplus"),     # one chunk: the whole state in one workgroup
+    (3, 1000, 6, 128, 3, False, False, "weak"),      # no initial, no final state
+    (1, 21 * 256 - 5, 24, 128, 1, True, True, "weak"),  # 21 chunks: the three-launch path on both sides
+    (2, 15 * 256 + 77, 16, 128, 2, True, True, "weak"),  # 16 chunks, ragged, 512 items
+    (4, 1100, 20, 128, 4, True, True, "weak"),           # 5 chunks, ragged
+    (2, 5 * 256, 40, 64, 1, True, True, "softplus"),    # 5 chunks x 80 head-items
+]
+
+
+@pytest.mark.parametrize("B,L,H,N,G,init,final,mode", CASES)
+def test_fused_pass_equals_stages_and_oracle(B, L, H, N, G, init, final, mode):
+    torch = gh.torch()
+    if not _fits(B, L, H):
+        pytest.skip("problem does not fit this device in one round")
+    ws = ssd.alloc_workspace(B, L, H, 64, N, G, Q)
+    ci = CASES.index((B, L, H, N, G, init, final, mode))
+    for call in range(2):
+        seed = 700 + 10 * ci + call
+        inp = synth.random_prefill(np.random.Generator(np.random.PCG64(seed)), B, L, H, 64, N, G, "bf16",
+                                   init_state=init, dt_mode=mode)
+        print(f"[fused pass] B={B} L={L} H={H} N={N} G={G} init={init} final={final} {mode} call {call}", flush=True)
+        g = gh.upload(inp)
+        y, fin = _prefill(g, final, ws, staged=False)
+        torch.cuda.synchronize()
+        ys, fins = _prefill(g, final, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ys), "two-launch prefill y differs from the three-launch prefill"
+        if final:
+            assert torch.equal(fin, fins), "two-launch prefill final state differs from the three-launch prefill"
+        else:
+            assert fin is None
+        # oracle: sampled heads at the large shapes, every head at the small ones
+        heads = [0, H // 2, H - 1] if B * L * H > 20000 else list(range(H))
+        sub = dict(inp)
+        for k in ("x", "dt"):
+            sub[k] = inp[k][:, :, heads]
+        sub["A"], sub["D"] = inp["A"][heads], inp["D"][heads]
+        sub["h0"] = None if inp["h0"] is None else inp["h0"][:, heads]
+        # the heads keep their groups: expand B and C to one group per kept head
+        grp = [h // (H // G) for h in heads]
+        sub["B"], sub["C"] = inp["B"][:, :, grp], inp["C"][:, :, grp]
+        yo, ho = gh.oracle_prefill(sub)
+        ey = rel_err(y.cpu().numpy()[:, :, heads], yo)
+        msg = f"    y err {ey:.2e}"
+        assert ey < TOL["bf16"], msg
+        if final:
+            es = rel_err(fin.cpu().numpy()[:, heads], ho)
+            msg += f" state err {es:.2e}"
+            assert es < TOL["bf16"], msg
+        print(msg, flush=True)
+
+
+@pytest.mark.parametrize("B,L,H,N,G", [(1, 4096, 24, 128, 1), (2, 700, 8, 64, 2), (3, 2000, 10, 32, 5)])
+def test_chunk_scan_passing_entry_point(B, L, H, N, G):
+    """ssd_chunk_scan_passing against ssd_state_passing + ssd_chunk_scan on the same chunk states."""
+    torch = gh.torch()
+    if not _fits(B, L, H):
+        pytest.skip("problem does not fit this device in one round")
+    inp = synth.random_prefill(np.random.Generator(np.random.PCG64(790 + L)), B, L, H, 64, N, G, "bf16",
+                               dt_mode="weak")
+    print(f"[chunk_scan_passing] B={B} L={L} H={H} N={N} G={G}", flush=True)
+    g = gh.upload(inp)
+    acum, dtc = ssd.chunk_cumsum(g["dt"], g["A"], chunk=Q)
+    st = ssd.chunk_state(g["x"], g["B"], acum, dtc, chunk=Q)
+    cb = ssd.chunk_gemm1(g["B"], g["C"], chunk=Q)
+    st2 = st.clone()
+    fin = ssd.state_passing(st, acum, g["h0"], chunk=Q)
+    y = ssd.chunk_scan(g["x"], g["C"], cb, acum, dtc, st, g["D"], chunk=Q)
+    sync = ssd.alloc_sync(B, H)
+    for call in range(2):
+        st3 = st2.clone()
+        sync.zero_()
+        y2, fin2 = ssd.chunk_scan_passing(g["x"], g["C"], cb, acum, dtc, st3, sync, g["D"], g["h0"], chunk=Q)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2) and torch.equal(fin, fin2), call
+        assert torch.equal(st, st3), "entering states differ"
+        nc = ssd.nchunks(L, Q)
+        assert torch.all(sync.view(B * H, -1)[:, 0] == nc)
+
+
+def test_chunk_scan_passing_rejects_unsupported_shapes():
+    torch = gh.torch()
+    x = torch.zeros((1, 4096, 24, 64), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((1, 4096, 1, 128), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros((1, 24, 16, 64, 128), dtype=torch.float16, device="cuda")
+    acum = torch.zeros((1, 24, 16, 256), dtype=torch.float32, device="cuda")
+    cb = torch.zeros(ssd.chunk_gemm1_size(1, 4096, 1, 128) // 4 + 4, dtype=torch.float32, device="cuda")
+    sync = ssd.alloc_sync(1, 24)
+    with pytest.raises(ssd.SsdError, match="UNSUPPORTED"):
+        ssd.chunk_scan_passing(x, C, cb, acum, acum, st, sync, chunk=128)   # Q = 128
+    big = torch.cuda.get_device_properties(0).multi_processor_count * 2 // 24 + 1  # heads x 1 chunk > 2 per CU
+    xb = torch.zeros((big, 256, 24, 64), dtype=torch.bfloat16, device="cuda")
+    Cb = torch.zeros((big, 256, 1, 128), dtype=torch.bfloat16, device="cuda")
+    stb = torch.zeros((big, 24, 1, 64, 128), dtype=torch.float16, device="cuda")
+    ab = torch.zeros((big, 24, 1, 256), dtype=torch.float32, device="cuda")
+    cbb = torch.zeros(ssd.chunk_gemm1_size(big, 256, 1, 256) // 4 + 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(ssd.SsdError, match="UNSUPPORTED"):
+        ssd.chunk_scan_passing(xb, Cb, cbb, ab, ab, stb, ssd.alloc_sync(big, 24), chunk=256)
