@@ -249,7 +249,7 @@ int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const
     ssd::SsdOpts o = {nullptr, 0, nullptr, 0};
     o.sync = sync;
     return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, dA_cum, dt_c, states, initial_state, final_state, D, y,
-                                                   o, d, (hipStream_t)hip_stream));
+                                                   o, d, ncu, (hipStream_t)hip_stream));
 }
 
 int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
@@ -291,7 +291,7 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
         o.sync = reinterpret_cast<unsigned *>(ws + w.sync);
         SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
         return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, acum, dtc, states, initial_state, final_state, D, y,
-                                                       o, d, s));
+                                                       o, d, ncu, s));
     }
     SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));

@@ -616,7 +616,7 @@ hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, cons
         SsdOpts po = o;
         po.sync = nullptr;  // entering states given
         return launch_chunk_scan_small(x, Cm, cb, acum, dtc, const_cast<void *>(h_enter), nullptr, nullptr, D, y, po,
-                                       d, s);
+                                       d, ncu, s);
     }
     return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
                   : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);

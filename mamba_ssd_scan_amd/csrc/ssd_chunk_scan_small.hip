@@ -44,7 +44,8 @@ template <int P, int N, bool OPT, int PNC>
 __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves per SIMD: <= 128 VGPRs
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, f16 *hen, const float *init, float *fin,
-    unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int nc)
+    unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int nc,
+    int nwhole)
 {
     constexpr int Q = 256, ROWS = 256, NT = 512, NSMAX = 8;
     constexpr int TP = P / 16, KS = N / 32;
@@ -57,7 +58,15 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
-    const int item = blockIdx.x;
+    // Workgroups below nwhole take a whole item; the others take half an item each (half 0
+    // and half 1), one 16-row tile per wavefront.  The first nwhole workgroups land one per
+    // compute unit and the halves fill the second slots, so every compute unit gets the
+    // same work when items are between one and two per compute unit.  The two halves of an
+    // item are 8 workgroups apart: workgroups go to the XCDs in turn, so both land on the
+    // same XCD and the second one's X and state reads hit that XCD's L2.
+    const int wg = blockIdx.x, j = wg - nwhole;
+    const int half = wg < nwhole ? -1 : (j >> 3) & 1;
+    const int item = wg < nwhole ? wg : nwhole + ((j >> 4) << 3) + (j & 7);
     const int c = item % nc, h = (item / nc) % H, b = item / (nc * H), g = h / (H / G);
     const size_t bhc = ((size_t)b * H + h) * nc + c;
     const long tc = (long)c * Q;
@@ -72,7 +81,8 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     constexpr int PN2 = P * N / 2;  // 32-bit words (two fp16 elements) of one state
     constexpr int PS = PASS ? PNC : 1;
     const size_t bh = (size_t)b * H + h;
-    const int share = (PN2 + nc - 1) / nc, w0 = c * share, nw = min(share, PN2 - w0);
+    const int share = (PN2 + nc - 1) / nc, w0 = c * share;
+    const int nw = half == 1 ? 0 : min(share, PN2 - w0);  // (half 1 of an item leaves Step-3 to half 0)
     __amdgpu_buffer_rsrc_t rp = make_rsrc(hen, 0u), ri = rp, rf = rp;
     uint32_t pv[PS], pi0 = 0u, pi1 = 0u;
     float pdec[PS];
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
         // kernel exchanges between workgroups.)
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's stores are done
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0 && half != 1)
             __hip_atomic_fetch_add(sync + ((size_t)b * H + h) * kSyncStride, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -209,8 +219,11 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
         (uint32_t)(((vrows - 1) * H * P + P) * es));
 
 #pragma unroll 1
-    for (int k = 0; k < 2; ++k) {
-        const int t = k == 0 ? wave : 15 - wave;
+    for (int k = 0; k < (half < 0 ? 2 : 1); ++k) {
+        // whole item: tiles w and 15 - w; half 0: tiles {0, 3, 5, 6, 15, 12, 10, 9}, half 1:
+        // {1, 2, 4, 7, 14, 13, 11, 8} by wavefront (36 steps per half, 9 per SIMD)
+        const int t = half < 0 ? (k == 0 ? wave : 15 - wave)
+                               : (int)(((half ? 0x8BDE7421u : 0x9ACF6530u) >> (4 * wave)) & 15u);
         const int ibase = 16 * t;
         const int ns = (ibase + 15) / 32 + 1;  // 32-column steps up to the diagonal
         const int Tt = (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
@@ -396,15 +409,21 @@ bool chunk_scan_small_pass_fits(const Dims &d, int ncu) { return chunk_scan_smal
 
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
                                    const float *dtc, void *h, const float *init, float *fin, const float *D,
-                                   void *y, const SsdOpts &o, const Dims &d, hipStream_t s)
+                                   void *y, const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     if (o.sync && d.nc > 16) return hipErrorInvalidValue;
-    const unsigned nitems = (unsigned)(d.nc * d.H * d.B);
+    const int items = d.nc * d.H * d.B;
+    // Between one and two items per compute unit: split items past the first ncu in two (in
+    // groups of 8, see the kernel), as many as keep the grid within two per compute unit
+    // (the Step-3 wait needs every workgroup resident).
+    const int nsplit = (items > ncu && items <= 2 * ncu) ? min(items - ncu, 2 * ncu - items) / 8 * 8 : 0;
+    const int nwhole = items - nsplit;
+    const unsigned nitems = (unsigned)(nwhole + 2 * nsplit);  // workgroups
     const bf16_t *xx = static_cast<const bf16_t *>(x), *cc = static_cast<const bf16_t *>(Cm);
     f16 *hh = static_cast<f16 *>(h);
 #define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                        \
     chunk_scan_small_kernel<64, NN, OO, PP><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, init, fin, o.sync, \
-                                                                    D, y, o, d.L, d.H, d.G, d.nc)
+                                                                    D, y, o, d.L, d.H, d.G, d.nc, nwhole)
 #define SSD_SMALL_LAUNCH2(NN, PP)                                                                            \
     do {                                                                                                     \
         if (o.z || o.y_bf16) SSD_SMALL_LAUNCH3(NN, true, PP);                                                \

@@ -49,7 +49,7 @@ bool chunk_scan_small_pass_shape(const Dims &d);          // the part of it that
 hipError_t device_cu_count(int *ncu);  // compute units of the current device
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
                                    const float *dtc, void *h, const float *init, float *fin, const float *D,
-                                   void *y, const SsdOpts &o, const Dims &d, hipStream_t s);
+                                   void *y, const SsdOpts &o, const Dims &d, int ncu, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,

@@ -4,7 +4,8 @@ When every (b, h, chunk) item of a bf16 problem with 256-token chunks and
 headdim 64 fits the GPU at once, ssd_prefill runs two launches: chunk state,
 then the chunk scan with the inter-chunk recurrence (Step-3) inside it, each
 workgroup walking the recurrence for its share of the head's state and waiting
-for the head's other chunks.  The recurrence's arithmetic is the standalone
+for the head's other chunks (with between one and two items per compute unit,
+some items are split over two workgroups of one 16-row tile per wavefront).  The recurrence's arithmetic is the standalone
 state-passing kernel's, so the two-launch prefill must equal the three-launch
 one (SSD_PREFILL_STAGED=1) bit for bit, and the fp64 oracle within the bf16
 bar.  Every case runs twice on one workspace with different inputs: the
@@ -60,6 +61,8 @@ CASES = [
     (1, 21 * 256 - 5, 24, 128, 1, True, True, "weak"),  # 21 chunks: the three-launch path on both sides
     (2, 15 * 256 + 77, 16, 128, 2, True, True, "weak"),  # 16 chunks, ragged, 512 items
     (4, 1100, 20, 128, 4, True, True, "weak"),           # 5 chunks, ragged
+    (1, 12 * 256 - 100, 25, 64, 5, True, True, "weak"),  # 300 items: 40 of them split in halves
+    (1, 14 * 256, 32, 128, 1, False, True, "softplus"),  # 448 items: 64 split
     (2, 5 * 256, 40, 64, 1, True, True, "softplus"),    # 5 chunks x 80 head-items
 ]
 
