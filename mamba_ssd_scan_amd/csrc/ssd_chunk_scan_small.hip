@@ -73,6 +73,28 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
     const float Dh = D ? D[h] : 0.f;
 
+    // ---- the first tile's GEMM1 slices (fp16, accumulator order), requested first: the
+    // item's SPC slices (1 KB each) start at slice T(t) for tile t; slots past the tile's
+    // steps read past the range (zeros), so every slot is loaded and the waits stay exact
+    const __amdgpu_buffer_rsrc_t rg =
+        make_rsrc(static_cast<const f16 *>(cbg) + (((size_t)b * G + g) * nc + c) * SPC * 512, SPC * 1024u);
+    f16x8 gs[NSMAX];
+    auto load_g = [&](int t) {
+        const int ns = (16 * t + 15) / 32 + 1;
+        const int Tt = (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
+#pragma unroll
+        for (int s = 0; s < NSMAX; ++s) {
+            const uint32_t off = (s < ns ? (uint32_t)(Tt + s) : (uint32_t)SPC) * 1024u + 16u * lane;
+            gs[s] = __builtin_bit_cast(f16x8, buf_load16(rg, off));
+        }
+    };
+    // whole item: tiles w and 15 - w; half 0: tiles {0, 3, 5, 6, 15, 12, 10, 9}, half 1:
+    // {1, 2, 4, 7, 14, 13, 11, 8} by wavefront (36 steps per half, 9 per SIMD)
+    auto tile_of = [&](int k) {
+        return half < 0 ? (k == 0 ? wave : 15 - wave) : (int)(((half ? 0x8BDE7421u : 0x9ACF6530u) >> (4 * wave)) & 15u);
+    };
+    load_g(tile_of(0));
+
     // ---- Step-3 operands first (PNC > 0): word q = w0 + tid (two state elements) of each
     // chunk's state, the chunks' total decays and the initial state.  Every load is issued
     // unconditionally (slots past nc or past the share read past a buffer range: zeros), so
@@ -220,20 +242,10 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 
 #pragma unroll 1
     for (int k = 0; k < (half < 0 ? 2 : 1); ++k) {
-        // whole item: tiles w and 15 - w; half 0: tiles {0, 3, 5, 6, 15, 12, 10, 9}, half 1:
-        // {1, 2, 4, 7, 14, 13, 11, 8} by wavefront (36 steps per half, 9 per SIMD)
-        const int t = half < 0 ? (k == 0 ? wave : 15 - wave)
-                               : (int)(((half ? 0x8BDE7421u : 0x9ACF6530u) >> (4 * wave)) & 15u);
+        const int t = tile_of(k);
         const int ibase = 16 * t;
         const int ns = (ibase + 15) / 32 + 1;  // 32-column steps up to the diagonal
-        const int Tt = (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
-        // the tile's GEMM1 slices (fp16, accumulator order) and C rows
-        const size_t slice0 = (((size_t)b * G + g) * nc + c) * SPC + Tt;
-        const f16 *gq = static_cast<const f16 *>(cbg) + (slice0 * 64 + lane) * 8;
-        f16x8 gs[NSMAX];
-#pragma unroll
-        for (int s = 0; s < NSMAX; ++s)
-            if (s < ns) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)s * 512);
+        if (k > 0) load_g(t);
 
         f32x4 acc[TP];
 #pragma unroll
