@@ -156,3 +156,47 @@ def test_chunk_scan_passing_rejects_unsupported_shapes():
     cbb = torch.zeros(ssd.chunk_gemm1_size(big, 256, 1, 256) // 4 + 4, dtype=torch.float32, device="cuda")
     with pytest.raises(ssd.SsdError, match="UNSUPPORTED"):
         ssd.chunk_scan_passing(xb, Cb, cbb, ab, ab, stb, ssd.alloc_sync(big, 24), chunk=256)
+
+
+def test_prefill_in_a_callers_graph():
+    """ssd_prefill captured by a caller's graph (torch.cuda.CUDAGraph) on the two-launch path:
+    the per-head counters are zeroed by the chunk-state launch, not by a memset, so every replay
+    starts from zero.  Inputs are rewritten between replays, with eager work and
+    synchronisations in between; every replay must equal an eager call bit for bit."""
+    torch = gh.torch()
+    B, L, H, N, G = 1, 4096, 24, 128, 1
+    if not _fits(B, L, H):
+        pytest.skip("problem does not fit this device in one round")
+    inp = synth.random_prefill(np.random.Generator(np.random.PCG64(880)), B, L, H, 64, N, G, "bf16", dt_mode="weak")
+    g = gh.upload(inp)
+    ws = ssd.alloc_workspace(B, L, H, 64, N, G, Q)
+    y = torch.empty((B, L, H, 64), dtype=torch.float32, device="cuda")
+    fin = torch.empty((B, H, 64, N), dtype=torch.float32, device="cuda")
+    run = lambda: ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=Q, y=y,
+                              final_state=fin, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm the library on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        print(f"[prefill graph] replay {r}", flush=True)
+        new = synth.random_prefill(np.random.Generator(np.random.PCG64(881 + r)), B, L, H, 64, N, G, "bf16",
+                                   dt_mode="weak")
+        nd = gh.upload(new)
+        for k in ("x", "dt", "B", "C", "A", "D", "h0"):
+            g[k].copy_(nd[k])
+        graph.replay()
+        torch.cuda.synchronize()
+        yg, fg = y.clone(), fin.clone()
+        ye, fe = ssd.prefill(nd["x"], nd["dt"], nd["A"], nd["B"], nd["C"], nd["D"], nd["h0"], chunk=Q)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye) and torch.equal(fg, fe), f"replay {r} differs from the eager prefill"
+        (torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")).sum().item()
