@@ -93,7 +93,7 @@ size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim
  * indefinitely while this one starts could delay it (the wait is bounded; past
  * the bound the result is not valid).  Results equal the staged path's bit for bit;
  * SSD_PREFILL_STAGED=1 in the environment (read on every call) forces the staged
- * path, for comparisons.
+ * path with one head per chunk-state workgroup, for comparisons.
  *
  *   x   [B, L, H, P] in_dtype       dt [B, L, H] in_dtype (used as given:
  *   A   [H] fp32                          positive step sizes, no softplus)

@@ -293,7 +293,10 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
         return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, acum, dtc, states, initial_state, final_state, D, y,
                                                        o, d, ncu, s));
     }
-    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
+    // (forced staging also keeps the one-head-per-workgroup chunk-state kernel: the
+    // comparison then covers every fast-path kernel)
+    SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s,
+                                                            !staged_forced())));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, o, d, s));
 }

@@ -425,6 +425,8 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, con
                               float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o, const Dims &d,
                               hipStream_t s)
 {
+    // the kernels size their buffer ranges by the element type: never run one on the other's inputs
+    if (d.bf16 != (sizeof(TIn) == 2)) return hipErrorInvalidValue;
     // More workgroups than two per compute unit: the smaller staged blocks (more resident
     // workgroups) pay off; otherwise the larger ones (fewer barriers).
     int dev = 0, ncu = 0;
@@ -463,10 +465,16 @@ static hipError_t launch_fused_t(const void *x, const void *Bm, const void *dt, 
 
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
                                            float *acum, float *dtc, void *states, const void *Cm, void *cb,
-                                           const SsdOpts &o, const Dims &d, hipStream_t s)
+                                           const SsdOpts &o, const Dims &d, hipStream_t s, bool pair)
 {
-    return d.bf16 ? launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)
-                  : launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    if (!d.bf16) return launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    if (pair) {
+        int ncu = 0;
+        const hipError_t e = device_cu_count(&ncu);
+        if (e != hipSuccess) return e;
+        if (chunk_state_pair_fits(d, ncu)) return launch_chunk_state_pair(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    }
+    return launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
 }
 
 }  // namespace ssd

@@ -22,9 +22,16 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
                               void *states, const Dims &d, hipStream_t s);
 // Step-0 and Step-1 GEMM1 fused into the Step-2 launch: writes acum/dtc (same values as
 // launch_chunk_cumsum), states, and the GEMM1 products cb (same as launch_chunk_gemm1).
+// pair: whether two heads per workgroup may be used where they fit (same results)
 hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const void *dt, const float *A,
                                            float *acum, float *dtc, void *states, const void *Cm, void *cb,
-                                           const SsdOpts &o, const Dims &d, hipStream_t s);
+                                           const SsdOpts &o, const Dims &d, hipStream_t s, bool pair = true);
+// The same launch with two heads of a group per workgroup (bf16, Q = 256, P = 64, an even
+// number of heads per group, the grid resident in one round): identical results.
+bool chunk_state_pair_fits(const Dims &d, int ncu);
+hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
+                                   float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o,
+                                   const Dims &d, hipStream_t s);
 hipError_t launch_state_passing(void *states, const float *acum, const float *init, float *fin,
                                 const Dims &d, hipStream_t s);
 // Step-1 GEMM1 once per (batch, group, chunk): cb holds B * G * nc * gemm1_steps_per_chunk(Q)

@@ -8,7 +8,9 @@ for the head's other chunks (with between one and two items per compute unit,
 some items are split over two workgroups of one 16-row tile per wavefront).  The recurrence's arithmetic is the standalone
 state-passing kernel's, so the two-launch prefill must equal the three-launch
 one (SSD_PREFILL_STAGED=1) bit for bit, and the fp64 oracle within the bf16
-bar.  Every case runs twice on one workspace with different inputs: the
+bar.  The forced three-launch path also keeps one head per chunk-state
+workgroup, so the same comparison covers the two-heads-per-workgroup chunk-state
+kernel the default path uses where it fits.  Every case runs twice on one workspace with different inputs: the
 per-head counters must start from zero on every call.
 """
 from __future__ import annotations
