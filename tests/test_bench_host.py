@@ -1,0 +1,76 @@
+"""CPU tests of bench.py's host logic: which launches a prefill makes at a given compute-unit
+count (the same rules as the library's launchers), the algorithmic byte counts the roofline
+uses, and the refusal of more than one GPU."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from mamba_ssd_scan_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+NCU = 256  # MI355X compute units
+
+
+def _shape(B, L, H, G, Q=256, P=64, N=128, dtype="bf16"):
+    return synth.PrefillShape(B, L, H, P, N, G, Q, dtype)
+
+
+def test_launches_of_the_benchmarked_prefill():
+    s = synth.WORKLOADS[1]  # 130M layer, 4096 tokens: 384 items, 16 chunks, 256 pair workgroups
+    assert bench.scan_kernel_name(s, NCU) == "chunk_scan_small_kernel"
+    assert bench.passing_in_scan(s, NCU)
+    assert bench.chunk_state_pair(s, NCU)
+    assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "chunk_scan_small_kernel"]
+
+
+@pytest.mark.parametrize("w,expect", [
+    (0, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # fp32, Q = 64
+    (2, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # Q = 64
+    (3, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # 5120 items, 2816 pair workgroups
+])
+def test_launches_of_the_other_workloads(w, expect):
+    assert bench.step_kernels(synth.WORKLOADS[w], NCU) == expect
+
+
+def test_launch_rules_at_their_edges():
+    # 21 chunks: one-round scan (21 x 24 = 504 items) but Step-3 stays a launch of its own;
+    # the pair kernel still fits (21 x 16 = 336 workgroups)
+    s = _shape(1, 21 * 256 - 5, 24, 1)
+    assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "state_passing_kernel",
+                                          "chunk_scan_small_kernel"]
+    # 513 items: the persistent scan
+    assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1), NCU) == "chunk_scan_kernel"
+    assert bench.scan_kernel_name(_shape(1, 16 * 256, 32, 1), NCU) == "chunk_scan_small_kernel"  # 512 items
+    # an odd number of heads per group keeps one head per workgroup
+    assert not bench.chunk_state_pair(_shape(1, 12 * 256 - 100, 25, 5), NCU)
+    assert bench.chunk_state_pair(_shape(2, 700, 8, 2, N=64), NCU)
+    # pair workgroups: 32 x (16 + 4) = 640 > 512
+    assert not bench.chunk_state_pair(_shape(1, 32 * 256, 32, 1), NCU)
+    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, Q=128), NCU)
+    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, dtype="f32"), NCU)
+
+
+def test_algorithmic_bytes_of_the_benchmarked_prefill():
+    k = bench.alg_counts(synth.WORKLOADS[1], NCU)["kernels"]
+    x, dt, bc = 4096 * 24 * 64 * 2, 4096 * 24 * 2, 4096 * 128 * 2
+    tab = 2 * 24 * 16 * 256 * 4          # dA_cum and dt per chunk
+    states = 24 * 16 * 64 * 128 * 2      # fp16 chunk states
+    cb = 16 * 72 * 512 * 2               # 72 stored 32-column steps per chunk, 512 fp16 values each
+    y, st = 4096 * 24 * 64 * 4, 24 * 64 * 128 * 4
+    assert k["chunk_state_pair_kernel"]["bytes"] == x + dt + 2 * bc + tab + states + cb == 23134208
+    # Step-3 inside the scan: chunk states and the final state, no entering states (and no
+    # initial state: this workload starts from zero)
+    assert synth.WORKLOADS[1].init_state == "zero"
+    assert k["chunk_scan_small_kernel"]["bytes"] == x + bc + cb + tab + states + st + y == 47841280
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
