@@ -62,24 +62,18 @@ def passing_in_scan(s, ncu=None) -> bool:
     return scan_kernel_name(s, ncu) == "chunk_scan_small_kernel" and -(-s.seqlen // s.chunk) <= 16
 
 
-def chunk_state_pair(s, ncu=None) -> bool:
+def chunk_state_pair(s) -> bool:
     """Whether ssd_prefill's first launch (cumulative decay, chunk states and GEMM1) takes two
-    heads of a group per workgroup: bf16, 256-token chunks, P = 64, an even number of heads
-    per group, and nc * (H/2 + 4G) * B workgroups at most two per compute unit (the same
-    rule as the library)."""
-    if ncu is None:
-        import torch
-        ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    nc = -(-s.seqlen // s.chunk)
-    return (s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and (s.nheads // s.ngroups) % 2 == 0
-            and nc * (s.nheads // 2 + 4 * s.ngroups) * s.batch <= 2 * ncu)
+    heads of a group per workgroup: bf16, 256-token chunks, P = 64 and an even number of heads
+    per group (the same rule as the library)."""
+    return s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and (s.nheads // s.ngroups) % 2 == 0
 
 
 def step_kernels(s, ncu=None) -> list:
     """The kernels one ssd_prefill launches, in order.  The first is the fused launch
     (cumulative decay + chunk states + GEMM1): chunk_state_pair_kernel, or chunk_state_kernel's
     fused instantiation."""
-    first = "chunk_state_pair_kernel" if chunk_state_pair(s, ncu) else "chunk_state_kernel"
+    first = "chunk_state_pair_kernel" if chunk_state_pair(s) else "chunk_state_kernel"
     if passing_in_scan(s, ncu):
         return [first, "chunk_scan_small_kernel"]
     return [first, "state_passing_kernel", scan_kernel_name(s, ncu)]

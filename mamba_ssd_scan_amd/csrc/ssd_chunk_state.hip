@@ -468,12 +468,8 @@ hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const 
                                            const SsdOpts &o, const Dims &d, hipStream_t s, bool pair)
 {
     if (!d.bf16) return launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
-    if (pair) {
-        int ncu = 0;
-        const hipError_t e = device_cu_count(&ncu);
-        if (e != hipSuccess) return e;
-        if (chunk_state_pair_fits(d, ncu)) return launch_chunk_state_pair(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
-    }
+    if (pair && chunk_state_pair_fits(d))
+        return launch_chunk_state_pair(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     return launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
 }
 

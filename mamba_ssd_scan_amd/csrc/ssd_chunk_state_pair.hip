@@ -1,6 +1,6 @@
 // ssd_chunk_state_pair.hip -- Step-0 and Step-2 for two heads per workgroup, with the
 // Step-1 GEMM1 workgroups in the same grid: the prefill's first launch for bf16
-// problems with 256-token chunks and P = 64 whose grid fits the GPU in one round.
+// problems with 256-token chunks, P = 64 and an even number of heads per group.
 //
 // Same arithmetic, in the same order, as ssd_chunk_state.hip with the fused cumulative
 // decay ("Mamba-Family State-Space Model Kernels on a Programmable CGLA", Sec. III-A:
@@ -14,6 +14,9 @@
 //
 // The whole chunk is requested at once (four 64-token blocks in registers), then
 // contracted block by block through double-buffered LDS with one barrier per block.
+// Workgroups share nothing, so the grid may take any number of rounds; on grids much
+// larger than the GPU the whole-chunk requests keep 128 KB of X per compute unit in
+// flight (two workgroups of two heads), which is what HBM needs to stream near its rate.
 #include "ssd_common.h"
 #include "ssd_gemm1_body.h"
 #include "ssd_launch.h"
@@ -222,18 +225,16 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     }
 }
 
-bool chunk_state_pair_fits(const Dims &d, int ncu)
+bool chunk_state_pair_fits(const Dims &d)
 {
-    const int hg = d.G > 0 ? d.H / d.G : 0;
-    const long nwg = (long)d.nc * (d.H / 2 + 4L * d.G) * d.B;
-    return d.bf16 && d.Q == 256 && d.P == 64 && hg % 2 == 0 && nwg <= 2L * ncu;
+    return d.bf16 && d.Q == 256 && d.P == 64 && d.G > 0 && (d.H / d.G) % 2 == 0;
 }
 
 hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
                                    float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o,
                                    const Dims &d, hipStream_t s)
 {
-    if (!d.bf16 || d.Q != 256 || d.P != 64 || d.G <= 0 || (d.H / d.G) % 2 != 0) return hipErrorInvalidValue;
+    if (!chunk_state_pair_fits(d)) return hipErrorInvalidValue;
     const dim3 grid(d.nc, d.H / 2 + 4 * d.G, d.B);
     const bf16_t *xx = static_cast<const bf16_t *>(x), *bb = static_cast<const bf16_t *>(Bm),
                  *dd = static_cast<const bf16_t *>(dt), *cc = static_cast<const bf16_t *>(Cm);

@@ -27,8 +27,8 @@ hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const 
                                            float *acum, float *dtc, void *states, const void *Cm, void *cb,
                                            const SsdOpts &o, const Dims &d, hipStream_t s, bool pair = true);
 // The same launch with two heads of a group per workgroup (bf16, Q = 256, P = 64, an even
-// number of heads per group, the grid resident in one round): identical results.
-bool chunk_state_pair_fits(const Dims &d, int ncu);
+// number of heads per group): identical results.
+bool chunk_state_pair_fits(const Dims &d);
 hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
                                    float *dtc, void *states, const void *Cm, void *cb, const SsdOpts &o,
                                    const Dims &d, hipStream_t s);

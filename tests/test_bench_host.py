@@ -24,22 +24,21 @@ def test_launches_of_the_benchmarked_prefill():
     s = synth.WORKLOADS[1]  # 130M layer, 4096 tokens: 384 items, 16 chunks, 256 pair workgroups
     assert bench.scan_kernel_name(s, NCU) == "chunk_scan_small_kernel"
     assert bench.passing_in_scan(s, NCU)
-    assert bench.chunk_state_pair(s, NCU)
+    assert bench.chunk_state_pair(s)
     assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "chunk_scan_small_kernel"]
 
 
 @pytest.mark.parametrize("w,expect", [
     (0, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # fp32, Q = 64
     (2, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # Q = 64
-    (3, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # 5120 items, 2816 pair workgroups
+    (3, ["chunk_state_pair_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # 5120 items
 ])
 def test_launches_of_the_other_workloads(w, expect):
     assert bench.step_kernels(synth.WORKLOADS[w], NCU) == expect
 
 
 def test_launch_rules_at_their_edges():
-    # 21 chunks: one-round scan (21 x 24 = 504 items) but Step-3 stays a launch of its own;
-    # the pair kernel still fits (21 x 16 = 336 workgroups)
+    # 21 chunks: one-round scan (21 x 24 = 504 items) but Step-3 stays a launch of its own
     s = _shape(1, 21 * 256 - 5, 24, 1)
     assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "state_passing_kernel",
                                           "chunk_scan_small_kernel"]
@@ -47,12 +46,11 @@ def test_launch_rules_at_their_edges():
     assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1), NCU) == "chunk_scan_kernel"
     assert bench.scan_kernel_name(_shape(1, 16 * 256, 32, 1), NCU) == "chunk_scan_small_kernel"  # 512 items
     # an odd number of heads per group keeps one head per workgroup
-    assert not bench.chunk_state_pair(_shape(1, 12 * 256 - 100, 25, 5), NCU)
-    assert bench.chunk_state_pair(_shape(2, 700, 8, 2, N=64), NCU)
-    # pair workgroups: 32 x (16 + 4) = 640 > 512
-    assert not bench.chunk_state_pair(_shape(1, 32 * 256, 32, 1), NCU)
-    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, Q=128), NCU)
-    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, dtype="f32"), NCU)
+    assert not bench.chunk_state_pair(_shape(1, 12 * 256 - 100, 25, 5))
+    assert bench.chunk_state_pair(_shape(2, 700, 8, 2, N=64))
+    assert bench.chunk_state_pair(_shape(1, 32 * 256, 32, 1))  # any number of rounds
+    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, Q=128))
+    assert not bench.chunk_state_pair(_shape(1, 4096, 24, 1, dtype="f32"))
 
 
 def test_algorithmic_bytes_of_the_benchmarked_prefill():

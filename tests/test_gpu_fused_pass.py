@@ -10,7 +10,8 @@ state-passing kernel's, so the two-launch prefill must equal the three-launch
 one (SSD_PREFILL_STAGED=1) bit for bit, and the fp64 oracle within the bf16
 bar.  The forced three-launch path also keeps one head per chunk-state
 workgroup, so the same comparison covers the two-heads-per-workgroup chunk-state
-kernel the default path uses where it fits.  Every case runs twice on one workspace with different inputs: the
+kernel the default path uses (on one-round grids here, on grids of many rounds in the last
+test).  Every case runs twice on one workspace with different inputs: the
 per-head counters must start from zero on every call.
 """
 from __future__ import annotations
@@ -202,3 +203,23 @@ def test_prefill_in_a_callers_graph():
         torch.cuda.synchronize()
         assert torch.equal(yg, ye) and torch.equal(fg, fe), f"replay {r} differs from the eager prefill"
         (torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")).sum().item()
+
+
+@pytest.mark.parametrize("B,L,H,N,G", [
+    (1, 16384, 80, 128, 1),      # the 2.7B layer at 16384 tokens: 64 chunks, 2816 workgroups
+    (2, 9 * 256 + 31, 12, 64, 3),  # ragged, two heads per group
+    (3, 3000, 8, 32, 1),
+])
+def test_two_head_chunk_state_on_grids_of_many_rounds(B, L, H, N, G):
+    """The two-heads-per-workgroup chunk state also runs where its grid takes several rounds
+    (it needs no co-residency); the prefill then equals the forced-staged one, which keeps one
+    head per workgroup, bit for bit."""
+    torch = gh.torch()
+    inp = synth.random_prefill(np.random.Generator(np.random.PCG64(950 + H)), B, L, H, 64, N, G, "bf16",
+                               init_state=True, dt_mode="weak")
+    print(f"[two-head chunk state, many rounds] B={B} L={L} H={H} N={N} G={G}", flush=True)
+    g = gh.upload(inp)
+    y, fin = _prefill(g, True, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=False)
+    ys, fins = _prefill(g, True, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ys) and torch.equal(fin, fins)
