@@ -435,7 +435,7 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=PREFILL_WORKLOAD, choices=[0, 1, 2, 3],
                     help="prefill workload timed as the step (default 1; the others are for comparison)")
