@@ -133,6 +133,36 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
                    int nheads, int headdim, int dstate, int ngroups, int chunk,
                    void *workspace, size_t workspace_bytes, void *hip_stream);
 /*
+ * ssd_prefill_ex with the sequence inputs read in place from wider token rows, so
+ * that a Mamba-2 layer needs no copies between its projections and the SSD core
+ * ("Mamba-Family State-Space Model Kernels on a Programmable CGLA", Sec. III-A: the
+ * input projection yields z, x, B, C and the step sizes side by side for each token).
+ * x, B and C can then point into the convolved [x | B | C] rows and dt and z into the
+ * input-projection rows; each is read as [B, L, ...] with consecutive tokens the given
+ * number of elements apart, and batches L tokens apart (token (b, t) of x starts at
+ * x + (b * L + t) * x_stride).
+ *
+ *   x_stride    >= H * P     (0: H * P, dense)
+ *   bc_stride   >= G * N     B and C share it (0: G * N)
+ *   dt_stride   >= H         (0: H)
+ *   z_stride    >= H * P     (0: H * P; unused without z)
+ * x, B and C are read with 16-byte loads: their pointers must be 16-byte aligned and
+ * x_stride and bc_stride whole multiples of 16 bytes (8 bf16 or 4 fp32 elements).
+ * y, the states and the workspace are as in ssd_prefill_ex (y dense [B, L, H, P]).
+ * Errors: SSD_ERR_INVALID_ARG for a stride below its dense row or misaligned;
+ * SSD_ERR_UNSUPPORTED when chunk * stride * element size reaches 2^31 bytes (one
+ * chunk is addressed with 32-bit offsets).  ssd_prefill_ex is this call with all
+ * four strides 0.
+ */
+int ssd_prefill_strided(const void *x, const void *dt, const float *A, const void *Bm,
+                        const void *Cm, const float *D, const float *dt_bias, int dt_softplus,
+                        const void *z, const float *initial_state, float *final_state, void *y,
+                        ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                        int nheads, int headdim, int dstate, int ngroups, int chunk,
+                        long long x_stride, long long bc_stride, long long dt_stride,
+                        long long z_stride, void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+/*
  * One decode token for every (b, h), fused: the state is read once,
  * decayed, updated with the token's input and written back in place, and
  * the output is read off the updated state.

@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <new>
 
 #include "ssd_launch.h"
@@ -86,6 +87,7 @@ ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, 
     d.B = batch; d.L = seqlen; d.H = nheads; d.P = headdim; d.N = dstate; d.G = ngroups; d.Q = chunk;
     d.nc = chunk > 0 ? (seqlen + chunk - 1) / chunk : 0;
     d.bf16 = (t == SSD_BF16);
+    d.sx = nheads * headdim; d.sbc = ngroups * dstate; d.sdt = nheads; d.sz = nheads * headdim;
     return d;
 }
 
@@ -137,7 +139,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (3 << 16) | 1; }
+int ssd_version(void) { return (3 << 16) | 2; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -252,16 +254,26 @@ int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const
                                                    o, d, ncu, (hipStream_t)hip_stream));
 }
 
-int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
-                   const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
-                   float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
-                   int nheads, int headdim, int dstate, int ngroups, int chunk, void *workspace,
-                   size_t workspace_bytes, void *hip_stream)
+int ssd_prefill_strided(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                        const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                        float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch,
+                        int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, long long x_stride,
+                        long long bc_stride, long long dt_stride, long long z_stride, void *workspace,
+                        size_t workspace_bytes, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
     SSD_TRY(check_dtype(y_dtype));
     if (!aligned(dt_bias, 4) || !aligned(z, in_size(in_dtype))) return SSD_ERR_INVALID_ARG;
     SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
+    // token strides: 0 = dense; x, B and C rows are read with 16-byte loads
+    const long long esz = (long long)in_size(in_dtype), hp = (long long)nheads * headdim,
+                    gn = (long long)ngroups * dstate;
+    const long long sx = x_stride ? x_stride : hp, sbc = bc_stride ? bc_stride : gn,
+                    sdt = dt_stride ? dt_stride : nheads, sz = z_stride ? z_stride : hp;
+    if (sx < hp || sbc < gn || sdt < nheads || sz < hp) return SSD_ERR_INVALID_ARG;
+    if ((sx * esz) % 16 != 0 || (sbc * esz) % 16 != 0) return SSD_ERR_INVALID_ARG;
+    const long long smax = std::max(std::max(sx, sbc), std::max(sdt, sz));
+    if ((long long)chunk * esz * smax >= 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;  // 32-bit offsets per chunk
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)hip_stream;
     if (seqlen == 0) {
@@ -281,7 +293,8 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
     float *dtc = reinterpret_cast<float *>(ws + w.dtc);
     void *states = ws + w.states;
     float *cb = reinterpret_cast<float *>(ws + w.cb);
-    const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
+    ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype);
+    d.sx = (int)sx; d.sbc = (int)sbc; d.sdt = (int)sdt; d.sz = (int)sz;
 
     ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
     int ncu = 0;
@@ -299,6 +312,17 @@ int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm
                                                             !staged_forced())));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, o, d, s));
+}
+
+int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                   const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                   float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk, void *workspace,
+                   size_t workspace_bytes, void *hip_stream)
+{
+    return ssd_prefill_strided(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype,
+                               y_dtype, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, 0, 0, 0, 0, workspace,
+                               workspace_bytes, hip_stream);
 }
 
 int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_gemm1_kernel(const TIn *__restr
 {
     typedef Gemm1Chunk<TIn, N, NW, 16 * NW> K;
     __shared__ __align__(16) unsigned char smem[K::kLdsBytes];
-    K::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+    K::run(Bm, Cm, cb, L, G, G * N, Q, nc, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
 // Steps of 32 columns per chunk of q tokens (T(q/16) above).

@@ -65,7 +65,7 @@ template <typename TIn, int P, int N, int NW, bool OPT>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
-    const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int Q, int nc,
+    const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sz, int Q, int nc,
     int nitems)
 {
     typedef ScanLds<TIn, P, N, NW> S;
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     // buffer resource over the item's valid rows of X: rows past the chunk or the
     // sequence read as zeros (the masked columns of the last step multiply finite values)
     auto x_rsrc = [&](const Item &it) {
-        return make_rsrc(x + ((size_t)it.b * L + it.tc) * H * P + (size_t)it.h * P,
-                         (uint32_t)(((it.vrows - 1) * H * P + P) * sizeof(TIn)));
+        return make_rsrc(x + ((size_t)it.b * L + it.tc) * sx + (size_t)it.h * P,
+                         (uint32_t)(((it.vrows - 1) * sx + P) * sizeof(TIn)));
     };
 
     // ---- staging (bf16 inputs): direct-to-LDS loads of the raw X rows, the raw fp32
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 const int wi = k * NW + wave;
                 const int byte = 1024 * wi + 16 * lane, row = byte / (2 * P), col = byte % (2 * P);
                 buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
-                                 (uint32_t)(row * H * P * 2 + col));
+                                 (uint32_t)(row * sx * 2 + col));
             }
             const f16 *hen = static_cast<const f16 *>(henv);
             const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + it.bhc * P * N, live ? (uint32_t)S::SH : 0u);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 if (u < XU) {
                     const int jr = u / (P / 8), cg = u % (P / 8);
 #pragma unroll
-                    for (int e = 0; e < XR; ++e) px[k][e].load(rx, (uint32_t)((XR * jr + e) * H * P + 8 * cg));
+                    for (int e = 0; e < XR; ++e) px[k][e].load(rx, (uint32_t)((XR * jr + e) * sx + 8 * cg));
                 }
             }
             if constexpr (!F32) {
@@ -277,9 +277,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     // past the buffer range, which return zeros): the wait before the next barrier then
     // knows exactly how many loads follow the staging loads it has to wait for.
     auto load_tile_operands = [&](const Item &it) {
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * G * N + (size_t)it.g * N,
-                                                    (uint32_t)(((it.vrows - 1) * G * N + N) * sizeof(TIn)));
-        const uint32_t row = (uint32_t)((ibase + li) * G * N);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * sbc + (size_t)it.g * N,
+                                                    (uint32_t)(((it.vrows - 1) * sbc + N) * sizeof(TIn)));
+        const uint32_t row = (uint32_t)((ibase + li) * sbc);
         if constexpr (F32) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -510,15 +510,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         }
         // ---- optional output gate: y <- y * z * sigmoid(z), z laid out as x
         if (OPT && opt.z && t >= 0) {
-            const TIn *zp = static_cast<const TIn *>(opt.z) + ((size_t)cur.b * L + cur.tc) * H * P + (size_t)cur.h * P;
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * H * P + P) * sizeof(TIn)));
+            const TIn *zp = static_cast<const TIn *>(opt.z) + ((size_t)cur.b * L + cur.tc) * sz + (size_t)cur.h * P;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * sz + P) * sizeof(TIn)));
             // all of the lane's z values are requested before the first is used
             uint32_t zr[TP][4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) {
-                    const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * H * P + pt * 16 + li);
+                    const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * sz + pt * 16 + li);
                     if constexpr (F32)
                         zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)(4u * e), 0, 0);
                     else
@@ -558,10 +558,10 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
         const int nwg = nitems < ncu * per_cu ? nitems : ncu * per_cu;                                   \
         if (o.z || o.y_bf16)                                                                              \
             chunk_scan_kernel<TIn, P, NN, NWV, true><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
-                                                                              d.L, d.H, d.G, d.Q, d.nc, nitems); \
+                                                                              d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems); \
         else                                                                                              \
             chunk_scan_kernel<TIn, P, NN, NWV, false><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
-                                                                               d.L, d.H, d.G, d.Q, d.nc, nitems); \
+                                                                               d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems); \
     } while (0)
 #define SSD_SCAN_BY_Q(NN)                                  \
     if (d.Q == 256)                                        \

@@ -44,7 +44,8 @@ template <int P, int N, bool OPT, int PNC>
 __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves per SIMD: <= 128 VGPRs
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, f16 *hen, const float *init, float *fin,
-    unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int nc,
+    unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int sx, int sbc,
+    int sz, int nc,
     int nwhole)
 {
     constexpr int Q = 256, ROWS = 256, NT = 512, NSMAX = 8;
@@ -153,8 +154,8 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 
     // ---- the item's X rows (fp16), entering state and decay tables into LDS
     {
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P,
-                                                    (uint32_t)(((vrows - 1) * H * P + P) * 2));
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * sx + (size_t)h * P,
+                                                    (uint32_t)(((vrows - 1) * sx + P) * 2));
         constexpr int XU = ROWS * (P / 8), XPT = XU / NT;
         constexpr int HU = P * N / 8, HPT = (HU + NT - 1) / NT;
         Raw8<bf16_t> px[XPT];
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int u = tid + k * NT;
-            px[k].load(rx, (uint32_t)((u / (P / 8)) * H * P + 8 * (u % (P / 8))));
+            px[k].load(rx, (uint32_t)((u / (P / 8)) * sx + 8 * (u % (P / 8))));
         }
         const f16 *hp = hen + bhc * P * N;
         if constexpr (!PASS) {
@@ -231,8 +232,8 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
         __syncthreads();
     }
 
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)b * L + tc) * G * N + (size_t)g * N,
-                                                (uint32_t)(((vrows - 1) * G * N + N) * 2));
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)b * L + tc) * sbc + (size_t)g * N,
+                                                (uint32_t)(((vrows - 1) * sbc + N) * 2));
     const size_t base_y = (((size_t)b * L + tc) * H + h) * P;
     const bool y16 = OPT && opt.y_bf16;
     const uint32_t es = y16 ? 2u : 4u;
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
         // loaded only now, so that they do not hold registers through the steps)
         {
             bf16x8 cb[KS];
-            const uint32_t row = (uint32_t)((ibase + li) * G * N);
+            const uint32_t row = (uint32_t)((ibase + li) * sbc);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
             f32x4 off[TP];
@@ -375,15 +376,15 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
         }
         // ---- optional output gate: y <- y * z * sigmoid(z), z laid out as x
         if (OPT && opt.z) {
-            const bf16_t *zp = static_cast<const bf16_t *>(opt.z) + ((size_t)b * L + tc) * H * P + (size_t)h * P;
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((vrows - 1) * H * P + P) * 2));
+            const bf16_t *zp = static_cast<const bf16_t *>(opt.z) + ((size_t)b * L + tc) * sz + (size_t)h * P;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((vrows - 1) * sz + P) * 2));
             uint32_t zr[TP][4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt)
                     zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rz, (int)(2u * (uint32_t)((ibase + 4 * lg + r) * H * P + pt * 16 + li)), 0, 0);
+                        rz, (int)(2u * (uint32_t)((ibase + 4 * lg + r) * sz + pt * 16 + li)), 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -440,7 +441,8 @@ hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb
     f16 *hh = static_cast<f16 *>(h);
 #define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                        \
     chunk_scan_small_kernel<64, NN, OO, PP><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, init, fin, o.sync, \
-                                                                    D, y, o, d.L, d.H, d.G, d.nc, nwhole)
+                                                                    D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc, \
+                                                                    nwhole)
 #define SSD_SMALL_LAUNCH2(NN, PP)                                                                            \
     do {                                                                                                     \
         if (o.z || o.y_bf16) SSD_SMALL_LAUNCH3(NN, true, PP);                                                \

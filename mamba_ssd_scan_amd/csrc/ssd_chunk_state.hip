@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                                                           float *__restrict__ dtc,
                                                           void *__restrict__ states,
                                                           const TIn *__restrict__ Cm, void *__restrict__ cb,
-                                                          SsdOpts opt, int L, int H, int G, int Q, int nc)
+                                                          SsdOpts opt, int L, int H, int G, int sx, int sbc, int sdt, int Q, int nc)
 {
     typedef Traits<TIn> Tr;
     typedef typename Tr::op_t op_t;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     __shared__ __align__(16) unsigned char smem[kBytes];
     if constexpr (GR > 0) {
         if ((int)blockIdx.y < 4 * G) {
-            G1::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y >> 2, blockIdx.z, smem, blockIdx.y & 3);
+            G1::run(Bm, Cm, cb, L, G, sbc, Q, nc, blockIdx.x, blockIdx.y >> 2, blockIdx.z, smem, blockIdx.y & 3);
             return;
         }
     }
@@ -101,9 +101,9 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     // the chunk or the sequence return zeros.
     const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
     const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P, (uint32_t)(((vrows - 1) * H * P + P) * sizeof(TIn)));
+        make_rsrc(x + ((size_t)b * L + tc) * sx + (size_t)h * P, (uint32_t)(((vrows - 1) * sx + P) * sizeof(TIn)));
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(Bm + ((size_t)b * L + tc) * G * N + (size_t)g * N, (uint32_t)(((vrows - 1) * G * N + N) * sizeof(TIn)));
+        make_rsrc(Bm + ((size_t)b * L + tc) * sbc + (size_t)g * N, (uint32_t)(((vrows - 1) * sbc + N) * sizeof(TIn)));
 
     // (live == false: a block past the chunk; its loads read an empty range)
     auto prefetch = [&](Stage &st, int jbk, bool live = true) {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
             if (XU % 256 == 0 || u < XU) {  // (true at compile time when every thread has a unit)
                 const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) st.x[k][e].load(bx, (uint32_t)((j + e) * H * P + 8 * pg));
+                for (int e = 0; e < 2; ++e) st.x[k][e].load(bx, (uint32_t)((j + e) * sx + 8 * pg));
             }
         }
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
             if (BU % 256 == 0 || u < BU) {
                 const int jp = u / (N / 8), ng = u % (N / 8), j = j0 + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) st.b[k][e].load(bb, (uint32_t)((j + e) * G * N + 8 * ng));
+                for (int e = 0; e < 2; ++e) st.b[k][e].load(bb, (uint32_t)((j + e) * sbc + 8 * ng));
             }
         }
     };
@@ -247,12 +247,12 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
         if (wave == 0) {
             const long vq = (L - tc) < Q ? (L - tc) : Q;
             const __amdgpu_buffer_rsrc_t rd =
-                make_rsrc(dt + ((size_t)b * L + tc) * H + h, (uint32_t)(((vq - 1) * H + 1) * sizeof(TIn)));
+                make_rsrc(dt + ((size_t)b * L + tc) * sdt + h, (uint32_t)(((vq - 1) * sdt + 1) * sizeof(TIn)));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 // (for k >= per this reads a neighbour's token, or zero past the range: unused,
                 // but a select here would become a branch, and a branch hides the load count)
-                const uint32_t off = (uint32_t)((lane * per + k) * H * sizeof(TIn));
+                const uint32_t off = (uint32_t)((lane * per + k) * sdt * sizeof(TIn));
                 if constexpr (F32)
                     dtf[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)off, 0, 0));
                 else
@@ -403,7 +403,7 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
               *cc = static_cast<const TIn *>(Cm);
 #define SSD_CS_LAUNCH(NN, JJ)                                                                                      \
     chunk_state_kernel<TIn, P, NN, FUSE, GR, JJ><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, o, \
-                                                                      d.L, d.H, d.G, d.Q, d.nc)
+                                                                      d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.Q, d.nc)
 #define SSD_CS_BY_JB(NN)          \
     if (big || sizeof(TIn) == 4)  \
         SSD_CS_LAUNCH(NN, 32);    \

@@ -27,7 +27,8 @@ template <int N>
 __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Bm, const bf16_t *__restrict__ dt,
     const float *__restrict__ A, float *__restrict__ acum, float *__restrict__ dtc, f16 *__restrict__ states,
-    const bf16_t *__restrict__ Cm, void *__restrict__ cb, SsdOpts opt, int L, int H, int G, int nc)
+    const bf16_t *__restrict__ Cm, void *__restrict__ cb, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sdt,
+    int nc)
 {
     constexpr int P = 64, Q = 256, JB = 64, NBLK = Q / JB;
     constexpr int LDXR = P + 16, LDBR = N + 16;  // (width + 16) halves: the transposing reads hit distinct banks
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     if ((int)blockIdx.y < 4 * G) {
         // GEMM1 workgroups: four wavefronts each (the others have nothing to do)
         if (tid >= 256) return;
-        G1::run(Bm, Cm, cb, L, G, Q, nc, blockIdx.x, blockIdx.y >> 2, blockIdx.z, smem, blockIdx.y & 3);
+        G1::run(Bm, Cm, cb, L, G, sbc, Q, nc, blockIdx.x, blockIdx.y >> 2, blockIdx.z, smem, blockIdx.y & 3);
         return;
     }
     // xs[buf][hw]: the head's weighted X block (fp16); bs[buf]: the shared B block (fp16);
@@ -73,17 +74,17 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     // ---- prologue: the step sizes first (wavefront 0 of each head), then every block of
     // the chunk: X for this thread's head, B shared by the pair
     const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * H * P + (size_t)h * P,
-                                                (uint32_t)(((vrows - 1) * H * P + P) * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + ((size_t)b * L + tc) * G * N + (size_t)g * N,
-                                                (uint32_t)(((vrows - 1) * G * N + N) * 2));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * sx + (size_t)h * P,
+                                                (uint32_t)(((vrows - 1) * sx + P) * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + ((size_t)b * L + tc) * sbc + (size_t)g * N,
+                                                (uint32_t)(((vrows - 1) * sbc + N) * 2));
     unsigned short dtraw[4];
     const float dbias = opt.dt_bias ? opt.dt_bias[h] : 0.f;  // read before the block loads
     if (lw == 0) {
         const __amdgpu_buffer_rsrc_t rd =
-            make_rsrc(dt + ((size_t)b * L + tc) * H + h, (uint32_t)(((vrows - 1) * H + 1) * 2));
+            make_rsrc(dt + ((size_t)b * L + tc) * sdt + h, (uint32_t)(((vrows - 1) * sdt + 1) * 2));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dtraw[k] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)((lane * 4 + k) * H * 2), 0, 0);
+        for (int k = 0; k < 4; ++k) dtraw[k] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)((lane * 4 + k) * sdt * 2), 0, 0);
     }
     Raw8<bf16_t> px[NBLK][2], pb[NBLK][BPT][2];
 #pragma unroll
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
         {
             const int jp = ht / (P / 8), pg = ht % (P / 8), j = JB * m + 2 * jp;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) px[m][e].load(rx, (uint32_t)((j + e) * H * P + 8 * pg));
+            for (int e = 0; e < 2; ++e) px[m][e].load(rx, (uint32_t)((j + e) * sx + 8 * pg));
         }
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
             if (BU % 512 == 0 || u < BU) {
                 const int jp = u / (N / 8), ng = u % (N / 8), j = JB * m + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) pb[m][k][e].load(rb, (uint32_t)((j + e) * G * N + 8 * ng));
+                for (int e = 0; e < 2; ++e) pb[m][k][e].load(rb, (uint32_t)((j + e) * sbc + 8 * ng));
             }
         }
     }
@@ -240,7 +241,8 @@ hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt
                  *dd = static_cast<const bf16_t *>(dt), *cc = static_cast<const bf16_t *>(Cm);
     f16 *st = static_cast<f16 *>(states);
 #define SSD_CSP_LAUNCH(NN) \
-    chunk_state_pair_kernel<NN><<<grid, 512, 0, s>>>(xx, bb, dd, A, acum, dtc, st, cc, cb, o, d.L, d.H, d.G, d.nc)
+    chunk_state_pair_kernel<NN><<<grid, 512, 0, s>>>(xx, bb, dd, A, acum, dtc, st, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, \
+                                                     d.sdt, d.nc)
     switch (d.N) {
     case 32: SSD_CSP_LAUNCH(32); break;
     case 64: SSD_CSP_LAUNCH(64); break;

@@ -44,8 +44,8 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
     // tile tile_of(part, w) alone, so the four workgroups take the balanced tile sets
     // {p, 7-p, 8+p, 15-p} and no wavefront walks more than one tile.
     static __device__ __forceinline__ void run(const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
-                                               void *__restrict__ cb, int L, int G, int Q, int nc, int c, int g,
-                                               int b, unsigned char *smem, int part = -1)
+                                               void *__restrict__ cb, int L, int G, int sbc, int Q, int nc, int c,
+                                               int g, int b, unsigned char *smem, int part = -1)
     {
         raw_t *bs = reinterpret_cast<raw_t *>(smem);
         const int tid = threadIdx.x, lane = tid & 63;
@@ -55,16 +55,17 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
         const int nt = Q >> 4;
 
         const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
-        const size_t row0 = ((size_t)b * L + tc) * G + g;  // (token, group) row of the chunk's first token
-        const uint32_t bytes = (uint32_t)(((vrows - 1) * G + 1) * N * sizeof(TIn));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + row0 * N, bytes);
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + row0 * N, bytes);
+        // the group's N values of the chunk's first token; tokens sbc elements apart
+        const size_t row0 = ((size_t)b * L + tc) * sbc + (size_t)g * N;
+        const uint32_t bytes = (uint32_t)(((vrows - 1) * sbc + N) * sizeof(TIn));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + row0, bytes);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + row0, bytes);
 
         // C rows of a row tile (the GEMM1^T B operand), held in registers
         bf16x8 cbf[F32 ? 1 : KS];
         float cf[F32 ? KS : 1];
         auto load_c = [&](int t) {
-            const uint32_t row = (uint32_t)((16 * t + li) * G * N);
+            const uint32_t row = (uint32_t)((16 * t + li) * sbc);
             if constexpr (F32) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
@@ -94,7 +95,7 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
                 const int u = tid + k * NT;
                 if (u < BU) {
                     if (q < npass)
-                        bv[q][k].load(rb, (uint32_t)((q * PASS_ROWS + u / (N / 8)) * G * N + 8 * (u % (N / 8))));
+                        bv[q][k].load(rb, (uint32_t)((q * PASS_ROWS + u / (N / 8)) * sbc + 8 * (u % (N / 8))));
                     else
                         bv[q][k].zero();
                 }

@@ -13,6 +13,9 @@ namespace ssd {
 struct Dims {
     int B, L, H, P, N, G, Q, nc;  // batch, seqlen, heads, headdim, dstate, groups, chunk, chunks
     bool bf16;                    // input storage: bf16 (true) or fp32
+    // elements between consecutive tokens of x, of B and C, of dt and of z (dense: H*P, G*N,
+    // H, H*P); the prefill's kernels read their inputs with these, y is always dense
+    int sx, sbc, sdt, sz;
 };
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, float *dtc,

@@ -19,7 +19,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_prefill_ex", "ssd_step_ex",
+           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_step_ex",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
            "ssd_chunk_gemm1", "ssd_chunk_scan", "ssd_chunk_scan_passing")
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.ssd_step.restype = i
     L.ssd_prefill_ex.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [vp, sz, vp]
     L.ssd_prefill_ex.restype = i
+    ll = ctypes.c_longlong
+    L.ssd_prefill_strided.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [ll] * 4 + [vp, sz, vp]
+    L.ssd_prefill_strided.restype = i
     L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
     L.ssd_step_ex.restype = i
     L.ssd_decode_graph_create.argtypes = [ctypes.POINTER(vp), i] + [vp] * 8 + [i] + [vp] * 2 + [i] * 7
@@ -124,6 +127,45 @@ def _dev(*ts):
                 raise ValueError("all tensors must be contiguous")
 
 
+def _token_stride(t, name: str) -> int:
+    """Elements between consecutive tokens of a [B, L, ...] sequence input.
+
+    Each token's values must be contiguous; the tokens may sit in wider rows (a view
+    into a buffer holding other channels too), with batches L tokens apart.
+    """
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    shape, st = t.shape, t.stride()
+    if t.numel() == 0:  # nothing is read: treat as dense
+        tail = 1
+        for v in shape[2:]:
+            tail *= v
+        return tail
+    tail = 1
+    for k in range(t.dim() - 1, 1, -1):
+        if shape[k] != 1 and st[k] != tail:
+            raise ValueError(f"{name}: the values of one token must be contiguous (strides {st})")
+        tail *= shape[k]
+    b, l = shape[0], shape[1]
+    ts = st[1] if l > 1 else (st[0] if b > 1 else tail)
+    if b > 1 and st[0] != l * ts:
+        raise ValueError(f"{name}: batches must be seqlen tokens apart (strides {st})")
+    return ts
+
+
+def _seq_strides(x, dt, B, C, z):
+    """Token strides (x, B and C, dt, z) and whether all are dense."""
+    sx, sb, sc = _token_stride(x, "x"), _token_stride(B, "B"), _token_stride(C, "C")
+    sd, sz = _token_stride(dt, "dt"), _token_stride(z, "z")
+    if sb != sc:
+        raise ValueError("B and C must have the same token stride")
+    hp, gn = x.shape[2] * x.shape[3], B.shape[2] * B.shape[3]
+    dense = sx == hp and sb == gn and sd == x.shape[2] and (z is None or sz == hp)
+    return (sx, sb, sd, sz), dense
+
+
 def _f32(*ts):
     torch = _torch()
     for t in ts:
@@ -158,6 +200,9 @@ def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=N
             workspace=None, stream=None) -> Tuple[object, Optional[object]]:
     """Chunked SSD prefill.  Returns (y [B,L,H,P] fp32, final_state [B,H,P,N] fp32 or None).
 
+    x, dt, B and C may be views into wider token rows (e.g. slices of a layer's
+    projection output): they are then read in place through ssd_prefill_strided.
+
     ``final_state``: "new" allocates it, None skips it, or pass a tensor
     (which may be ``initial_state`` itself for an in-place update).
     """
@@ -168,7 +213,8 @@ def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=N
     for t in (dt, B, C):
         if t.dtype != x.dtype:
             raise TypeError("x, dt, B and C must share one dtype")
-    _dev(x, dt, A, B, C, D, initial_state, y, workspace)
+    strides, dense = _seq_strides(x, dt, B, C, None)  # views into wider token rows are read in place
+    _dev(A, D, initial_state, y, workspace)
     _f32(A, D, initial_state, y)
     if y is None:
         y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
@@ -179,6 +225,12 @@ def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=N
     if workspace is None:
         workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
     wbytes = workspace.numel() * workspace.element_size()
+    if not dense:
+        _check(lib().ssd_prefill_strided(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), None, 0, None,
+                                         _ptr(initial_state), _ptr(final_state), _ptr(y), code, SSD_F32, batch,
+                                         seqlen, nheads, headdim, dstate, ngroups, chunk, *strides, _ptr(workspace),
+                                         wbytes, _stream(stream)), "ssd_prefill_strided")
+        return y, final_state
     _check(lib().ssd_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
                              _ptr(final_state), _ptr(y), code, batch, seqlen, nheads, headdim, dstate, ngroups,
                              chunk, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill")
@@ -199,7 +251,8 @@ def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_s
             raise TypeError("x, dt, B, C and z must share one dtype")
     y_dtype = torch.float32 if y_dtype is None else y_dtype
     ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
-    _dev(x, dt, A, B, C, D, initial_state, y, workspace, dt_bias, z)
+    strides, dense = _seq_strides(x, dt, B, C, z)  # views into wider token rows are read in place
+    _dev(A, D, initial_state, y, workspace, dt_bias)
     _f32(A, D, initial_state, dt_bias)
     if y is None:
         y = torch.empty((batch, seqlen, nheads, headdim), dtype=y_dtype, device=x.device)
@@ -212,6 +265,12 @@ def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_s
     if workspace is None:
         workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
     wbytes = workspace.numel() * workspace.element_size()
+    if not dense:
+        _check(lib().ssd_prefill_strided(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+                                         int(bool(dt_softplus)), _ptr(z), _ptr(initial_state), _ptr(final_state),
+                                         _ptr(y), code, ycode, batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                         *strides, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill_strided")
+        return y, final_state
     _check(lib().ssd_prefill_ex(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
                                 int(bool(dt_softplus)), _ptr(z), _ptr(initial_state), _ptr(final_state), _ptr(y),
                                 code, ycode, batch, seqlen, nheads, headdim, dstate, ngroups, chunk,

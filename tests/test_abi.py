@@ -139,6 +139,39 @@ def test_option_entry_points_reject_before_launch():
     assert st(headdim=48) == UNS
 
 
+def test_strided_prefill_checks_token_strides_before_launch():
+    """ssd_prefill_strided: strides below the dense row, rows not a whole number of 16 bytes,
+    and chunks past 32-bit offsets are refused before anything is launched; accepted strides
+    reach the workspace check (no workspace here)."""
+    L = ssd.lib()
+    base = dict(x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, bias=None, sp=1, z=None, h0=None, hT=None, y=P0, dtype=BF,
+                ydtype=F, batch=1, seqlen=300, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64,
+                sx=0, sb=0, sd=0, sz=0, ws=None, wsb=1 << 30, stream=None)
+
+    def pf(**kw):
+        a = dict(base, **kw)
+        return L.ssd_prefill_strided(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["bias"], a["sp"], a["z"],
+                                     a["h0"], a["hT"], a["y"], a["dtype"], a["ydtype"], a["batch"], a["seqlen"],
+                                     a["nheads"], a["headdim"], a["dstate"], a["ngroups"], a["chunk"], a["sx"],
+                                     a["sb"], a["sd"], a["sz"], a["ws"], a["wsb"], a["stream"])
+    assert pf() == WS                                   # all dense (0)
+    assert pf(sx=256, sb=64, sd=4, sz=256) == WS        # the dense strides spelled out
+    assert pf(sx=256 + 2 * 64 + 8, sb=256 + 2 * 64 + 8, sd=13, sz=1000) == WS  # wider token rows
+    assert pf(sx=255) == INV                            # below H * P
+    assert pf(sb=56) == INV                             # below G * N
+    assert pf(sd=3) == INV                              # below H
+    assert pf(sz=200) == INV                            # below H * P
+    assert pf(sx=-256) == INV
+    assert pf(sx=260) == INV                            # 520 bytes: not a multiple of 16
+    assert pf(sb=68) == INV
+    assert pf(dtype=F, sx=260) == WS                    # fp32: 1040 bytes
+    assert pf(dtype=F, sx=258) == INV
+    assert pf(sx=1 << 24) == UNS                        # 64 tokens x 2 bytes x 2^24 = 2^31 bytes per chunk
+    assert pf(sd=1 << 24) == UNS
+    assert L.ssd_prefill_ex(P0, P0, P0, P0, P0, None, None, 1, None, None, None, P0, BF, F, 1, 300, 4, 64, 64, 1, 64,
+                            None, 1 << 30, None) == WS  # the dense call is the strided one with zeros
+
+
 def test_decode_graph_rejects_before_capture():
     """ssd_decode_graph_create validates everything before any HIP call and leaves *out NULL."""
     import ctypes
