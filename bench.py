@@ -16,6 +16,7 @@ the host's cores as "cpu_baseline".
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -200,27 +201,42 @@ def time_launches(torch, fn, n, flush=None, before=None):
     the events bracket [eviction + fn] and, on interleaved iterations,
     [eviction] alone; the difference of the means is fn's duration with the
     event overhead cancelled (the eviction itself is outside the result).
+
+    An interval also counts any time the GPU waits for the host to enqueue the next
+    command, so the host must stay ahead: evictions are put in flight before the first
+    timed launch (the GPU works through them while the loop enqueues), and Python's
+    garbage collector, whose pauses can drain the queue, is off during the loop.
+    (Without this a single stalled interval moved a 200-launch mean by over 100 us.)
     """
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     with_fn, alone = [], []
-    for _ in range(n):
-        if before is not None:
-            before()
-        a, b = ev(), ev()
-        a.record(stream)
+    gc_on = gc.isenabled()
+    gc.disable()
+    try:
         if flush is not None:
-            flush()
-        fn()
-        b.record(stream)
-        with_fn.append((a, b))
-        if flush is not None:
-            c, d = ev(), ev()
-            c.record(stream)
-            flush()
-            d.record(stream)
-            alone.append((c, d))
-    torch.cuda.synchronize()
+            for _ in range(8):
+                flush()
+        for _ in range(n):
+            if before is not None:
+                before()
+            a, b = ev(), ev()
+            a.record(stream)
+            if flush is not None:
+                flush()
+            fn()
+            b.record(stream)
+            with_fn.append((a, b))
+            if flush is not None:
+                c, d = ev(), ev()
+                c.record(stream)
+                flush()
+                d.record(stream)
+                alone.append((c, d))
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
     t = np.array([a.elapsed_time(b) * 1e3 for a, b in with_fn])
     if flush is None:
         return float(t.mean()), float(t.min())
@@ -386,6 +402,41 @@ def time_back_to_back(torch, fn, n):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / n
+
+
+def bench_layer_rows(torch, s, g, flush, steps):
+    """The prefill with its inputs where a Mamba-2 layer holds them: x, B and C in the
+    convolved [x | B | C] rows, dt in the input-projection [z | x | B | C | dt] rows.
+    Cold, like the step: read in place through token strides, against copying the four
+    inputs out to dense tensors first (what a dense-only call needs)."""
+    B, L, H, P, N, G = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups
+    hp, gn = H * P, G * N
+    xbc = torch.empty((B, L, hp + 2 * gn), dtype=g["x"].dtype, device="cuda")
+    zin = torch.empty((B, L, 2 * hp + 2 * gn + H), dtype=g["x"].dtype, device="cuda")
+    xbc[..., :hp] = g["x"].reshape(B, L, hp)
+    xbc[..., hp:hp + gn] = g["B"].reshape(B, L, gn)
+    xbc[..., hp + gn:] = g["C"].reshape(B, L, gn)
+    zin[..., 2 * hp + 2 * gn:] = g["dt"]
+    v = dict(x=xbc[..., :hp].unflatten(-1, (H, P)), B=xbc[..., hp:hp + gn].unflatten(-1, (G, N)),
+             C=xbc[..., hp + gn:].unflatten(-1, (G, N)), dt=zin[..., 2 * hp + 2 * gn:])
+    ws = g["ws"]
+
+    def in_place():
+        ssd.prefill(v["x"], v["dt"], g["A"], v["B"], v["C"], g["D"], g["h0"], chunk=s.chunk, y=g["y"],
+                    final_state=g["final"], workspace=ws)
+
+    def copied():
+        ssd.prefill(v["x"].contiguous(), v["dt"].contiguous(), g["A"], v["B"].contiguous(), v["C"].contiguous(),
+                    g["D"], g["h0"], chunk=s.chunk, y=g["y"], final_state=g["final"], workspace=ws)
+    for _ in range(3):
+        in_place()
+        copied()
+    torch.cuda.synchronize()
+    us_in, _ = time_launches(torch, in_place, steps, flush=flush)
+    us_cp, _ = time_launches(torch, copied, steps, flush=flush)
+    return {"in_place_us": us_in, "copy_then_dense_us": us_cp,
+            "rows": f"x|B|C rows of {hp + 2 * gn} and z|x|B|C|dt rows of {2 * hp + 2 * gn + H} elements",
+            "note": "cold, events on the launch stream; the copies are torch's, outside the library"}
 
 
 def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
@@ -570,6 +621,7 @@ def main():
         "step_launches": step_kernels(s),
         "timed_wall_s": wall,
     }
+    out["layer_rows"] = bench_layer_rows(torch, s, g, flush, args.steps)
     if not args.no_decode:
         out["decode"] = bench_decode(torch, args.decode_steps, flush)
         out["cached_vs_recompute"] = bench_cached_vs_recompute(torch)
