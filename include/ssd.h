@@ -183,6 +183,24 @@ int ssd_step_ex(float *state, const void *x, const void *dt, const float *A,
                 int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
                 ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
                 int ngroups, void *hip_stream);
+/*
+ * ssd_step_ex with a decode token's inputs read in place from wider rows, as
+ * ssd_prefill_strided does for a sequence: x, B and C from the convolution step's
+ * [x | B | C] row of each batch entry, dt and z from its input-projection row.  The
+ * strides are the elements between consecutive batch entries (0: dense):
+ *   x_stride >= H * P, bc_stride >= G * N (B and C share it), dt_stride >= H,
+ *   z_stride >= H * P.
+ * The step reads its inputs element by element: pointers need only their element's
+ * alignment.  y is dense [B, H, P].  Errors: SSD_ERR_INVALID_ARG for a stride below
+ * its dense row; SSD_ERR_UNSUPPORTED for a stride of 2^31 elements or more.
+ * ssd_step_ex is this call with all four strides 0.
+ */
+int ssd_step_strided(float *state, const void *x, const void *dt, const float *A,
+                     const void *Bm, const void *Cm, const float *D, const float *dt_bias,
+                     int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
+                     ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
+                     int ngroups, long long x_stride, long long bc_stride,
+                     long long dt_stride, long long z_stride, void *hip_stream);
 
 /*
  * A decode loop of `nsteps` tokens captured once as a HIP graph and replayed

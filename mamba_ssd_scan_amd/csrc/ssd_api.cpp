@@ -139,7 +139,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (3 << 16) | 2; }
+int ssd_version(void) { return (3 << 16) | 3; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -335,15 +335,32 @@ int ssd_prefill(const void *x, const void *dt, const float *A, const void *Bm, c
                           hip_stream);
 }
 
+int ssd_step_strided(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
+                     const float *D, const float *dt_bias, int dt_softplus, const void *z, void *y,
+                     ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
+                     int ngroups, long long x_stride, long long bc_stride, long long dt_stride, long long z_stride,
+                     void *hip_stream)
+{
+    SSD_TRY(check_step_args(state, x, dt, A, Bm, Cm, D, dt_bias, z, y, in_dtype, y_dtype, batch, nheads, headdim,
+                            dstate, ngroups));
+    // batch strides: 0 = dense; each at least its dense row (element loads: no other alignment)
+    const long long hp = (long long)nheads * headdim, gn = (long long)ngroups * dstate;
+    const long long sx = x_stride ? x_stride : hp, sbc = bc_stride ? bc_stride : gn,
+                    sdt = dt_stride ? dt_stride : nheads, sz = z_stride ? z_stride : hp;
+    if (sx < hp || sbc < gn || sdt < nheads || sz < hp) return SSD_ERR_INVALID_ARG;
+    if (std::max(std::max(sx, sbc), std::max(sdt, sz)) > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+    ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
+    d.sx = (int)sx; d.sbc = (int)sbc; d.sdt = (int)sdt; d.sz = (int)sz;
+    const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    return hip_status(ssd::launch_step(state, x, dt, A, Bm, Cm, D, y, o, d, (hipStream_t)hip_stream));
+}
+
 int ssd_step_ex(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
                 const float *D, const float *dt_bias, int dt_softplus, const void *z, void *y, ssd_dtype_t in_dtype,
                 ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate, int ngroups, void *hip_stream)
 {
-    SSD_TRY(check_step_args(state, x, dt, A, Bm, Cm, D, dt_bias, z, y, in_dtype, y_dtype, batch, nheads, headdim,
-                            dstate, ngroups));
-    const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
-    const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
-    return hip_status(ssd::launch_step(state, x, dt, A, Bm, Cm, D, y, o, d, (hipStream_t)hip_stream));
+    return ssd_step_strided(state, x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, y, in_dtype, y_dtype, batch, nheads,
+                            headdim, dstate, ngroups, 0, 0, 0, 0, hip_stream);
 }
 
 int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,

@@ -26,8 +26,11 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
                                                    const TIn *__restrict__ dt, const float *__restrict__ A,
                                                    const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
                                                    const float *__restrict__ D, void *__restrict__ y,
-                                                   SsdOpts opt, int H, int G, int P)
+                                                   SsdOpts opt, int H, int G, int P, int sx, int sbc, int sdt,
+                                                   int sz)
 {
+    // inputs: batch entry b of x, B/C, dt and z starts sx, sbc, sdt and sz elements after
+    // entry b - 1 (dense: H P, G N, H, H P); y is dense
     constexpr int NQ = N / 4;          // lanes per state row (8, 16 or 32)
     constexpr int RP = 256 / NQ;       // rows per pass of the workgroup
     constexpr int MAXIT = 128 / RP > 0 ? 128 / RP : 1;  // P <= 128
@@ -37,14 +40,14 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
     const int q = threadIdx.x % NQ;
     const int r0 = threadIdx.x / NQ;
 
-    const float dtv = dt_effective(load_in(dt + bh), opt, h);
+    const float dtv = dt_effective(load_in(dt + (size_t)b * sdt + h), opt, h);
     const float r = exp_fast(dtv * A[h]);
     const float Dh = D ? D[h] : 0.f;
     float bv[4], cv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        bv[k] = load_in(Bm + ((size_t)b * G + g) * N + 4 * q + k);
-        cv[k] = load_in(Cm + ((size_t)b * G + g) * N + 4 * q + k);
+        bv[k] = load_in(Bm + (size_t)b * sbc + (size_t)g * N + 4 * q + k);
+        cv[k] = load_in(Cm + (size_t)b * sbc + (size_t)g * N + 4 * q + k);
     }
     float4 *st = reinterpret_cast<float4 *>(state) + (size_t)bh * P * NQ;
 
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
         const int p = r0 + k * RP;
         if (p < P) {
             s[k] = st[p * NQ + q];
-            xs[k] = load_in(x + (size_t)bh * P + p);
+            xs[k] = load_in(x + (size_t)b * sx + (size_t)h * P + p);
         }
     }
 #pragma unroll
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
             for (int off = NQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
             if (q == 0) {
                 float out = part + Dh * xs[k];
-                if (opt.z) out *= silu(load_in(static_cast<const TIn *>(opt.z) + (size_t)bh * P + p));
+                if (opt.z) out *= silu(load_in(static_cast<const TIn *>(opt.z) + (size_t)b * sz + (size_t)h * P + p));
                 if (opt.y_bf16)
                     static_cast<uint16_t *>(y)[(size_t)bh * P + p] = f32_to_bf16_rne(out);
                 else
@@ -93,9 +96,9 @@ static hipError_t launch_step_t(float *state, const void *x, const void *dt, con
     const TIn *xx = static_cast<const TIn *>(x), *dd = static_cast<const TIn *>(dt);
     const TIn *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
     switch (d.N) {
-    case 32: step_kernel<TIn, 32><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
-    case 64: step_kernel<TIn, 64><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
-    case 128: step_kernel<TIn, 128><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P); break;
+    case 32: step_kernel<TIn, 32><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P, d.sx, d.sbc, d.sdt, d.sz); break;
+    case 64: step_kernel<TIn, 64><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P, d.sx, d.sbc, d.sdt, d.sz); break;
+    case 128: step_kernel<TIn, 128><<<grid, 256, 0, s>>>(state, xx, dd, A, bb, cc, D, y, o, d.H, d.G, d.P, d.sx, d.sbc, d.sdt, d.sz); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -19,7 +19,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_step_ex",
+           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_step_ex", "ssd_step_strided",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
            "ssd_chunk_gemm1", "ssd_chunk_scan", "ssd_chunk_scan_passing")
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_prefill_strided.restype = i
     L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
     L.ssd_step_ex.restype = i
+    L.ssd_step_strided.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [ctypes.c_longlong] * 4 + [vp]
+    L.ssd_step_strided.restype = i
     L.ssd_decode_graph_create.argtypes = [ctypes.POINTER(vp), i] + [vp] * 8 + [i] + [vp] * 2 + [i] * 7
     L.ssd_decode_graph_create.restype = i
     L.ssd_decode_graph_launch.argtypes = [vp, vp]
@@ -163,6 +165,33 @@ def _seq_strides(x, dt, B, C, z):
         raise ValueError("B and C must have the same token stride")
     hp, gn = x.shape[2] * x.shape[3], B.shape[2] * B.shape[3]
     dense = sx == hp and sb == gn and sd == x.shape[2] and (z is None or sz == hp)
+    return (sx, sb, sd, sz), dense
+
+
+def _batch_stride(t, name: str) -> int:
+    """Elements between consecutive batch entries of a [B, ...] decode input whose per-entry
+    values are contiguous (a view into wider rows is fine)."""
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    shape, st = t.shape, t.stride()
+    tail = 1
+    for k in range(t.dim() - 1, 0, -1):
+        if shape[k] != 1 and st[k] != tail:
+            raise ValueError(f"{name}: the values of one batch entry must be contiguous (strides {st})")
+        tail *= shape[k]
+    return st[0] if shape[0] > 1 and t.numel() > 0 else tail
+
+
+def _step_strides(x, dt, B, C, z):
+    """Batch strides (x, B and C, dt, z) and whether all are dense."""
+    sx, sb, sc = _batch_stride(x, "x"), _batch_stride(B, "B"), _batch_stride(C, "C")
+    sd, sz = _batch_stride(dt, "dt"), _batch_stride(z, "z")
+    if sb != sc:
+        raise ValueError("B and C must have the same batch stride")
+    hp, gn = x.shape[1] * x.shape[2], B.shape[1] * B.shape[2]
+    dense = sx == hp and sb == gn and sd == x.shape[1] and (z is None or sz == hp)
     return (sx, sb, sd, sz), dense
 
 
@@ -287,10 +316,16 @@ def step_ex(state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z
     code = _dtype_code(x)
     y_dtype = torch.float32 if y_dtype is None else y_dtype
     ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
-    _dev(state, x, dt, A, B, C, D, y, dt_bias, z)
+    strides, dense = _step_strides(x, dt, B, C, z)  # views into wider rows are read in place
+    _dev(state, A, D, y, dt_bias)
     _f32(state, A, D, dt_bias)
     if y is None:
         y = torch.empty((batch, nheads, headdim), dtype=y_dtype, device=x.device)
+    if not dense:
+        _check(lib().ssd_step_strided(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(dt_bias), int(bool(dt_softplus)), _ptr(z), _ptr(y), code, ycode, batch,
+                                      nheads, headdim, dstate, ngroups, *strides, _stream(stream)), "ssd_step_strided")
+        return y
     _check(lib().ssd_step_ex(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
                              int(bool(dt_softplus)), _ptr(z), _ptr(y), code, ycode, batch, nheads, headdim, dstate,
                              ngroups, _stream(stream)), "ssd_step_ex")
@@ -298,15 +333,24 @@ def step_ex(state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z
 
 
 def step(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
-    """One fused decode token; ``state`` [B,H,P,N] fp32 is updated in place.  Returns y [B,H,P] fp32."""
+    """One fused decode token; ``state`` [B,H,P,N] fp32 is updated in place.  Returns y [B,H,P] fp32.
+
+    x, dt, B and C may be views into wider per-entry rows (a layer's projection outputs):
+    they are then read in place through ssd_step_strided."""
     torch = _torch()
     batch, nheads, headdim, dstate = state.shape
     ngroups = B.shape[1]
     code = _dtype_code(x)
-    _dev(state, x, dt, A, B, C, D, y)
+    strides, dense = _step_strides(x, dt, B, C, None)  # views into wider rows are read in place
+    _dev(state, A, D, y)
     _f32(state, A, D, y)
     if y is None:
         y = torch.empty((batch, nheads, headdim), dtype=torch.float32, device=x.device)
+    if not dense:
+        _check(lib().ssd_step_strided(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), None, 0,
+                                      None, _ptr(y), code, SSD_F32, batch, nheads, headdim, dstate, ngroups, *strides,
+                                      _stream(stream)), "ssd_step_strided")
+        return y
     _check(lib().ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), code,
                           batch, nheads, headdim, dstate, ngroups, _stream(stream)), "ssd_step")
     return y

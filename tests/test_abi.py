@@ -172,6 +172,26 @@ def test_strided_prefill_checks_token_strides_before_launch():
                             None, 1 << 30, None) == WS  # the dense call is the strided one with zeros
 
 
+def test_strided_step_checks_batch_strides_before_launch():
+    L = ssd.lib()
+
+    def st(**kw):
+        a = dict(state=P0, x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, bias=None, sp=0, z=None, y=P0, dtype=BF, ydtype=F,
+                 batch=2, nheads=4, headdim=64, dstate=64, ngroups=1, sx=0, sb=0, sd=0, sz=0, stream=None)
+        a.update(kw)
+        return L.ssd_step_strided(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["bias"], a["sp"],
+                                  a["z"], a["y"], a["dtype"], a["ydtype"], a["batch"], a["nheads"], a["headdim"],
+                                  a["dstate"], a["ngroups"], a["sx"], a["sb"], a["sd"], a["sz"], a["stream"])
+    assert st(sx=255) == INV        # below H * P
+    assert st(sb=63) == INV         # below G * N
+    assert st(sd=3) == INV          # below H
+    assert st(sz=255) == INV        # below H * P
+    assert st(sx=-1) == INV
+    assert st(sx=1 << 31) == UNS    # past 32-bit element offsets
+    assert st(x=None, sx=300) == INV
+    assert st(headdim=48, sx=300) == UNS
+
+
 def test_decode_graph_rejects_before_capture():
     """ssd_decode_graph_create validates everything before any HIP call and leaves *out NULL."""
     import ctypes

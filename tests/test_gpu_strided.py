@@ -115,3 +115,39 @@ def test_views_the_kernels_cannot_read_are_refused():
     odd = torch.zeros((2, 300, 256 + 4), dtype=torch.bfloat16, device="cuda")[..., :256].unflatten(-1, (4, 64))
     with pytest.raises(ssd.SsdError, match="INVALID"):
         ssd.prefill(odd, g["dt"], g["A"], g["B"], g["C"], chunk=64)
+
+
+@pytest.mark.parametrize("dtype,B,H,P,N,G,opts", [("bf16", 64, 80, 64, 128, 1, True), ("bf16", 3, 8, 64, 64, 2, False),
+                                                  ("f32", 5, 4, 32, 128, 2, True), ("bf16", 1, 24, 64, 128, 1, True)])
+def test_strided_decode_inputs_equal_dense_inputs(dtype, B, H, P, N, G, opts):
+    """A decode token read in place from the rows of each batch entry (ssd_step_strided)
+    equals the step on dense copies bit for bit, state and y."""
+    torch = gh.torch()
+    rng = np.random.Generator(np.random.PCG64(1400 + B + H))
+    inp = synth.random_prefill(rng, B, 1, H, P, N, G, dtype, init_state=True)
+    g = gh.upload(inp)
+    kw, z = {}, None
+    if opts:
+        opt = synth.option_inputs(rng, inp)
+        z = synth.to_torch(opt["z"], dtype)
+        g["dt"] = synth.to_torch(opt["dt_raw"], dtype)
+        kw = dict(dt_bias=torch.from_numpy(opt["dt_bias"]).cuda(), dt_softplus=True, z=z[:, 0])
+    print(f"[strided decode] {dtype} B={B} H={H} P={P} N={N} G={G} opts={opts}", flush=True)
+    s0 = g["h0"].clone()
+    y = ssd.step_ex(s0, g["x"][:, 0].contiguous(), g["dt"][:, 0].contiguous(), g["A"], g["B"][:, 0].contiguous(),
+                    g["C"][:, 0].contiguous(), g["D"], **kw)
+    v, keep = _layer_rows(g, z, pad_xbc=8)
+    assert not v["x"][:, 0].is_contiguous() or B == 1
+    kws = dict(kw)
+    if opts:
+        kws["z"] = v["z"][:, 0]
+    s1 = g["h0"].clone()
+    ys = ssd.step_ex(s1, v["x"][:, 0], v["dt"][:, 0], g["A"], v["B"][:, 0], v["C"][:, 0], g["D"], **kws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ys).all(), "a read outside the inputs' own channels reached y"
+    assert torch.equal(y, ys) and torch.equal(s0, s1)
+    if not opts:
+        s2 = g["h0"].clone()
+        yp = ssd.step(s2, v["x"][:, 0], v["dt"][:, 0], g["A"], v["B"][:, 0], v["C"][:, 0], g["D"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, yp) and torch.equal(s0, s2)
