@@ -31,11 +31,18 @@
  *   validated before any HIP call, so a rejected call launches nothing.
  *   SSD_ERR_HIP means a launch failed; faults inside a kernel surface at the
  *   caller's next synchronisation.
- * - `in_dtype` selects the storage type of x, dt, B, C (and nothing else):
- *   SSD_BF16 (uint16 bit patterns of bfloat16) or SSD_F32.  A and D are
- *   always fp32; state, workspace and y are always fp32.
- * - Non-finite values are propagated, not trapped.  With SSD_BF16 inputs the
- *   matrix-core operands are fp16: |x|, |B|, |C| must stay below 65504.
+ * - `in_dtype` selects the storage type of x, dt, B, C (and z): SSD_BF16 (uint16 bit
+ *   patterns of bfloat16) or SSD_F32.  A and D are always fp32; the initial and final
+ *   states and y are fp32 (y may be bf16 through the _ex calls).  Accumulation is fp32.
+ * - Precision inside a prefill (bf16 inputs): the matrix-core operands are fp16 (the inputs
+ *   convert exactly; computed operands -- the masked scores, the weighted B or X, the
+ *   entering state of the off-diagonal product -- are rounded once).  Between kernels the
+ *   staged and one-round paths keep the chunk and entering states in fp16; the single-pass
+ *   path keeps them in fp32.  Range contract for bf16 inputs: |x|, |B|, |C|, every |C_i.B_j|
+ *   and, on the staged and one-round paths, every state (initial, entering and chunk states)
+ *   must stay below 65504, the fp16 limit; past it the values turn to inf in y (no error is
+ *   raised).  fp32 inputs keep every product and state in fp32.
+ * - Non-finite values are propagated, not trapped.
  *
  * Supported shapes: batch >= 1; seqlen >= 0; nheads % ngroups == 0;
  * headdim (P) in {32, 64, 128}; dstate (N) in {32, 64, 128};
@@ -58,7 +65,8 @@ enum {
     SSD_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer, H % G != 0 */
     SSD_ERR_UNSUPPORTED = -2, /* valid but unsupported P, N, Q or dtype */
     SSD_ERR_WORKSPACE = -3,   /* workspace missing, too small or not 256-byte aligned */
-    SSD_ERR_HIP = -4          /* a HIP launch failed */
+    SSD_ERR_HIP = -4,         /* a HIP launch failed */
+    SSD_ERR_SYNC = -5         /* ssd_prefill_check: a bounded wait of the last prefill gave up */
 };
 
 /* Static description of a status code (never NULL). */
@@ -69,31 +77,44 @@ int ssd_version(void);
 
 /*
  * Bytes of caller-provided workspace that ssd_prefill needs, or 0 for
- * invalid/unsupported shapes.  Layout (each region 256-byte aligned):
+ * invalid/unsupported shapes.  The first 256 bytes are a control block (word 1: the
+ * give-up word that ssd_prefill_check reads); the rest is carved by whichever path the
+ * prefill takes (below), and the size covers every path.  Staged and one-round paths,
+ * each region 256-byte aligned:
  *   dA_cum  [B, H, nc, Q] fp32   per-chunk inclusive cumsum of dt*A
  *   dt_c    [B, H, nc, Q] fp32   dt regrouped per chunk (0 past seqlen)
  *   states  [B, H, nc, P, N] x 4 bytes: the chunk states, then the entering
  *           states (fp16 for bf16 inputs -- half the region -- fp32 for fp32 inputs)
  *   cb      ssd_chunk_gemm1_size(B, L, G, Q) bytes: the C.B^T products
- *   sync    [B, H] uint32 counters, one per 256 bytes, of the two-launch path below
- * with nc = ceil(seqlen / Q).
+ *   sync    [B, H] uint32 counters, one per 256 bytes, of the one-round path
+ * Single-pass path: per (b, h) status words and 8 ring slots of P*N fp32 states, and the
+ * C.B^T products.  nc = ceil(seqlen / Q).
  */
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int dstate, int ngroups, int chunk);
 
 /*
- * Chunked prefill over a whole sequence (Step-1 intra-chunk output, chunk
- * states, Step-3 inter-chunk state passing, off-diagonal output; see the
- * stage entry points below, which it runs in order on `hip_stream`).
- * When every (b, h, chunk) item fits the device at once (bf16 inputs, Q = 256,
- * P = 64, nc <= 16, B*H*nc <= 2 x compute units) it runs two launches instead: the chunk
- * scan walks Step-3 itself, each workgroup for its share of its head's state,
- * and waits for the head's other workgroups.  That wait relies on all of them
- * being resident together: a kernel on another stream that holds compute units
- * indefinitely while this one starts could delay it (the wait is bounded; past
- * the bound the result is not valid).  Results equal the staged path's bit for bit;
- * SSD_PREFILL_STAGED=1 in the environment (read on every call) forces the staged
- * path with one head per chunk-state workgroup, for comparisons.
+ * Chunked prefill over a whole sequence ("Mamba-Family State-Space Model Kernels on a
+ * Programmable CGLA", Sec. III-A: chunks of Q tokens, Step-1 intra-chunk GEMM1 / mask /
+ * GEMM2, Step-3 inter-chunk recurrence of the state with a diagonal A_c, Sec. IV-C;
+ * "Compiler-First State Space Duality and Portable O(1) Autoregressive Caching for
+ * Inference", abstract: fixed-size chunking, the final state as the decode cache).
+ * Paths, all computing the same result up to rounding:
+ *  - one-round (two launches), taken when every (b, h, chunk) item is resident at once
+ *    (bf16, Q = 256, P = 64, nc <= 16, items <= 2 x compute units, and the compiled
+ *    kernel's occupancy confirmed on the device): chunk states, then a chunk scan that
+ *    walks Step-3 itself, its workgroups of a head waiting for each other;
+ *  - staged (three launches), taken otherwise: the stage entry points below in order;
+ *  - single pass (a GEMM1 launch, then one launch; bf16, Q = 256, P = 64, N in {64, 128}),
+ *    only through ssd_prefill_forced: each item forms its chunk state, takes the state
+ *    entering its chunk from the items of earlier chunks (they hold smaller tickets, so no
+ *    co-residency is assumed) and writes its output.  It keeps the states in fp32 and moves
+ *    about half the HBM bytes of the staged path, but on MI355X its device-coherent
+ *    hand-offs make it slower, so the library does not pick it.
+ * The waits between workgroups are bounded.  A wait that gives up (which needs a device
+ * that stops running some of the launch's workgroups for about a second) sets the give-up
+ * word; the kernels still finish, but y and final_state are then not valid:
+ * ssd_prefill_check reports it.
  *
  *   x   [B, L, H, P] in_dtype       dt [B, L, H] in_dtype (used as given:
  *   A   [H] fp32                          positive step sizes, no softplus)
@@ -163,7 +184,49 @@ int ssd_prefill_strided(const void *x, const void *dt, const float *A, const voi
                         long long z_stride, void *workspace, size_t workspace_bytes,
                         void *hip_stream);
 /*
- * One decode token for every (b, h), fused: the state is read once,
+ * Test and diagnostic entry point: ssd_prefill_strided on a path of the caller's choice,
+ * with the bound of the waits between workgroups set by the caller.
+ *   path        SSD_PATH_AUTO (the library's choice, as ssd_prefill_strided),
+ *               SSD_PATH_STAGED (three launches), SSD_PATH_ONE_ROUND, SSD_PATH_SINGLE_PASS,
+ *               or SSD_PATH_STAGED_ONE_HEAD (three launches with one head per chunk-state
+ *               workgroup: the same result as SSD_PATH_STAGED and SSD_PATH_ONE_ROUND bit for
+ *               bit, from other kernels); a path whose conditions (see ssd_prefill) do not
+ *               hold returns SSD_ERR_UNSUPPORTED.
+ *   spin_limit  < 0: the default bound; >= 0: polls per wait before it gives up (0: every
+ *               wait gives up at once -- the output is then not valid and
+ *               ssd_prefill_check returns SSD_ERR_SYNC; for tests of that report).
+ */
+enum {
+    SSD_PATH_AUTO = 0,
+    SSD_PATH_STAGED = 1,
+    SSD_PATH_ONE_ROUND = 2,
+    SSD_PATH_SINGLE_PASS = 3,
+    SSD_PATH_STAGED_ONE_HEAD = 4
+};
+int ssd_prefill_forced(const void *x, const void *dt, const float *A, const void *Bm,
+                       const void *Cm, const float *D, const float *dt_bias, int dt_softplus,
+                       const void *z, const float *initial_state, float *final_state, void *y,
+                       ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                       int nheads, int headdim, int dstate, int ngroups, int chunk,
+                       long long x_stride, long long bc_stride, long long dt_stride,
+                       long long z_stride, void *workspace, size_t workspace_bytes,
+                       void *hip_stream, int path, long long spin_limit);
+/*
+ * Whether the last prefill that used `workspace` completed its waits between workgroups
+ * (a prefill with seqlen == 0 does not touch the workspace and is not that prefill).
+ * Synchronises `hip_stream` (so call it after the prefill was enqueued there), then reads
+ * the workspace's give-up word: SSD_OK, or SSD_ERR_SYNC when a bounded wait gave up and
+ * that prefill's y and final_state are not valid.  SSD_ERR_WORKSPACE for a NULL,
+ * misaligned or too small (< 256 bytes) workspace; SSD_ERR_HIP if the synchronisation or
+ * the read failed (e.g. a kernel fault).
+ */
+int ssd_prefill_check(const void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One decode token for every (b, h), fused ("Compiler-First State Space Duality and
+ * Portable O(1) Autoregressive Caching for Inference", abstract: cached O(1) decode carries
+ * the recurrent state from token to token; "Mamba-Family State-Space Model Kernels on a
+ * Programmable CGLA", Sec. III-A: the per-token recurrence with a diagonal decay): the state is read once,
  * decayed, updated with the token's input and written back in place, and
  * the output is read off the updated state.
  *
@@ -320,9 +383,10 @@ int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *
  *   initial_state / final_state: as in ssd_state_passing (NULL allowed)
  *   sync   B*H*64 uint32 (256 bytes per (b, h)), ZERO on entry; each (b, h)
  *          counter holds nc on exit.  The launch's workgroups of one (b, h) wait
- *          for each other through it, which needs them resident together: a
- *          kernel on another stream that holds compute units indefinitely could
- *          delay the wait (it is bounded; past the bound y is not valid).
+ *          for each other through it, which needs them resident together (the call
+ *          checks the kernel's occupancy on the device: SSD_ERR_UNSUPPORTED if it cannot
+ *          hold the grid).  The wait is bounded: a workgroup that gives up sets bit 31 of
+ *          its head's counter, and y and the states of that head are then not valid.
  *   Other arguments as ssd_chunk_scan; y [B, L, H, P] fp32 (written).
  */
 int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const float *dA_cum,

@@ -16,13 +16,6 @@
 
 namespace {
 
-// SSD_PREFILL_STAGED=1 in the environment: always the three-launch path (for comparisons)
-bool staged_forced()
-{
-    const char *e = getenv("SSD_PREFILL_STAGED");
-    return e && e[0] == '1';
-}
-
 
 constexpr size_t kWsAlign = 256;
 
@@ -42,6 +35,8 @@ int check_shape(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     if (!supported_dim(headdim) || !supported_dim(dstate)) return SSD_ERR_UNSUPPORTED;
     if (need_chunk && !supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
     if (batch > 65535 || nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y/z limits
+    // chunk counts and token offsets are formed in 32-bit ints
+    if (need_chunk && (long long)seqlen + chunk > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     if (need_chunk && (long long)nheads + 4LL * ngroups > 65535) return SSD_ERR_UNSUPPORTED;  // chunk-state grid y
     if ((long long)batch * nheads > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     // One chunk of x or B/C is addressed with 32-bit byte offsets inside the kernels.
@@ -57,7 +52,7 @@ int check_dtype(ssd_dtype_t t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK
 size_t in_size(ssd_dtype_t t) { return t == SSD_BF16 ? 2 : 4; }
 
 struct WsLayout {
-    size_t acum, dtc, states, cb, sync, total;  // byte offsets of each region, then total bytes
+    size_t ctl, acum, dtc, states, cb, sync, total;  // byte offsets of each region, then total bytes
 };
 
 // fp32 elements of the GEMM1 output: 512 per 32-column step of every chunk of every group
@@ -66,17 +61,27 @@ size_t gemm1_elems(int batch, int ngroups, int nchunks, int chunk)
     return (size_t)batch * ngroups * nchunks * ssd::gemm1_steps_per_chunk(chunk) * 512;
 }
 
+ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk,
+                    ssd_dtype_t t);
+
+// The workspace of every prefill path.  The first 256 bytes are the control block that all
+// paths share (word 1: the give-up word that ssd_prefill_check reads); the staged and
+// one-round paths carve their regions after it, the single-pass path carves its own layout
+// from offset 0 (its control block is the same 256 bytes), and the size covers both.
 WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk)
 {
-    const size_t nc = (size_t)(seqlen + chunk - 1) / chunk;
+    const size_t nc = ((size_t)seqlen + chunk - 1) / chunk;
     const size_t bhq = (size_t)batch * nheads * nc * chunk;
     WsLayout w;
-    w.acum = 0;
+    w.ctl = 0;
+    w.acum = kWsAlign;
     w.dtc = align_up(w.acum + 4 * bhq, kWsAlign);
     w.states = align_up(w.dtc + 4 * bhq, kWsAlign);
     w.cb = align_up(w.states + 4 * (size_t)batch * nheads * nc * headdim * dstate, kWsAlign);
     w.sync = align_up(w.cb + 4 * gemm1_elems(batch, ngroups, (int)nc, chunk), kWsAlign);
     w.total = align_up(w.sync + 4 * (size_t)batch * nheads * ssd::kSyncStride, kWsAlign);  // a counter per (b, h)
+    const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, SSD_BF16);
+    if (ssd::fused_prefill_shape(d)) w.total = std::max(w.total, ssd::fused_prefill_ws_bytes(d));
     return w;
 }
 
@@ -85,7 +90,7 @@ ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, 
 {
     ssd::Dims d;
     d.B = batch; d.L = seqlen; d.H = nheads; d.P = headdim; d.N = dstate; d.G = ngroups; d.Q = chunk;
-    d.nc = chunk > 0 ? (seqlen + chunk - 1) / chunk : 0;
+    d.nc = chunk > 0 ? (int)(((long long)seqlen + chunk - 1) / chunk) : 0;
     d.bf16 = (t == SSD_BF16);
     d.sx = nheads * headdim; d.sbc = ngroups * dstate; d.sdt = nheads; d.sz = nheads * headdim;
     return d;
@@ -132,14 +137,15 @@ const char *ssd_status_string(int status)
     switch (status) {
     case SSD_OK: return "SSD_OK: success";
     case SSD_ERR_INVALID_ARG: return "SSD_ERR_INVALID_ARG: null/misaligned pointer, bad size or dtype, or nheads % ngroups != 0";
-    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: headdim/dstate must be 32, 64 or 128; chunk 16..256 (power of two); batch, nheads <= 65535";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: unsupported headdim/dstate/chunk, size limits, or a forced path that does not apply";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, smaller than ssd_prefill_workspace_size() or not 256-byte aligned";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP kernel launch failed";
+    case SSD_ERR_SYNC: return "SSD_ERR_SYNC: a bounded wait between workgroups of the last prefill gave up; its output is not valid";
     default: return "unknown ssd status";
     }
 }
 
-int ssd_version(void) { return (3 << 16) | 3; }
+int ssd_version(void) { return (4 << 16) | 0; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -181,6 +187,7 @@ int ssd_state_passing(void *states, const float *dA_cum, const float *initial_st
 {
     SSD_TRY(check_dtype(in_dtype));
     if (nchunks < 0) return SSD_ERR_INVALID_ARG;
+    if ((long long)nchunks * chunk > 0x7fffffffLL - 256) return SSD_ERR_UNSUPPORTED;  // nchunks * chunk is an int below
     SSD_TRY(check_shape(batch, nchunks, nheads, headdim, dstate, 1, chunk, true));
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, nchunks * chunk, nheads, headdim, dstate, 1, chunk, in_dtype);
@@ -250,19 +257,28 @@ int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const
     if (!ssd::chunk_scan_small_pass_fits(d, ncu)) return SSD_ERR_UNSUPPORTED;
     ssd::SsdOpts o = {nullptr, 0, nullptr, 0};
     o.sync = sync;
+    bool resident = false;
+    SSD_TRY(hip_status(ssd::chunk_scan_small_resident(d, o, ncu, &resident)));
+    if (!resident) return SSD_ERR_UNSUPPORTED;
     return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, dA_cum, dt_c, states, initial_state, final_state, D, y,
                                                    o, d, ncu, (hipStream_t)hip_stream));
 }
 
-int ssd_prefill_strided(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
-                        const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
-                        float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch,
-                        int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, long long x_stride,
-                        long long bc_stride, long long dt_stride, long long z_stride, void *workspace,
-                        size_t workspace_bytes, void *hip_stream)
+}  // extern "C"
+
+namespace {
+
+// The prefill with an explicit path (0: the library's choice) and wait bound (< 0: default).
+int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                 const float *dt_bias, int dt_softplus, const void *z, const float *initial_state, float *final_state,
+                 void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen, int nheads, int headdim,
+                 int dstate, int ngroups, int chunk, long long x_stride, long long bc_stride, long long dt_stride,
+                 long long z_stride, void *workspace, size_t workspace_bytes, void *hip_stream, int path,
+                 long long spin_limit)
 {
     SSD_TRY(check_dtype(in_dtype));
     SSD_TRY(check_dtype(y_dtype));
+    if (path < SSD_PATH_AUTO || path > SSD_PATH_STAGED_ONE_HEAD) return SSD_ERR_INVALID_ARG;
     if (!aligned(dt_bias, 4) || !aligned(z, in_size(in_dtype))) return SSD_ERR_INVALID_ARG;
     SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
     // token strides: 0 = dense; x, B and C rows are read with 16-byte loads
@@ -297,21 +313,80 @@ int ssd_prefill_strided(const void *x, const void *dt, const float *A, const voi
     d.sx = (int)sx; d.sbc = (int)sbc; d.sdt = (int)sdt; d.sz = (int)sz;
 
     ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
+    o.ctl = reinterpret_cast<unsigned *>(ws + w.ctl);
+    o.spin = spin_limit < 0 ? 0u : (unsigned)std::min(spin_limit, 0x7fffffffLL) + 1u;
     int ncu = 0;
     SSD_TRY(hip_status(ssd::device_cu_count(&ncu)));
-    if (ssd::chunk_scan_small_pass_fits(d, ncu) && !staged_forced()) {
+    // The one-round path needs every workgroup of the chunk scan resident at once (its
+    // workgroups of a head wait for each other): the grid must fit and the compiled kernel's
+    // occupancy must allow it.
+    bool one_round = false;
+    if (ssd::chunk_scan_small_pass_fits(d, ncu)) {
+        ssd::SsdOpts po = o;
+        po.sync = reinterpret_cast<unsigned *>(ws + w.sync);
+        SSD_TRY(hip_status(ssd::chunk_scan_small_resident(d, po, ncu, &one_round)));
+    }
+    const bool single_pass = ssd::fused_prefill_shape(d);
+    // The single pass is taken only when asked for: measured on MI355X it is slower than the
+    // three launches on every many-round shape tried (0.58-0.99x), its items being bound by
+    // the latency of their device-coherent exchange rather than by HBM.
+    if (path == SSD_PATH_AUTO) path = one_round ? SSD_PATH_ONE_ROUND : SSD_PATH_STAGED;
+    if ((path == SSD_PATH_ONE_ROUND && !one_round) || (path == SSD_PATH_SINGLE_PASS && !single_pass))
+        return SSD_ERR_UNSUPPORTED;
+
+    if (path == SSD_PATH_ONE_ROUND) {
         // every (b, h, chunk) item is resident at once: Step-3 runs inside the chunk scan
         o.sync = reinterpret_cast<unsigned *>(ws + w.sync);
         SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s)));
         return hip_status(ssd::launch_chunk_scan_small(x, Cm, cb, acum, dtc, states, initial_state, final_state, D, y,
                                                        o, d, ncu, s));
     }
-    // (forced staging also keeps the one-head-per-workgroup chunk-state kernel: the
-    // comparison then covers every fast-path kernel)
+    if (path == SSD_PATH_SINGLE_PASS)
+        return hip_status(ssd::launch_prefill_fused(x, Bm, Cm, dt, A, D, initial_state, final_state, y, workspace, o,
+                                                    d, s));
+    // Three launches (SSD_PATH_STAGED_ONE_HEAD: one head per chunk-state workgroup, so that a
+    // comparison with the other paths covers the two-heads-per-workgroup kernel too).
     SSD_TRY(hip_status(ssd::launch_cumsum_chunk_state_gemm1(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s,
-                                                            !staged_forced())));
+                                                            path != SSD_PATH_STAGED_ONE_HEAD)));
     SSD_TRY(hip_status(ssd::launch_state_passing(states, acum, initial_state, final_state, d, s)));
     return hip_status(ssd::launch_chunk_scan(x, Cm, cb, acum, dtc, states, D, y, o, d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_prefill_strided(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                        const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                        float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch,
+                        int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, long long x_stride,
+                        long long bc_stride, long long dt_stride, long long z_stride, void *workspace,
+                        size_t workspace_bytes, void *hip_stream)
+{
+    return prefill_impl(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype, y_dtype,
+                        batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x_stride, bc_stride, dt_stride,
+                        z_stride, workspace, workspace_bytes, hip_stream, SSD_PATH_AUTO, -1);
+}
+
+int ssd_prefill_forced(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                       const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                       float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                       int nheads, int headdim, int dstate, int ngroups, int chunk, long long x_stride,
+                       long long bc_stride, long long dt_stride, long long z_stride, void *workspace,
+                       size_t workspace_bytes, void *hip_stream, int path, long long spin_limit)
+{
+    return prefill_impl(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype, y_dtype,
+                        batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x_stride, bc_stride, dt_stride,
+                        z_stride, workspace, workspace_bytes, hip_stream, path, spin_limit);
+}
+
+int ssd_prefill_check(const void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < kWsAlign) return SSD_ERR_WORKSPACE;
+    SSD_TRY(hip_status(hipStreamSynchronize((hipStream_t)hip_stream)));
+    unsigned v = 0;
+    SSD_TRY(hip_status(hipMemcpy(&v, static_cast<const char *>(workspace) + 4, 4, hipMemcpyDeviceToHost)));
+    return v ? SSD_ERR_SYNC : SSD_OK;
 }
 
 int ssd_prefill_ex(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,

@@ -23,6 +23,8 @@
 // That replaces the separate state-passing launch (its read and write of every state, and
 // a launch) with one extra read of the chunk's state per workgroup, taken after the first
 // tile's steps, by which time the head's other workgroups are done.
+#include <algorithm>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -31,7 +33,6 @@ namespace ssd {
 // Cache-policy bit of buffer loads and stores: coherent across the whole device (the
 // per-XCD L2 caches are not coherent with each other; such accesses go through to memory).
 constexpr int kDeviceCoherent = 16;
-constexpr unsigned kSpinLimit = 1u << 22;  // bound of the wait for a head's other chunks
 
 // PNC = 0: hen holds the entering states [B, H, nc, P, N] (fp16).
 // PNC > 0 (nc <= PNC): hen holds the chunk states; Step-3 runs inside this launch.  The
@@ -320,10 +321,22 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             // it through to memory (written by other workgroups; words past the state read past
             // the range: zeros, not stored), and put it into LDS (rows p, padded).
             if (tid == 0) {
-                const unsigned *cnt = sync + ((size_t)b * H + h) * kSyncStride;
-                for (unsigned it = 0; it < kSpinLimit; ++it) {
-                    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)nc) break;
+                // Bounded: past the bound the workgroup gives up, sets bit 31 of the head's
+                // counter (which also releases the head's other waiters) and the prefill's
+                // give-up word, and goes on; the output is then not valid.
+                unsigned *cnt = sync + ((size_t)b * H + h) * kSyncStride;
+                const unsigned polls = spin_polls(opt.spin);
+                bool done = false;
+                for (unsigned it = 0; it < polls; ++it) {
+                    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)nc) {
+                        done = true;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(8);
+                }
+                if (!done) {
+                    __hip_atomic_fetch_or(cnt, 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (opt.ctl) __hip_atomic_fetch_or(&opt.ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             __syncthreads();
@@ -424,6 +437,45 @@ bool chunk_scan_small_fits(const Dims &d, int ncu)
 // (a thread keeps one state word of every chunk in registers).
 bool chunk_scan_small_pass_shape(const Dims &d) { return chunk_scan_small_shape(d) && d.nc <= 16; }
 bool chunk_scan_small_pass_fits(const Dims &d, int ncu) { return chunk_scan_small_pass_shape(d) && chunk_scan_small_fits(d, ncu); }
+
+// Whether the one-round launch's workgroups can all be resident at once on this device: the
+// occupancy the compiled instantiation allows (registers and LDS) times the compute units
+// must cover the grid, since the workgroups of a head wait for each other.
+hipError_t chunk_scan_small_resident(const Dims &d, const SsdOpts &o, int ncu, bool *ok)
+{
+    *ok = false;
+    const long items = (long)d.nc * d.H * d.B;
+    const long nsplit = (items > ncu && items <= 2L * ncu) ? std::min(items - ncu, 2L * ncu - items) / 8 * 8 : 0;
+    const long wgs = items + nsplit;
+    int per_cu = 0;
+    hipError_t e = hipSuccess;
+    const bool opt = o.z || o.y_bf16;
+#define SSD_SMALL_OCC(NN, OO, PP) \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_scan_small_kernel<64, NN, OO, PP>, 512, 0)
+#define SSD_SMALL_OCC2(NN, PP)              \
+    do {                                    \
+        if (opt) SSD_SMALL_OCC(NN, true, PP); \
+        else SSD_SMALL_OCC(NN, false, PP);  \
+    } while (0)
+#define SSD_SMALL_OCC3(NN)                      \
+    do {                                        \
+        if (!o.sync) SSD_SMALL_OCC2(NN, 0);     \
+        else if (d.nc <= 8) SSD_SMALL_OCC2(NN, 8); \
+        else SSD_SMALL_OCC2(NN, 16);            \
+    } while (0)
+    switch (d.N) {
+    case 32: SSD_SMALL_OCC3(32); break;
+    case 64: SSD_SMALL_OCC3(64); break;
+    case 128: SSD_SMALL_OCC3(128); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef SSD_SMALL_OCC3
+#undef SSD_SMALL_OCC2
+#undef SSD_SMALL_OCC
+    if (e != hipSuccess) return e;
+    *ok = (long)per_cu * ncu >= wgs;
+    return hipSuccess;
+}
 
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
                                    const float *dtc, void *h, const float *init, float *fin, const float *D,

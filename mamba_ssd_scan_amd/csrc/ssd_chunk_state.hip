@@ -93,6 +93,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     const int nblk = (Q + JB - 1) / JB;
     // the head's completion counter of a chunk scan that runs Step-3 itself starts at zero
     if (FUSE_CUMSUM && opt.sync && c == 0 && tid == 0) opt.sync[((size_t)b * H + h) * kSyncStride] = 0u;
+    // ... and the prefill's give-up word is clear
+    if (FUSE_CUMSUM && opt.ctl && c == 0 && h == 0 && b == 0 && tid == 0) opt.ctl[1] = 0u;
 
     struct Stage {
         Raw8<TIn> x[XPT][2], b[BPT][2];

@@ -70,6 +70,8 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     float *ws = wsb + hw * Q;
     // the head's completion counter of a chunk scan that runs Step-3 itself starts at zero
     if (opt.sync && c == 0 && ht == 0) opt.sync[((size_t)b * H + h) * kSyncStride] = 0u;
+    // ... and the prefill's give-up word is clear
+    if (opt.ctl && c == 0 && h == 0 && b == 0 && tid == 0) opt.ctl[1] = 0u;
 
     // ---- prologue: the step sizes first (wavefront 0 of each head), then every block of
     // the chunk: X for this thread's head, B shared by the pair

@@ -82,7 +82,16 @@ struct SsdOpts {
     const void *z;
     int y_bf16;
     unsigned *sync;  // per-(b, h) counters of a launch that runs Step-3 inside the chunk scan
+    // The prefill's control words: ctl[1] is the give-up word (set when a bounded wait between
+    // workgroups gave up; cleared by the prefill's first launch).  nullptr: none.
+    unsigned *ctl;
+    // Bound of every wait between workgroups: 0 = the default; n > 0 = n - 1 polls (1: give up
+    // at once, which only a test of the give-up path asks for).
+    unsigned spin;
 };
+// Polls a bounded wait makes: the default bound, or the one SsdOpts::spin asks for.
+constexpr unsigned kSpinLimit = 1u << 22;
+__host__ __device__ __forceinline__ unsigned spin_polls(unsigned spin) { return spin ? spin - 1u : kSpinLimit; }
 // One counter per 256 bytes, so that the heads' counters sit in different lines.
 constexpr int kSyncStride = 64;
 

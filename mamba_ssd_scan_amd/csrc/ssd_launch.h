@@ -57,9 +57,25 @@ bool chunk_scan_small_fits(const Dims &d, int ncu);
 bool chunk_scan_small_pass_fits(const Dims &d, int ncu);  // ... and o.sync may be set (nc <= 16)
 bool chunk_scan_small_pass_shape(const Dims &d);          // the part of it that needs no device query
 hipError_t device_cu_count(int *ncu);  // compute units of the current device
+// Whether the one-round launch (with o.sync as given) can have every workgroup resident at
+// once on the current device (its occupancy, queried for the instantiation it would launch).
+hipError_t chunk_scan_small_resident(const Dims &d, const SsdOpts &o, int ncu, bool *ok);
 hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb, const float *acum,
                                    const float *dtc, void *h, const float *init, float *fin, const float *D,
                                    void *y, const SsdOpts &o, const Dims &d, int ncu, hipStream_t s);
+// The single-pass prefill for grids of many rounds (bf16, Q = 256, P = 64, N in {64, 128}):
+// a GEMM1 launch, then one launch in which every (b, h, chunk) item forms its chunk state,
+// receives its entering state through a look-back of kFusedDepth chunks and writes its
+// output.  ws: fused_prefill_ws_bytes(d) bytes, 256-byte aligned; its first word after the
+// ticket (byte 4) is the give-up word (nonzero: a bounded wait gave up, the output is not
+// valid); o.spin bounds the waits.
+constexpr int kFusedDepth = 2;
+constexpr int kFusedRing = 8;  // ring slots per (b, h) of each kind (aggregates, inclusive states)
+bool fused_prefill_shape(const Dims &d);
+size_t fused_prefill_ws_bytes(const Dims &d);
+hipError_t launch_prefill_fused(const void *x, const void *Bm, const void *Cm, const void *dt, const float *A,
+                                const float *D, const float *init, float *fin, void *y, void *ws, const SsdOpts &o,
+                                const Dims &d, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,

@@ -15,11 +15,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
-SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = 0, -1, -2, -3, -4
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_SYNC = 0, -1, -2, -3, -4, -5
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_step_ex", "ssd_step_strided",
+           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_prefill_forced", "ssd_prefill_check",
+           "ssd_step_ex", "ssd_step_strided",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
            "ssd_chunk_gemm1", "ssd_chunk_scan", "ssd_chunk_scan_passing")
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
     ll = ctypes.c_longlong
     L.ssd_prefill_strided.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [ll] * 4 + [vp, sz, vp]
     L.ssd_prefill_strided.restype = i
+    L.ssd_prefill_forced.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [ll] * 4 + [vp, sz, vp, i, ll]
+    L.ssd_prefill_forced.restype = i
+    L.ssd_prefill_check.argtypes = [vp, sz, vp]
+    L.ssd_prefill_check.restype = i
     L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
     L.ssd_step_ex.restype = i
     L.ssd_step_strided.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [ctypes.c_longlong] * 4 + [vp]
@@ -225,52 +230,20 @@ def alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, devi
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=None, final_state="new",
-            workspace=None, stream=None) -> Tuple[object, Optional[object]]:
-    """Chunked SSD prefill.  Returns (y [B,L,H,P] fp32, final_state [B,H,P,N] fp32 or None).
+PATH_AUTO, PATH_STAGED, PATH_ONE_ROUND, PATH_SINGLE_PASS, PATH_STAGED_ONE_HEAD = 0, 1, 2, 3, 4
 
-    x, dt, B and C may be views into wider token rows (e.g. slices of a layer's
-    projection output): they are then read in place through ssd_prefill_strided.
 
-    ``final_state``: "new" allocates it, None skips it, or pass a tensor
-    (which may be ``initial_state`` itself for an in-place update).
-    """
+def _on_stream(stream):
+    """Context in which the wrappers allocate: the caller's stream when one is given, so that
+    the caching allocator does not hand the memory (the workspace above all) to other work
+    while the kernels on that stream still use it."""
+    import contextlib
     torch = _torch()
-    batch, seqlen, nheads, headdim = x.shape
-    ngroups, dstate = B.shape[2], B.shape[3]
-    code = _dtype_code(x)
-    for t in (dt, B, C):
-        if t.dtype != x.dtype:
-            raise TypeError("x, dt, B and C must share one dtype")
-    strides, dense = _seq_strides(x, dt, B, C, None)  # views into wider token rows are read in place
-    _dev(A, D, initial_state, y, workspace)
-    _f32(A, D, initial_state, y)
-    if y is None:
-        y = torch.empty((batch, seqlen, nheads, headdim), dtype=torch.float32, device=x.device)
-    if isinstance(final_state, str):
-        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
-    _dev(final_state)
-    _f32(final_state)
-    if workspace is None:
-        workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
-    wbytes = workspace.numel() * workspace.element_size()
-    if not dense:
-        _check(lib().ssd_prefill_strided(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), None, 0, None,
-                                         _ptr(initial_state), _ptr(final_state), _ptr(y), code, SSD_F32, batch,
-                                         seqlen, nheads, headdim, dstate, ngroups, chunk, *strides, _ptr(workspace),
-                                         wbytes, _stream(stream)), "ssd_prefill_strided")
-        return y, final_state
-    _check(lib().ssd_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
-                             _ptr(final_state), _ptr(y), code, batch, seqlen, nheads, headdim, dstate, ngroups,
-                             chunk, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill")
-    return y, final_state
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
-def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_softplus=False, z=None,
-               y_dtype=None, chunk: int = 256, y=None, final_state="new", workspace=None, stream=None):
-    """ssd_prefill_ex: prefill with dt = softplus(dt + dt_bias) (or dt + dt_bias), the z gate
-    y * z * sigmoid(z), and y stored as float32 or bfloat16 (``y_dtype``, default float32).
-    Returns (y, final_state or None)."""
+def _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state, workspace,
+             stream, path, spin_limit, plain):
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
@@ -283,28 +256,71 @@ def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_s
     strides, dense = _seq_strides(x, dt, B, C, z)  # views into wider token rows are read in place
     _dev(A, D, initial_state, y, workspace, dt_bias)
     _f32(A, D, initial_state, dt_bias)
-    if y is None:
-        y = torch.empty((batch, seqlen, nheads, headdim), dtype=y_dtype, device=x.device)
-    elif y.dtype != y_dtype:
-        raise TypeError("y does not have y_dtype")
-    if isinstance(final_state, str):
-        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+    with _on_stream(stream):
+        if y is None:
+            y = torch.empty((batch, seqlen, nheads, headdim), dtype=y_dtype, device=x.device)
+        elif y.dtype != y_dtype:
+            raise TypeError("y does not have y_dtype")
+        if isinstance(final_state, str):
+            final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
     _dev(final_state)
     _f32(final_state)
-    if workspace is None:
-        workspace = alloc_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x.device)
     wbytes = workspace.numel() * workspace.element_size()
-    if not dense:
-        _check(lib().ssd_prefill_strided(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
-                                         int(bool(dt_softplus)), _ptr(z), _ptr(initial_state), _ptr(final_state),
-                                         _ptr(y), code, ycode, batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
-                                         *strides, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill_strided")
-        return y, final_state
-    _check(lib().ssd_prefill_ex(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
-                                int(bool(dt_softplus)), _ptr(z), _ptr(initial_state), _ptr(final_state), _ptr(y),
-                                code, ycode, batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
-                                _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill_ex")
+    shape = (batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+    opts = (_ptr(dt_bias), int(bool(dt_softplus)), _ptr(z))
+    ins = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D))
+    if path != PATH_AUTO or spin_limit is not None:
+        _check(lib().ssd_prefill_forced(*ins, *opts, _ptr(initial_state), _ptr(final_state), _ptr(y), code, ycode,
+                                        *shape, *strides, _ptr(workspace), wbytes, _stream(stream), int(path),
+                                        -1 if spin_limit is None else int(spin_limit)), "ssd_prefill_forced")
+    elif not dense:
+        _check(lib().ssd_prefill_strided(*ins, *opts, _ptr(initial_state), _ptr(final_state), _ptr(y), code, ycode,
+                                         *shape, *strides, _ptr(workspace), wbytes, _stream(stream)),
+               "ssd_prefill_strided")
+    elif plain:
+        _check(lib().ssd_prefill(*ins, _ptr(initial_state), _ptr(final_state), _ptr(y), code, *shape,
+                                 _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill")
+    else:
+        _check(lib().ssd_prefill_ex(*ins, *opts, _ptr(initial_state), _ptr(final_state), _ptr(y), code, ycode,
+                                    *shape, _ptr(workspace), wbytes, _stream(stream)), "ssd_prefill_ex")
     return y, final_state
+
+
+def prefill(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y=None, final_state="new",
+            workspace=None, stream=None, path=PATH_AUTO, spin_limit=None) -> Tuple[object, Optional[object]]:
+    """Chunked SSD prefill.  Returns (y [B,L,H,P] fp32, final_state [B,H,P,N] fp32 or None).
+
+    x, dt, B and C may be views into wider token rows (e.g. slices of a layer's
+    projection output): they are then read in place through ssd_prefill_strided.
+
+    ``final_state``: "new" allocates it, None skips it, or pass a tensor
+    (which may be ``initial_state`` itself for an in-place update).
+    ``path`` / ``spin_limit`` (tests and diagnostics): run through ssd_prefill_forced on the
+    given path (PATH_*) with the given bound of the waits between workgroups.
+    """
+    if y is not None:
+        _f32(y)
+    return _prefill(x, dt, A, B, C, D, initial_state, None, False, None, None, chunk, y, final_state, workspace,
+                    stream, path, spin_limit, plain=True)
+
+
+def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_softplus=False, z=None,
+               y_dtype=None, chunk: int = 256, y=None, final_state="new", workspace=None, stream=None,
+               path=PATH_AUTO, spin_limit=None):
+    """ssd_prefill_ex: prefill with dt = softplus(dt + dt_bias) (or dt + dt_bias), the z gate
+    y * z * sigmoid(z), and y stored as float32 or bfloat16 (``y_dtype``, default float32).
+    Returns (y, final_state or None)."""
+    return _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state,
+                    workspace, stream, path, spin_limit, plain=False)
+
+
+def prefill_check(workspace, stream=None) -> int:
+    """ssd_prefill_check: synchronise ``stream`` and return SSD_OK, or SSD_ERR_SYNC when a bounded
+    wait of the last prefill on ``workspace`` gave up (its output is then not valid)."""
+    return int(lib().ssd_prefill_check(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
 
 
 def step_ex(state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z=None, y_dtype=None, y=None,

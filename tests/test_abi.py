@@ -32,9 +32,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for s in (0, -1, -2, -3, -4, 99):
+    for s in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(ssd.status_string(s), str) and ssd.status_string(s)
-    assert ssd.lib().ssd_version() >> 16 == 3
+    assert "SYNC" in ssd.status_string(ssd.SSD_ERR_SYNC)
+    assert ssd.lib().ssd_version() >> 16 == 4
 
 
 def gemm1_steps(q):
@@ -47,20 +48,43 @@ def test_gemm1_steps_closed_form():
     assert [gemm1_steps(q) for q in (16, 32, 64, 128, 256)] == [1, 2, 6, 20, 72]
 
 
+FUSED_DEPTH = 2  # look-back depth of the single-pass prefill: 2 * depth ring slots of each kind per (b, h)
+
+
 def test_workspace_size_formula():
     L = ssd.lib()
     al = lambda v: (v + 255) // 256 * 256
     for (b, l, h, p, n, g, q) in [(1, 4096, 24, 64, 128, 1, 256), (8, 2048, 32, 64, 64, 1, 64),
-                                  (2, 1000, 6, 32, 128, 3, 128), (1, 1, 1, 32, 32, 1, 16)]:
+                                  (2, 1000, 6, 32, 128, 3, 128), (1, 1, 1, 32, 32, 1, 16),
+                                  (1, 16384, 80, 64, 128, 1, 256), (3, 3000, 8, 64, 64, 2, 256)]:
         nc = -(-l // q)
         bhq = b * h * nc * q * 4
         cb = 4 * b * g * nc * gemm1_steps(q) * 512
-        want = al(al(al(al(al(bhq) + bhq) + 4 * b * h * nc * p * n) + cb) + 256 * b * h)
-        assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want
+        # control block, dA_cum, dt_c, states, GEMM1 products, one counter per (b, h)
+        want = al(al(al(al(al(256 + bhq) + bhq) + 4 * b * h * nc * p * n) + cb) + 256 * b * h)
+        if q == 256 and p == 64 and n in (64, 128):
+            # single pass: control block, status words, ring slots, fp16 GEMM1 products
+            fused = al(al(al(256 + b * h * 256) + b * h * 4 * FUSED_DEPTH * p * n * 4) + cb // 2)
+            want = max(want, fused)
+        assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want, (b, l, h, p, n, g, q)
         assert L.ssd_chunk_gemm1_size(b, l, g, q) == cb
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 1, 48) == 0   # bad chunk
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 48, 128, 1, 64) == 0   # bad headdim
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 5, 64) == 0   # H % G
+
+
+def test_forced_path_and_check_reject_before_any_hip_call():
+    L = ssd.lib()
+    args = [P0, P0, P0, P0, P0, None, None, 0, None, None, None, P0, BF, F, 1, 300, 4, 64, 64, 1, 64, 0, 0, 0, 0,
+            P0, 1 << 30, None]
+    assert L.ssd_prefill_forced(*args, 5, -1) == INV      # no such path
+    assert L.ssd_prefill_forced(*args, -1, -1) == INV
+    bad = list(args)
+    bad[12] = 7                                            # bad dtype, any path
+    assert L.ssd_prefill_forced(*bad, ssd.PATH_STAGED, -1) == INV
+    assert L.ssd_prefill_check(None, 1 << 20, None) == WS
+    assert L.ssd_prefill_check(P0 + 16, 1 << 20, None) == WS  # misaligned
+    assert L.ssd_prefill_check(P0, 255, None) == WS           # smaller than the control block
 
 
 def _prefill(**kw):

@@ -7,7 +7,7 @@ workgroup walking the recurrence for its share of the head's state and waiting
 for the head's other chunks (with between one and two items per compute unit,
 some items are split over two workgroups of one 16-row tile per wavefront).  The recurrence's arithmetic is the standalone
 state-passing kernel's, so the two-launch prefill must equal the three-launch
-one (SSD_PREFILL_STAGED=1) bit for bit, and the fp64 oracle within the bf16
+one (ssd_prefill_forced with SSD_PATH_STAGED_ONE_HEAD) bit for bit, and the fp64 oracle within the bf16
 bar.  The forced three-launch path also keeps one head per chunk-state
 workgroup, so the same comparison covers the two-heads-per-workgroup chunk-state
 kernel the default path uses (on one-round grids here, on grids of many rounds in the last
@@ -16,7 +16,6 @@ per-head counters must start from zero on every call.
 """
 from __future__ import annotations
 
-import os
 import numpy as np
 import pytest
 
@@ -44,15 +43,20 @@ def _fits(B, L, H):
     return B * H * ssd.nchunks(L, Q) <= 2 * ncu
 
 
-def _prefill(g, final, ws, staged):
-    """ssd_prefill on the two-launch path, or on the three-launch one (staged)."""
-    if staged:
-        os.environ["SSD_PREFILL_STAGED"] = "1"
-    try:
-        return ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=Q,
-                           final_state="new" if final else None, workspace=ws)
-    finally:
-        os.environ.pop("SSD_PREFILL_STAGED", None)
+def _two_launch_path(B, L, H):
+    """The path these tests compare with the one-head three-launch prefill bit for bit: the
+    one-round path where it applies (at most 16 chunks), else the three-launch path with two
+    heads per chunk-state workgroup."""
+    return ssd.PATH_ONE_ROUND if _fits(B, L, H) and ssd.nchunks(L, Q) <= 16 else ssd.PATH_STAGED
+
+
+def _prefill(g, final, ws, staged, path=None):
+    """ssd_prefill on the library's path, or on the three-launch one with one head per
+    chunk-state workgroup (staged)."""
+    if path is None:
+        path = ssd.PATH_STAGED_ONE_HEAD if staged else ssd.PATH_AUTO
+    return ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=Q,
+                       final_state="new" if final else None, workspace=ws, path=path)
 
 
 # (B, L, H, N, G, with initial state, with final state, dt mode)
@@ -83,7 +87,7 @@ def test_fused_pass_equals_stages_and_oracle(B, L, H, N, G, init, final, mode):
                                    init_state=init, dt_mode=mode)
         print(f"[fused pass] B={B} L={L} H={H} N={N} G={G} init={init} final={final} {mode} call {call}", flush=True)
         g = gh.upload(inp)
-        y, fin = _prefill(g, final, ws, staged=False)
+        y, fin = _prefill(g, final, ws, staged=False, path=_two_launch_path(B, L, H))
         torch.cuda.synchronize()
         ys, fins = _prefill(g, final, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=True)
         torch.cuda.synchronize()
@@ -212,14 +216,14 @@ def test_prefill_in_a_callers_graph():
 ])
 def test_two_head_chunk_state_on_grids_of_many_rounds(B, L, H, N, G):
     """The two-heads-per-workgroup chunk state also runs where its grid takes several rounds
-    (it needs no co-residency); the prefill then equals the forced-staged one, which keeps one
-    head per workgroup, bit for bit."""
+    (it needs no co-residency); the three-launch prefill with it equals the one that keeps one
+    head per chunk-state workgroup, bit for bit."""
     torch = gh.torch()
     inp = synth.random_prefill(np.random.Generator(np.random.PCG64(950 + H)), B, L, H, 64, N, G, "bf16",
                                init_state=True, dt_mode="weak")
     print(f"[two-head chunk state, many rounds] B={B} L={L} H={H} N={N} G={G}", flush=True)
     g = gh.upload(inp)
-    y, fin = _prefill(g, True, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=False)
+    y, fin = _prefill(g, True, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=False, path=ssd.PATH_STAGED)
     ys, fins = _prefill(g, True, ssd.alloc_workspace(B, L, H, 64, N, G, Q), staged=True)
     torch.cuda.synchronize()
     assert torch.equal(y, ys) and torch.equal(fin, fins)

@@ -157,18 +157,14 @@ def test_strided_inputs_on_the_staged_path():
     """Strided inputs through the forced three-launch prefill (one head per chunk-state
     workgroup, the standalone state passing) equal the default two-launch prefill on the
     same views bit for bit."""
-    import os
     torch = gh.torch()
     rng = np.random.Generator(np.random.PCG64(1600))
     inp = synth.random_prefill(rng, 1, 4096, 24, 64, 128, 1, "bf16", dt_mode="weak")
     g = gh.upload(inp)
     v, keep = _layer_rows(g, None, pad_xbc=8)
     y, fin = ssd.prefill(v["x"], v["dt"], g["A"], v["B"], v["C"], g["D"], g["h0"], chunk=256)
-    os.environ["SSD_PREFILL_STAGED"] = "1"
-    try:
-        ys, fins = ssd.prefill(v["x"], v["dt"], g["A"], v["B"], v["C"], g["D"], g["h0"], chunk=256)
-    finally:
-        os.environ.pop("SSD_PREFILL_STAGED", None)
+    ys, fins = ssd.prefill(v["x"], v["dt"], g["A"], v["B"], v["C"], g["D"], g["h0"], chunk=256,
+                           path=ssd.PATH_STAGED_ONE_HEAD)
     torch.cuda.synchronize()
     assert torch.isfinite(ys).all()
     assert torch.equal(y, ys) and torch.equal(fin, fins)
