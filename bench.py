@@ -1,17 +1,17 @@
 """Benchmark of the SSD layer core on one MI355X.
 
-One step = one full chunked prefill (all prefill stages: cumulative decay,
-chunk states, inter-chunk state passing, intra-chunk + off-diagonal output)
-over the Mamba-2-130M-shaped workload (batch 1, 4096 tokens, 24 heads,
-headdim 64, d_state 128, chunk 256, bf16 inputs, fp32 state and output),
-with inputs resident in HBM.  Each timed step starts cold: a 512 MiB read
-evicts the 256 MiB Infinity Cache and the L2s first, outside the timed
-events.  The decode update (batch 64, 80 heads, 1024 tokens) is timed in the
-same run and reported under "decode".
+One step = one full chunked prefill (every prefill stage: cumulative decay, chunk states,
+inter-chunk state passing, intra-chunk + off-diagonal output) over the Mamba-2-2.7B-shaped
+long-context layer (batch 1, 16384 tokens, 80 heads, headdim 64, d_state 128, chunk 256,
+bf16 inputs, fp32 state and output, random initial state), with inputs resident in HBM.
+Each timed step starts cold: a 512 MiB read evicts the 256 MiB Infinity Cache and the L2s
+first, outside the timed events.  The 130M- and 370M-shaped layers are timed the same way
+and reported under "workloads"; the decode update (batch 64, 80 heads, 1024 tokens) under
+"decode".
 
-Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
-the stream the kernels run on.  The oracle (fp64 CPU recurrence) is timed on
-the host's cores as "cpu_baseline".
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on the stream
+the kernels run on.  The oracle (fp64 CPU recurrence) is timed on the host's cores on the
+same workload as "cpu_baseline".
 """
 from __future__ import annotations
 
@@ -33,7 +33,8 @@ from mamba_ssd_scan_amd import ssd, synth  # noqa: E402
 METRIC = "SSD tokens/s + % roofline (prefill MFMA TFLOPS, decode-step HBM GB/s)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 matrix, published
-PREFILL_WORKLOAD = 1
+PREFILL_WORKLOAD = 3              # the headline step: the 2.7B-shaped 16384-token layer
+EXTRA_WORKLOADS = (1, 2)          # also timed, each with its own roofline
 DECODE_WORKLOAD = 4
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -41,6 +42,7 @@ KERNEL_SOURCES = {
     "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
     "step_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
     "chunk_scan_small_kernel": "ssd_chunk_scan_small.hip", "chunk_state_pair_kernel": "ssd_chunk_state_pair.hip",
+    "chunk_fused_kernel": "ssd_prefill_fused.hip", "fused_prep_kernel": "ssd_prefill_fused.hip",
 }
 
 
@@ -126,6 +128,20 @@ def alg_counts(s: synth.PrefillShape, ncu=None) -> dict:
                                             flops=k["chunk_scan_kernel"]["flops"] + 2 * B * H * nc * P * N)
     fused_bytes = x + dt + 2 * bc + y + st + h0
     fused_flops = B * nc * (G * N * tri + H * P * tri) + 4 * B * H * L * P * N
+    # the method's own tensors each kernel reads or writes (inputs, y, the initial and final
+    # states), without the intermediates of this implementation (decay tables, chunk and
+    # entering states, GEMM1 products): what a kernel would move if nothing else existed
+    method = {
+        "chunk_cumsum_kernel": dt,
+        "chunk_state_kernel": x + bc,
+        "chunk_state_pair_kernel": x + dt + 2 * bc,
+        "state_passing_kernel": h0 + st,
+        "chunk_gemm1_kernel": 2 * bc,
+        "chunk_scan_kernel": x + bc + y,
+        "chunk_scan_small_kernel": x + bc + y + (h0 + st if passing_in_scan(s, ncu) else 0),
+    }
+    for name, b in method.items():
+        k[name]["method_bytes"] = b
     return dict(kernels=k, fused_bytes=fused_bytes, fused_flops=fused_flops)
 
 
@@ -239,9 +255,9 @@ def time_launches(torch, fn, n, flush=None, before=None):
             gc.enable()
     t = np.array([a.elapsed_time(b) * 1e3 for a, b in with_fn])
     if flush is None:
-        return float(t.mean()), float(t.min())
+        return float(t.mean()), float(t.min()), float(np.median(t))
     f = np.array([c.elapsed_time(d) * 1e3 for c, d in alone])
-    return float(t.mean() - f.mean()), float(t.min() - f.mean())
+    return float(t.mean() - f.mean()), float(t.min() - f.mean()), float(np.median(t) - np.median(f))
 
 
 def prefill_buffers(torch, s, inp):
@@ -320,7 +336,11 @@ def stage_fns(torch, g, s):
 
 def cpu_baseline(s, inp, min_seconds=10.0, max_reps=2000):
     from oracle import ref  # the oracle: test infrastructure, timed here as the CPU baseline
-    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("SSD_ORACLE_THREADS", "16")))
+    # every core this process may run on, within the host's share for this GPU when the
+    # environment states one (OMP_NUM_THREADS)
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit() and int(os.environ["OMP_NUM_THREADS"]) > 0:
+        cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
     f64 = {k: (None if inp[k] is None else np.ascontiguousarray(inp[k], np.float64))
            for k in ("x", "dt", "A", "B", "C", "D", "h0")}
     ref.load()
@@ -367,7 +387,7 @@ def bench_decode(torch, steps, flush):
         k[0] += 1
         ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
 
-    us_cold, _ = time_launches(torch, one, min(64, steps), flush=flush)
+    us_cold = time_launches(torch, one, min(64, steps), flush=flush)[0]
     # the same tokens as one HIP graph (ssd_decode_graph): one launch for all of them
     y_all = torch.empty((steps, s.batch, s.nheads, s.headdim), dtype=torch.float32, device="cuda")
     graph = ssd.DecodeGraph(state, xs, dts, A, Bs, Cs, D, y=y_all)
@@ -432,8 +452,8 @@ def bench_layer_rows(torch, s, g, flush, steps):
         in_place()
         copied()
     torch.cuda.synchronize()
-    us_in, _ = time_launches(torch, in_place, steps, flush=flush)
-    us_cp, _ = time_launches(torch, copied, steps, flush=flush)
+    us_in = time_launches(torch, in_place, steps, flush=flush)[0]
+    us_cp = time_launches(torch, copied, steps, flush=flush)[0]
     return {"in_place_us": us_in, "copy_then_dense_us": us_cp,
             "rows": f"x|B|C rows of {hp + 2 * gn} and z|x|B|C|dt rows of {2 * hp + 2 * gn + H} elements",
             "note": "cold, events on the launch stream; the copies are torch's, outside the library"}
@@ -483,19 +503,115 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
 
 # ---------------------------------------------------------------------------- main
 
+def bench_prefill_workload(torch, wl, steps, warmup, flush, headline=False):
+    """Cold prefill steps of one workload, its kernels one by one, and the rooflines.
+
+    Returns (record, inputs, buffers, wall seconds of the timed steps)."""
+    s = synth.WORKLOADS[wl]
+    inp = synth.prefill_inputs(s, synth.SEED_BASE + wl)
+    g = prefill_buffers(torch, s, inp)
+    settle_clocks(torch, flush)
+    for _ in range(warmup):
+        run_prefill(g, s)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` cold steps, bracketed by synchronisations
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    us_step, us_step_min, us_step_med = time_launches(torch, lambda: run_prefill(g, s), steps, flush=flush)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    tokens = s.batch * s.seqlen
+    us_warm = time_back_to_back(torch, lambda: run_prefill(g, s), steps)
+
+    # ---- per-kernel durations (cold), events on the launch stream
+    counts = alg_counts(s)
+    stages = stage_fns(torch, g, s)
+    kernels = {}
+    for name, (fn, before) in stages.items():
+        us, us_min, us_med = time_launches(torch, fn, steps, flush=flush, before=before)
+        c = counts["kernels"][name]
+        kernels[name] = {"us": us, "us_min": us_min, "us_median": us_med, "method_bytes": c["method_bytes"],
+                         "alg_bytes_incl_intermediates": c["bytes"], "alg_flops": c["flops"],
+                         "method_gbps": c["method_bytes"] / (us * 1e-6) / 1e9, "tflops": c["flops"] / (us * 1e-6) / 1e12}
+    # the step's longest launch among those timed on their own (the fused first launch has no
+    # entry point of its own; its duration is in the kernel trace)
+    dom = max((k for k in step_kernels(s) if k in kernels), key=lambda k: kernels[k]["us"])
+    d = kernels[dom]
+    roof = {"bound": "hbm", "achieved": d["method_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": d["method_gbps"] / HBM_PEAK_GBS, "traffic": counter_traffic(dom, synth.WORKLOAD_NAMES[wl]),
+            "kernel": dom,
+            "variant": ("with Step-3 (ssd_chunk_scan_passing)" if dom == "chunk_scan_small_kernel"
+                        and passing_in_scan(s) else "as launched by the stage entry point"),
+            "us_per_launch": d["us"], "method_bytes_per_launch": d["method_bytes"],
+            "alg_bytes_incl_intermediates_per_launch": d["alg_bytes_incl_intermediates"],
+            "alg_flops_per_launch": d["alg_flops"], "mfma_tflops": d["tflops"],
+            "mfma_frac": d["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+            "intensity_flop_per_method_byte": d["alg_flops"] / d["method_bytes"]}
+
+    sec = us_step * 1e-6
+    fb, ff = counts["fused_bytes"], counts["fused_flops"]
+    prefill = {
+        "us_per_step_cold": us_step, "us_per_step_cold_median": us_step_med, "us_per_step_cold_min": us_step_min,
+        "us_per_step_warm": us_warm, "tokens_per_s": tokens / sec, "warm_tokens_per_s": tokens / (us_warm * 1e-6),
+        "method_bytes": fb, "alg_flops": ff,
+        "method_gbps": fb / sec / 1e9, "hbm_frac_method_bytes": fb / sec / 1e9 / HBM_PEAK_GBS,
+        "alg_tflops": ff / sec / 1e12, "alg_mfma_frac": ff / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "hbm_floor_us": fb / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "step_launches": step_kernels(s),
+        "kernel_us_sum": sum(kernels[k]["us"] for k in step_kernels(s) if k in kernels),
+    }
+    # bf16 y (the fp32 result rounded once): halves the largest stream
+    if s.dtype == "bf16":
+        yb = torch.empty((s.batch, s.seqlen, s.nheads, s.headdim), dtype=torch.bfloat16, device="cuda")
+        fbf = lambda: ssd.prefill_ex(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], y_dtype=torch.bfloat16,
+                                     chunk=s.chunk, y=yb, final_state=g["final"], workspace=g["ws"])
+        for _ in range(3):
+            fbf()
+        torch.cuda.synchronize()
+        ub = time_launches(torch, fbf, steps, flush=flush)
+        bb = fb - s.batch * s.seqlen * s.nheads * s.headdim * 2
+        prefill["bf16_y"] = {"us_per_step_cold": ub[0], "us_per_step_cold_median": ub[2],
+                             "tokens_per_s": tokens / (ub[0] * 1e-6), "method_bytes": bb,
+                             "hbm_frac_method_bytes": bb / (ub[0] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    rec = {"workload": synth.WORKLOAD_NAMES[wl], "value": tokens / sec, "unit": "tokens/s",
+           "roofline": roof, "prefill": prefill, "kernels": kernels}
+    return rec, inp, g, wall
+
+
+def bench_single_pass(torch, wl, g, steps, flush):
+    """The single-pass prefill (only selected on request) on the same workload, cold."""
+    s = synth.WORKLOADS[wl]
+    ws = ssd.alloc_workspace(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk)
+    f = lambda: ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk, y=g["y"],
+                            final_state=g["final"], workspace=ws, path=ssd.PATH_SINGLE_PASS)
+    try:
+        f()
+    except ssd.SsdError:
+        return None
+    for _ in range(2):
+        f()
+    torch.cuda.synchronize()
+    us = time_launches(torch, f, steps, flush=flush)
+    return {"us_per_step_cold": us[0], "us_per_step_cold_median": us[2],
+            "tokens_per_s": s.batch * s.seqlen / (us[0] * 1e-6),
+            "note": "ssd_prefill_forced with SSD_PATH_SINGLE_PASS; the library's own path is the step above"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=PREFILL_WORKLOAD, choices=[0, 1, 2, 3],
-                    help="prefill workload timed as the step (default 1; the others are for comparison)")
+                    help="prefill workload timed as the step (default 3; 1 and 2 are also reported)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
                                        "chunk_cumsum_kernel", "chunk_gemm1_kernel", "chunk_scan_small_kernel",
-                                       "step", "cached", "copy"],
+                                       "single_pass", "step", "cached", "copy"],
                     help="profiling aid: launch only this work --steps times (cold), print nothing else")
     args = ap.parse_args()
 
@@ -533,95 +649,51 @@ def main():
     if args.only == "cached":
         print(json.dumps(bench_cached_vs_recompute(torch)))
         return 0
-
-    inp = synth.prefill_inputs(s, synth.SEED_BASE + args.workload)
-    g = prefill_buffers(torch, s, inp)
-    settle_clocks(torch, flush)
-    for _ in range(args.warmup):
-        run_prefill(g, s)
-    torch.cuda.synchronize()
-
-    if args.only == "prefill":
-        time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
-        return 0
-    stages = stage_fns(torch, g, s)
     if args.only is not None:
-        fn, before = stages[args.only]
-        time_launches(torch, fn, args.steps, flush=flush, before=before)
+        inp = synth.prefill_inputs(s, synth.SEED_BASE + args.workload)
+        g = prefill_buffers(torch, s, inp)
+        settle_clocks(torch, flush)
+        for _ in range(args.warmup):
+            run_prefill(g, s)
+        torch.cuda.synchronize()
+        if args.only == "prefill":
+            time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
+        elif args.only == "single_pass":
+            bench_single_pass(torch, args.workload, g, args.steps, flush)
+        else:
+            fn, before = stage_fns(torch, g, s)[args.only]
+            time_launches(torch, fn, args.steps, flush=flush, before=before)
         return 0
 
-    # ---- timed region: exactly K cold steps, bracketed by synchronisations
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    us_step, us_step_min = time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    tokens = s.batch * s.seqlen
-
-    # warm (back-to-back) steps, for reference only
-    stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(args.steps):
-        run_prefill(g, s)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us_warm = a.elapsed_time(b) * 1e3 / args.steps
-
-    # ---- per-kernel durations (cold), events on the launch stream
-    counts = alg_counts(s)
-    kernels = {}
-    for name, (fn, before) in stages.items():
-        us, us_min = time_launches(torch, fn, args.steps, flush=flush, before=before)
-        kb, kf = counts["kernels"][name]["bytes"], counts["kernels"][name]["flops"]
-        kernels[name] = {"us": us, "us_min": us_min, "alg_bytes": kb, "alg_flops": kf,
-                         "gbps": kb / (us * 1e-6) / 1e9, "tflops": kf / (us * 1e-6) / 1e12}
-    # the step's longest launch among those timed on their own (the fused first launch has no
-    # entry point of its own; its duration is in the kernel trace)
-    dom = max((k for k in step_kernels(s) if k in kernels), key=lambda k: kernels[k]["us"])
-    d = kernels[dom]
-    intensity = d["alg_flops"] / d["alg_bytes"]
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    bound = "hbm" if intensity < ridge else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["gbps"] / HBM_PEAK_GBS}
-    else:
-        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": d["tflops"] / MFMA_BF16_PEAK_TFLOPS}
-    roof.update({"traffic": counter_traffic(dom, wname), "kernel": dom,
-                 "variant": ("with Step-3 (ssd_chunk_scan_passing)" if dom == "chunk_scan_small_kernel"
-                             and passing_in_scan(s) else "as launched by the stage entry point"),
-                 "us_per_launch": d["us"],
-                 "alg_bytes_per_launch": d["alg_bytes"], "alg_flops_per_launch": d["alg_flops"],
-                 "intensity_flop_per_byte": intensity})
-
-    sec = us_step * 1e-6
-    prefill = {
-        "us_per_step_cold": us_step, "us_per_step_cold_min": us_step_min, "us_per_step_warm": us_warm,
-        "alg_tflops": counts["fused_flops"] / sec / 1e12,
-        "alg_mfma_frac": counts["fused_flops"] / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "alg_gbps_fused_bytes": counts["fused_bytes"] / sec / 1e9,
-        "hbm_frac_fused_bytes": counts["fused_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
-        "fused_alg_bytes": counts["fused_bytes"], "alg_flops": counts["fused_flops"],
-        "attainable_frac": (counts["fused_bytes"] / (HBM_PEAK_GBS * 1e9)) / sec,
-        "warm_tokens_per_s": tokens / (us_warm * 1e-6),
-    }
+    rec, inp, g, wall = bench_prefill_workload(torch, args.workload, args.steps, args.warmup, flush, headline=True)
+    us_step = rec["prefill"]["us_per_step_cold"]
     out = {
-        "metric": METRIC, "value": tokens / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us_step / 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": wname, "batch": s.batch, "seqlen": s.seqlen, "nheads": s.nheads,
                    "headdim": s.headdim, "dstate": s.dstate, "ngroups": s.ngroups, "chunk": s.chunk,
+                   "initial_state": s.init_state,
                    "cache": "cold (512 MiB eviction before each step, outside the events)",
                    "parallelism": "single GPU"},
-        "roofline": roof,
-        "prefill": prefill,
-        "kernels": kernels,
-        "step_launches": step_kernels(s),
+        "roofline": rec["roofline"],
+        "prefill": rec["prefill"],
+        "kernels": rec["kernels"],
         "timed_wall_s": wall,
     }
+    sp = bench_single_pass(torch, args.workload, g, args.steps, flush)
+    if sp is not None:
+        out["single_pass"] = sp
     out["layer_rows"] = bench_layer_rows(torch, s, g, flush, args.steps)
+    del g
+    if not args.no_extra:
+        out["workloads"] = {}
+        for wl in EXTRA_WORKLOADS:
+            if wl == args.workload:
+                continue
+            r, _, gx, _ = bench_prefill_workload(torch, wl, args.steps, args.warmup, flush)
+            out["workloads"][r["workload"]] = r
+            del gx
     if not args.no_decode:
         out["decode"] = bench_decode(torch, args.decode_steps, flush)
         out["cached_vs_recompute"] = bench_cached_vs_recompute(torch)

@@ -72,3 +72,20 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_method_bytes_of_the_headline_prefill():
+    """The 2.7B-shaped 16384-token layer: the method's own bytes per step (inputs, y, initial
+    and final state) are the 519.6 MB of the roofline floor; the persistent chunk scan's share is
+    x + C + y, without the entering states and GEMM1 products it also reads."""
+    s = synth.WORKLOADS[3]
+    c = bench.alg_counts(s, NCU)
+    L, H, P, N = 16384, 80, 64, 128
+    x, dt, bc, y, st = L * H * P * 2, L * H * 2, L * N * 2, L * H * P * 4, H * P * N * 4
+    assert c["fused_bytes"] == x + dt + 2 * bc + y + 2 * st == 519569408
+    k = c["kernels"]
+    assert k["chunk_scan_kernel"]["method_bytes"] == x + bc + y
+    assert k["chunk_scan_kernel"]["bytes"] > k["chunk_scan_kernel"]["method_bytes"]
+    assert k["chunk_state_pair_kernel"]["method_bytes"] == x + dt + 2 * bc
+    assert k["state_passing_kernel"]["method_bytes"] == 2 * st
+    assert bench.step_kernels(s, NCU)[-1] == "chunk_scan_kernel"
