@@ -21,8 +21,10 @@
  * - All tensor arguments are DEVICE pointers, dense, row-major in the
  *   layouts written next to each argument; base addresses 16-byte aligned.
  * - The caller owns all memory.  The library never allocates or frees device
- *   memory and keeps no device state; scratch comes from the caller's
- *   workspace.  No global mutable state: calls are reentrant and thread-safe.
+ *   memory; scratch comes from the caller's workspace, except for
+ *   ssd_prefill_noalloc, whose scratch is a device array of the library's own (one per
+ *   GPU, see there).  Apart from that array and its per-device address, no global state:
+ *   calls are reentrant and thread-safe.
  *   The one object the library creates is a decode graph, owned by the
  *   caller through its handle (ssd_decode_graph_create / _destroy).
  * - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
@@ -221,6 +223,26 @@ int ssd_prefill_forced(const void *x, const void *dt, const float *A, const void
  * the read failed (e.g. a kernel fault).
  */
 int ssd_prefill_check(const void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * ssd_prefill for callers that cannot allocate device memory -- code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: the same arguments without the
+ * workspace.  The scratch comes from a device array inside the library of
+ * SSD_PREFILL_NOALLOC_MAX_BYTES on each GPU it runs on (held until the process ends; its
+ * address is looked up once per device on the first call there).  The call allocates
+ * nothing.  It runs the three-launch path (no waits between workgroups), whose y and
+ * final_state equal ssd_prefill's bit for bit.
+ * Errors: as ssd_prefill, plus SSD_ERR_WORKSPACE when ssd_prefill_workspace_size(...) for
+ * the shape exceeds SSD_PREFILL_NOALLOC_MAX_BYTES.  Every call on one GPU uses that GPU's
+ * one array: calls that may overlap in time on one GPU (streams with no ordering between
+ * them) race and give undefined results.
+ */
+#define SSD_PREFILL_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int ssd_prefill_noalloc(const void *x, const void *dt, const float *A, const void *Bm,
+                        const void *Cm, const float *D, const float *initial_state,
+                        float *final_state, float *y, ssd_dtype_t in_dtype, int batch,
+                        int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                        int chunk, void *hip_stream);
 
 /*
  * One decode token for every (b, h), fused ("Compiler-First State Space Duality and

@@ -145,7 +145,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (4 << 16) | 0; }
+int ssd_version(void) { return (4 << 16) | 1; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)

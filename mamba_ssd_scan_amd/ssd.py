@@ -19,7 +19,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_prefill_forced", "ssd_prefill_check",
+           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_prefill_forced", "ssd_prefill_check", "ssd_prefill_noalloc",
            "ssd_step_ex", "ssd_step_strided",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_prefill_forced.restype = i
     L.ssd_prefill_check.argtypes = [vp, sz, vp]
     L.ssd_prefill_check.restype = i
+    L.ssd_prefill_noalloc.argtypes = [vp] * 9 + [i] * 8 + [vp]
+    L.ssd_prefill_noalloc.restype = i
     L.ssd_step_ex.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [vp]
     L.ssd_step_ex.restype = i
     L.ssd_step_strided.argtypes = [vp] * 8 + [i] + [vp] * 2 + [i] * 7 + [ctypes.c_longlong] * 4 + [vp]
@@ -314,6 +316,28 @@ def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_s
     Returns (y, final_state or None)."""
     return _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state,
                     workspace, stream, path, spin_limit, plain=False)
+
+
+NOALLOC_MAX_BYTES = 64 << 20  # SSD_PREFILL_NOALLOC_MAX_BYTES
+
+
+def prefill_noalloc(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 256, y, final_state=None,
+                    stream=None):
+    """ssd_prefill_noalloc: the prefill with the library's own scratch (no workspace, nothing
+    allocated by the library).  y [B,L,H,P] fp32 and final_state (or None) are the caller's;
+    x, dt, B and C must be dense.  Returns (y, final_state)."""
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    code = _dtype_code(x)
+    for t in (dt, B, C):
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise TypeError("x, dt, B and C must share one dtype and be dense")
+    _dev(A, D, initial_state, y, final_state)
+    _f32(A, D, initial_state, y, final_state)
+    _check(lib().ssd_prefill_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+                                     _ptr(final_state), _ptr(y), code, batch, seqlen, nheads, headdim, dstate,
+                                     ngroups, chunk, _stream(stream)), "ssd_prefill_noalloc")
+    return y, final_state
 
 
 def prefill_check(workspace, stream=None) -> int:
