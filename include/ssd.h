@@ -47,8 +47,13 @@
  * - Non-finite values are propagated, not trapped.
  *
  * Supported shapes: batch >= 1; seqlen >= 0; nheads % ngroups == 0;
- * headdim (P) in {32, 64, 128}; dstate (N) in {32, 64, 128};
- * chunk (Q) in {16, 32, 64, 128, 256}.  Anything else returns
+ * chunk (Q) in {16, 32, 64, 128, 256}; headdim (P) and dstate (N) any multiple of 16
+ * from 16 to 256 for the prefill and decode calls.  The kernels are built for
+ * P in {32, 64, 128} and N in {32, 64, 128, 256}: the prefill runs other sizes padded
+ * to the next built size inside its workspace (zero channels and zero state columns,
+ * which add exact zeros), and a P above 128 as two heads of P/2 channels (a head's
+ * channels evolve independently); the decode step takes every such size directly.
+ * The stage entry points take only the built sizes.  Anything else returns
  * SSD_ERR_UNSUPPORTED (or SSD_ERR_INVALID_ARG for non-positive sizes).
  */
 #ifndef MAMBA_SSD_SCAN_AMD_SSD_H
@@ -89,8 +94,11 @@ int ssd_version(void);
  *           states (fp16 for bf16 inputs -- half the region -- fp32 for fp32 inputs)
  *   cb      ssd_chunk_gemm1_size(B, L, G, Q) bytes: the C.B^T products
  *   sync    [B, H] uint32 counters, one per 256 bytes, of the one-round path
- * Single-pass path: per (b, h) status words and 8 ring slots of P*N fp32 states, and the
- * C.B^T products.  nc = ceil(seqlen / Q).
+ * Single-pass path: per (b, h) status words and 16 ring slots of P*N fp32 states, and the
+ * C.B^T products.  nc = ceil(seqlen / Q).  For a P or N the kernels are not built for, the
+ * workspace of the padded problem comes first, then padded copies of x, z, B, C, dt, A, D,
+ * the dt bias, the initial state, y and the final state (4 bytes per element).
+ * ssd_prefill_workspace_size returns the size of the layout the shape takes.
  */
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int dstate, int ngroups, int chunk);

@@ -22,23 +22,30 @@ constexpr size_t kWsAlign = 256;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool supported_dim(int v) { return v == 32 || v == 64 || v == 128; }
+// Sizes the kernels are built for (the stage entry points take only these); the prefill
+// and the decode step take any multiple of 16 up to 256 (the prefill pads to a built size).
+bool native_p(int v) { return v == 32 || v == 64 || v == 128; }
+bool native_n(int v) { return v == 32 || v == 64 || v == 128 || v == 256; }
+bool any16(int v) { return v >= 16 && v <= 256 && v % 16 == 0; }
 bool supported_chunk(int q) { return q == 16 || q == 32 || q == 64 || q == 128 || q == 256; }
 
-// Common shape checks.  seqlen < 0 => not a sequence call (decode).
+// Common shape checks.  seqlen < 0 => not a sequence call (decode).  native: only the
+// built sizes of P and N (stage entry points).
 int check_shape(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk,
-                bool need_chunk)
+                bool need_chunk, bool native = false)
 {
     if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return SSD_ERR_INVALID_ARG;
     if (need_chunk && (seqlen < 0 || chunk <= 0)) return SSD_ERR_INVALID_ARG;
     if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARG;
-    if (!supported_dim(headdim) || !supported_dim(dstate)) return SSD_ERR_UNSUPPORTED;
+    if (native ? !(native_p(headdim) && native_n(dstate)) : !(any16(headdim) && any16(dstate)))
+        return SSD_ERR_UNSUPPORTED;
     if (need_chunk && !supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
     if (batch > 65535 || nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y/z limits
     // chunk counts and token offsets are formed in 32-bit ints
     if (need_chunk && (long long)seqlen + chunk > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
-    if (need_chunk && (long long)nheads + 4LL * ngroups > 65535) return SSD_ERR_UNSUPPORTED;  // chunk-state grid y
-    if ((long long)batch * nheads > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+    const long long hx = headdim > 128 ? 2LL * nheads : nheads;  // heads as the kernels see them (see PadPlan)
+    if (need_chunk && hx + 4LL * ngroups > 65535) return SSD_ERR_UNSUPPORTED;  // chunk-state grid y
+    if ((long long)batch * hx > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     // One chunk of x or B/C is addressed with 32-bit byte offsets inside the kernels.
     if (need_chunk && (long long)chunk * 4 * ((long long)nheads * headdim > (long long)ngroups * dstate
                                                   ? (long long)nheads * headdim
@@ -83,6 +90,57 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, i
     const ssd::Dims d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, SSD_BF16);
     if (ssd::fused_prefill_shape(d)) w.total = std::max(w.total, ssd::fused_prefill_ws_bytes(d));
     return w;
+}
+
+// How the prefill runs a shape whose P or N the kernels are not built for: P and N padded to
+// the next built size (zero channels of x and z, zero state columns of B, C and the states),
+// and a head of more than 128 channels run as two heads of half as many (its channels evolve
+// independently and share dt, A, D and the head's group of B and C).
+struct PadPlan {
+    int H, P, N;  // the problem as the kernels see it
+    int split;    // 1, or 2 kernel heads per head
+};
+PadPlan pad_plan(int nheads, int headdim, int dstate)
+{
+    PadPlan q;
+    const int P = headdim <= 32 ? 32 : headdim <= 64 ? 64 : headdim <= 128 ? 128 : 256;
+    q.N = dstate <= 32 ? 32 : dstate <= 64 ? 64 : dstate <= 128 ? 128 : 256;
+    q.split = P == 256 ? 2 : 1;
+    q.P = P / q.split;
+    q.H = nheads * q.split;
+    return q;
+}
+// The padded route's workspace: the padded problem's own workspace first (its control block
+// at offset 0, so ssd_prefill_check reads the same word), then the padded copies.
+struct PadWs {
+    size_t inner, x, z, b, c, dt, A, D, bias, h0, y, fin, total;
+};
+PadWs pad_ws(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk)
+{
+    const PadPlan q = pad_plan(nheads, headdim, dstate);
+    const size_t tok = (size_t)batch * seqlen, xel = tok * q.H * q.P, bel = tok * ngroups * q.N;
+    const size_t sel = (size_t)batch * q.H * q.P * q.N;
+    PadWs w;
+    w.inner = ws_layout(batch, seqlen, q.H, q.P, q.N, ngroups, chunk).total;
+    w.x = align_up(w.inner, kWsAlign);
+    w.z = align_up(w.x + 4 * xel, kWsAlign);
+    w.b = align_up(w.z + 4 * xel, kWsAlign);
+    w.c = align_up(w.b + 4 * bel, kWsAlign);
+    w.dt = align_up(w.c + 4 * bel, kWsAlign);
+    w.A = align_up(w.dt + 4 * tok * q.H, kWsAlign);
+    w.D = align_up(w.A + 4 * (size_t)q.H, kWsAlign);
+    w.bias = align_up(w.D + 4 * (size_t)q.H, kWsAlign);
+    w.h0 = align_up(w.bias + 4 * (size_t)q.H, kWsAlign);
+    w.y = align_up(w.h0 + 4 * sel, kWsAlign);
+    w.fin = align_up(w.y + 4 * xel, kWsAlign);
+    w.total = align_up(w.fin + 4 * sel, kWsAlign);
+    return w;
+}
+bool native_shape(int headdim, int dstate) { return native_p(headdim) && native_n(dstate); }
+size_t prefill_ws_bytes(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk)
+{
+    return native_shape(headdim, dstate) ? ws_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk).total
+                                         : pad_ws(batch, seqlen, nheads, headdim, dstate, ngroups, chunk).total;
 }
 
 ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk,
@@ -137,7 +195,7 @@ const char *ssd_status_string(int status)
     switch (status) {
     case SSD_OK: return "SSD_OK: success";
     case SSD_ERR_INVALID_ARG: return "SSD_ERR_INVALID_ARG: null/misaligned pointer, bad size or dtype, or nheads % ngroups != 0";
-    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: unsupported headdim/dstate/chunk, size limits, or a forced path that does not apply";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: headdim/dstate not a multiple of 16 in 16..256 (stage entry points: 32/64/128, and 256 for dstate), chunk not 16..256 (power of two), size limits, or a forced path that does not apply";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, smaller than ssd_prefill_workspace_size() or not 256-byte aligned";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP kernel launch failed";
     case SSD_ERR_SYNC: return "SSD_ERR_SYNC: a bounded wait between workgroups of the last prefill gave up; its output is not valid";
@@ -145,13 +203,13 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (4 << 16) | 1; }
+int ssd_version(void) { return (4 << 16) | 2; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
 {
     if (check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true) != SSD_OK) return 0;
-    return ws_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk).total;
+    return prefill_ws_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk);
 }
 
 int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c, ssd_dtype_t in_dtype,
@@ -173,7 +231,7 @@ int ssd_chunk_state(const void *x, const void *Bm, const float *dA_cum, const fl
                     int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
+    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true, true));
     if (seqlen == 0) return SSD_OK;
     SSD_TRY(check_seq_inputs(x, dt_c, Bm, SSD_F32));
     if (!dA_cum || !states || !aligned(dA_cum, 16) || !aligned(states, 16)) return SSD_ERR_INVALID_ARG;
@@ -188,7 +246,7 @@ int ssd_state_passing(void *states, const float *dA_cum, const float *initial_st
     SSD_TRY(check_dtype(in_dtype));
     if (nchunks < 0) return SSD_ERR_INVALID_ARG;
     if ((long long)nchunks * chunk > 0x7fffffffLL - 256) return SSD_ERR_UNSUPPORTED;  // nchunks * chunk is an int below
-    SSD_TRY(check_shape(batch, nchunks, nheads, headdim, dstate, 1, chunk, true));
+    SSD_TRY(check_shape(batch, nchunks, nheads, headdim, dstate, 1, chunk, true, true));
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, nchunks * chunk, nheads, headdim, dstate, 1, chunk, in_dtype);
     hipStream_t s = (hipStream_t)hip_stream;
@@ -205,7 +263,7 @@ int ssd_state_passing(void *states, const float *dA_cum, const float *initial_st
 size_t ssd_chunk_gemm1_size(int batch, int seqlen, int ngroups, int chunk)
 {
     // headdim/dstate/nheads do not enter the size; pass supported placeholders.
-    if (check_shape(batch, seqlen, ngroups, 64, 64, ngroups, chunk, true) != SSD_OK) return 0;
+    if (check_shape(batch, seqlen, ngroups, 64, 64, ngroups, chunk, true, true) != SSD_OK) return 0;
     return 4 * gemm1_elems(batch, ngroups, (seqlen + chunk - 1) / chunk, chunk);
 }
 
@@ -213,7 +271,7 @@ int ssd_chunk_gemm1(const void *Bm, const void *Cm, float *cb, ssd_dtype_t in_dt
                     int dstate, int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_shape(batch, seqlen, ngroups, 64, dstate, ngroups, chunk, true));
+    SSD_TRY(check_shape(batch, seqlen, ngroups, 64, dstate, ngroups, chunk, true, true));
     if (seqlen == 0) return SSD_OK;
     if (!Bm || !Cm || !cb || !aligned(Bm, 16) || !aligned(Cm, 16) || !aligned(cb, 16)) return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, seqlen, ngroups, 64, dstate, ngroups, chunk, in_dtype);
@@ -225,7 +283,7 @@ int ssd_chunk_scan(const void *x, const void *Cm, const float *cb, const float *
                    int seqlen, int nheads, int headdim, int dstate, int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
+    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true, true));
     if (seqlen == 0) return SSD_OK;
     SSD_TRY(check_seq_inputs(x, dt_c, Cm, SSD_F32));
     if (!cb || !dA_cum || !h_enter || !y) return SSD_ERR_INVALID_ARG;
@@ -243,7 +301,7 @@ int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const
                            int dstate, int ngroups, int chunk, void *hip_stream)
 {
     SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
+    SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true, true));
     if (seqlen == 0) return SSD_OK;
     SSD_TRY(check_seq_inputs(x, dt_c, Cm, SSD_F32));
     if (!cb || !dA_cum || !states || !y || !sync) return SSD_ERR_INVALID_ARG;
@@ -267,6 +325,70 @@ int ssd_chunk_scan_passing(const void *x, const void *Cm, const float *cb, const
 }  // extern "C"
 
 namespace {
+
+int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                 const float *dt_bias, int dt_softplus, const void *z, const float *initial_state, float *final_state,
+                 void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen, int nheads, int headdim,
+                 int dstate, int ngroups, int chunk, long long x_stride, long long bc_stride, long long dt_stride,
+                 long long z_stride, void *workspace, size_t workspace_bytes, void *hip_stream, int path,
+                 long long spin_limit);
+
+// The prefill of a shape the kernels are not built for (see PadPlan): the inputs are copied
+// into the workspace padded, the built prefill runs on the copies, and y and the final state
+// are copied back without the padding.  Strides are the resolved (nonzero) ones.
+int prefill_padded(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                   const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                   float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk, long long sx, long long sbc,
+                   long long sdt, long long sz, void *workspace, size_t workspace_bytes, hipStream_t s, int path,
+                   long long spin_limit)
+{
+    const PadPlan q = pad_plan(nheads, headdim, dstate);
+    const PadWs w = pad_ws(batch, seqlen, nheads, headdim, dstate, ngroups, chunk);
+    if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const int es = (int)in_size(in_dtype), ys = (int)in_size(y_dtype);
+    const long long tok = (long long)batch * seqlen;
+    const int Pp = q.P * q.split;  // padded channels of one head
+    auto pad = [&](const void *src, size_t off, int e, long long nout, int nin_s, int nin_d, int slen, int dlen,
+                   long long so, long long si, long long sk) {
+        return hip_status(ssd::launch_pad_copy(src, ws + off, e, nout, nin_s, nin_d, slen, dlen, so, si, sk, s));
+    };
+    SSD_TRY(pad(x, w.x, es, tok, nheads, nheads, headdim, Pp, sx, headdim, 1));
+    if (z) SSD_TRY(pad(z, w.z, es, tok, nheads, nheads, headdim, Pp, sz, headdim, 1));
+    SSD_TRY(pad(Bm, w.b, es, tok, ngroups, ngroups, dstate, q.N, sbc, dstate, 1));
+    SSD_TRY(pad(Cm, w.c, es, tok, ngroups, ngroups, dstate, q.N, sbc, dstate, 1));
+    // per-head parameters of split heads: each value twice, in place for both halves
+    const void *dt2 = dt;
+    const float *A2 = A, *D2 = D, *bias2 = dt_bias;
+    long long dt_stride2 = sdt;
+    if (q.split == 2) {
+        SSD_TRY(pad(dt, w.dt, es, tok, nheads, nheads, 2, 2, sdt, 1, 0));
+        SSD_TRY(pad(A, w.A, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
+        if (D) SSD_TRY(pad(D, w.D, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
+        if (dt_bias) SSD_TRY(pad(dt_bias, w.bias, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
+        dt2 = ws + w.dt;
+        A2 = reinterpret_cast<const float *>(ws + w.A);
+        D2 = D ? reinterpret_cast<const float *>(ws + w.D) : nullptr;
+        bias2 = dt_bias ? reinterpret_cast<const float *>(ws + w.bias) : nullptr;
+        dt_stride2 = 0;
+    }
+    const long long hs = (long long)headdim * dstate;
+    if (initial_state)
+        SSD_TRY(pad(initial_state, w.h0, 4, (long long)batch * nheads, headdim, Pp, dstate, q.N, hs, dstate, 1));
+    SSD_TRY(prefill_impl(ws + w.x, dt2, A2, ws + w.b, ws + w.c, D2, bias2, dt_softplus, z ? ws + w.z : nullptr,
+                         initial_state ? reinterpret_cast<const float *>(ws + w.h0) : nullptr,
+                         final_state ? reinterpret_cast<float *>(ws + w.fin) : nullptr, ws + w.y, in_dtype, y_dtype,
+                         batch, seqlen, q.H, q.P, q.N, ngroups, chunk, 0, 0, dt_stride2, 0, workspace, w.inner, s,
+                         path, spin_limit));
+    // y [B, L, H, Pp] -> [B, L, H, P]; final [B, H, Pp, N'] -> [B, H, P, N]
+    SSD_TRY(hip_status(ssd::launch_pad_copy(ws + w.y, y, ys, tok, nheads, nheads, headdim, headdim,
+                                            (long long)nheads * Pp, Pp, 1, s)));
+    if (final_state)
+        SSD_TRY(hip_status(ssd::launch_pad_copy(ws + w.fin, final_state, 4, (long long)batch * nheads, headdim,
+                                                headdim, dstate, dstate, (long long)Pp * q.N, q.N, 1, s)));
+    return SSD_OK;
+}
 
 // The prefill with an explicit path (0: the library's choice) and wait bound (< 0: default).
 int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
@@ -301,6 +423,10 @@ int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, 
     SSD_TRY(check_seq_inputs(x, dt, Bm, in_dtype));
     if (!A || !Cm || !y || !aligned(A, 4) || !aligned(Cm, 16) || !aligned(y, 16) || !aligned(D, 4))
         return SSD_ERR_INVALID_ARG;
+    if (!native_shape(headdim, dstate))
+        return prefill_padded(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype,
+                              y_dtype, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, sx, sbc, sdt, sz,
+                              workspace, workspace_bytes, s, path, spin_limit);
     const WsLayout w = ws_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk);
     if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 

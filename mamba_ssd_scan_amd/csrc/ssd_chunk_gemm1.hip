@@ -61,6 +61,7 @@ static hipError_t launch_gemm1_t(const void *Bm, const void *Cm, void *cb, const
     case 32: SSD_G1_BY_Q(32); break;
     case 64: SSD_G1_BY_Q(64); break;
     case 128: SSD_G1_BY_Q(128); break;
+    case 256: SSD_G1_BY_Q(256); break;
     default: return hipErrorInvalidValue;
     }
 #undef SSD_G1_BY_Q

@@ -575,6 +575,7 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
     case 32: SSD_SCAN_BY_Q(32); break;
     case 64: SSD_SCAN_BY_Q(64); break;
     case 128: SSD_SCAN_BY_Q(128); break;
+    case 256: SSD_SCAN_BY_Q(256); break;
     default: return hipErrorInvalidValue;
     }
 #undef SSD_SCAN_BY_Q

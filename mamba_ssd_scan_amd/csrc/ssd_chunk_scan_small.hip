@@ -427,7 +427,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 
 // Whether the one-round kernel takes this problem: bf16 inputs, chunks of 256 tokens,
 // supported P, and no more items than two per compute unit.
-bool chunk_scan_small_shape(const Dims &d) { return d.bf16 && d.Q == 256 && d.P == 64; }
+bool chunk_scan_small_shape(const Dims &d) { return d.bf16 && d.Q == 256 && d.P == 64 && d.N <= 128; }
 bool chunk_scan_small_fits(const Dims &d, int ncu)
 {
     return chunk_scan_small_shape(d) && (long)d.nc * d.H * d.B <= 2L * ncu;

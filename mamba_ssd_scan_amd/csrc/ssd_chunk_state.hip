@@ -415,6 +415,7 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
     case 32: SSD_CS_BY_JB(32); break;
     case 64: SSD_CS_BY_JB(64); break;
     case 128: SSD_CS_BY_JB(128); break;
+    case 256: SSD_CS_BY_JB(256); break;
     default: return hipErrorInvalidValue;
     }
 #undef SSD_CS_BY_JB

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
 
 bool chunk_state_pair_fits(const Dims &d)
 {
-    return d.bf16 && d.Q == 256 && d.P == 64 && d.G > 0 && (d.H / d.G) % 2 == 0;
+    return d.bf16 && d.Q == 256 && d.P == 64 && d.N <= 128 && d.G > 0 && (d.H / d.G) % 2 == 0;
 }
 
 hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt, const float *A, float *acum,

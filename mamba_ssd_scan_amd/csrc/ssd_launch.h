@@ -76,6 +76,10 @@ size_t fused_prefill_ws_bytes(const Dims &d);
 hipError_t launch_prefill_fused(const void *x, const void *Bm, const void *Cm, const void *dt, const float *A,
                                 const float *D, const float *init, float *fin, void *y, void *ws, const SsdOpts &o,
                                 const Dims &d, hipStream_t s);
+// Zero-padding copy: dst[(o * nin_dst + i) * dlen + k] = (i < nin_src && k < slen) ?
+// src[o * so + i * si + k * sk] : 0 for o < nout, i < nin_dst, k < dlen; elements of 2 or 4 bytes.
+hipError_t launch_pad_copy(const void *src, void *dst, int elem_bytes, long long nout, int nin_src, int nin_dst,
+                           int slen, int dlen, long long so, long long si, long long sk, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).
 hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,

@@ -69,8 +69,42 @@ def test_workspace_size_formula():
         assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == want, (b, l, h, p, n, g, q)
         assert L.ssd_chunk_gemm1_size(b, l, g, q) == cb
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 1, 48) == 0   # bad chunk
-    assert L.ssd_prefill_workspace_size(1, 4096, 24, 48, 128, 1, 64) == 0   # bad headdim
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 40, 128, 1, 64) == 0   # headdim not a multiple of 16
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 272, 128, 1, 64) == 0  # headdim past 256
+    assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 8, 1, 64) == 0     # dstate below 16
     assert L.ssd_prefill_workspace_size(1, 4096, 24, 64, 128, 5, 64) == 0   # H % G
+
+
+def _native_ws(b, l, h, p, n, g, q):
+    al = lambda v: (v + 255) // 256 * 256
+    nc = -(-l // q)
+    bhq = b * h * nc * q * 4
+    cb = 4 * b * g * nc * gemm1_steps(q) * 512
+    want = al(al(al(al(al(256 + bhq) + bhq) + 4 * b * h * nc * p * n) + cb) + 256 * b * h)
+    if q == 256 and p == 64 and n in (64, 128):
+        want = max(want, al(al(al(256 + b * h * 256) + b * h * 4 * FUSED_DEPTH * p * n * 4) + cb // 2))
+    return want
+
+
+@pytest.mark.parametrize("p,n", [(16, 16), (48, 80), (96, 256), (16, 128), (128, 16), (144, 64), (256, 256)])
+def test_workspace_size_of_padded_shapes(p, n):
+    """P and N that the kernels are not built for run padded to the next built size (P over
+    128 as two heads of half the channels); the workspace holds the padded problem's own
+    workspace, then padded copies of x, z, B, C, dt, A, D, the bias, the initial state, y and
+    the final state (4 bytes per element, each region 256-byte aligned)."""
+    L = ssd.lib()
+    al = lambda v: (v + 255) // 256 * 256
+    b, l, h, g, q = 2, 1000, 6, 3, 128
+    pp = 32 if p <= 32 else 64 if p <= 64 else 128 if p <= 128 else 256
+    nn = 32 if n <= 32 else 64 if n <= 64 else 128 if n <= 128 else 256
+    split = 2 if pp == 256 else 1
+    hk, pk = h * split, pp // split
+    tok = b * l
+    xel, bel, sel = tok * hk * pk, tok * g * nn, b * hk * pk * nn
+    off = _native_ws(b, l, hk, pk, nn, g, q)
+    for nbytes in (4 * xel, 4 * xel, 4 * bel, 4 * bel, 4 * tok * hk, 4 * hk, 4 * hk, 4 * hk, 4 * sel, 4 * xel, 4 * sel):
+        off = al(al(off) + nbytes)
+    assert L.ssd_prefill_workspace_size(b, l, h, p, n, g, q) == off
 
 
 def test_forced_path_and_check_reject_before_any_hip_call():
@@ -98,8 +132,8 @@ def _prefill(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), INV), (dict(batch=0), INV), (dict(seqlen=-1), INV), (dict(nheads=0), INV),
-    (dict(nheads=6, ngroups=4), INV), (dict(headdim=48), UNS), (dict(headdim=256), UNS), (dict(dstate=16), UNS),
-    (dict(dstate=256), UNS), (dict(chunk=48), UNS), (dict(chunk=512), UNS), (dict(chunk=0), INV),
+    (dict(nheads=6, ngroups=4), INV), (dict(headdim=40), UNS), (dict(headdim=272), UNS), (dict(dstate=8), UNS),
+    (dict(dstate=272), UNS), (dict(headdim=0), INV), (dict(chunk=48), UNS), (dict(chunk=512), UNS), (dict(chunk=0), INV),
     (dict(batch=70000), UNS), (dict(x=None), INV), (dict(dt=None), INV), (dict(A=None), INV), (dict(B=None), INV),
     (dict(C=None), INV), (dict(y=None), INV), (dict(x=P0 + 2), INV), (dict(B=P0 + 8), INV), (dict(C=P0 + 4), INV),
     (dict(y=P0 + 4), INV), (dict(dt=P0 + 1), INV), (dict(h0=P0 + 4), INV), (dict(hT=P0 + 8), INV),
@@ -123,7 +157,8 @@ def test_step_rejects_before_launch():
     assert st(y=None) == INV
     assert st(dtype=3) == INV
     assert st(headdim=40) == UNS
-    assert st(dstate=48) == UNS
+    assert st(dstate=40) == UNS
+    assert st(dstate=272) == UNS
     assert st(nheads=3, ngroups=2) == INV
     assert st(batch=0) == INV
     assert st(x=P0 + 1) == INV
@@ -160,7 +195,7 @@ def test_option_entry_points_reject_before_launch():
     assert st(y=None) == INV
     assert st(y=P0 + 2) == INV                 # fp32 y must be 4-byte aligned
     assert st(z=P0 + 1) == INV
-    assert st(headdim=48) == UNS
+    assert st(headdim=24) == UNS
 
 
 def test_strided_prefill_checks_token_strides_before_launch():
@@ -213,7 +248,7 @@ def test_strided_step_checks_batch_strides_before_launch():
     assert st(sx=-1) == INV
     assert st(sx=1 << 31) == UNS    # past 32-bit element offsets
     assert st(x=None, sx=300) == INV
-    assert st(headdim=48, sx=300) == UNS
+    assert st(headdim=40, sx=300) == UNS
 
 
 def test_decode_graph_rejects_before_capture():
@@ -237,7 +272,7 @@ def test_decode_graph_rejects_before_capture():
     assert mk(state=P0 + 4) == INV              # the state needs 16-byte alignment
     assert mk(z=P0 + 1) == INV
     assert mk(ydtype=3) == INV
-    assert mk(headdim=48) == UNS
+    assert mk(headdim=40) == UNS
     assert mk(nheads=6, ngroups=4) == INV
     assert L.ssd_decode_graph_create(None, 8, P0, P0, P0, P0, P0, P0, None, None, 0, None, P0, BF, F, 2, 4, 64, 64,
                                      1) == INV
