@@ -30,6 +30,8 @@
 // for the error budget); the X operand, whose reduction index is the token,
 // is read with the transposing LDS read.  fp32 inputs store X transposed and
 // run the fp32 matrix path.  Columns above the diagonal are skipped.
+#include <atomic>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -596,13 +598,21 @@ static hipError_t launch_scan_t(const void *x, const void *Cm, const void *cbg, 
     }
 }
 
+// Compute units per device, looked up once per device (an immutable property; two threads
+// that look it up at once store the same value).
+static std::atomic<int> g_ncu[64];
 hipError_t device_cu_count(int *ncu)
 {
     int dev = 0;
     *ncu = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (*ncu <= 0) *ncu = 1;
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) *ncu = g_ncu[dev].load(std::memory_order_relaxed);
+    if (*ncu <= 0) {
+        e = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (*ncu <= 0) *ncu = 1;
+        if (e == hipSuccess && dev >= 0 && dev < 64) g_ncu[dev].store(*ncu, std::memory_order_relaxed);
+    }
     return e;
 }
 
