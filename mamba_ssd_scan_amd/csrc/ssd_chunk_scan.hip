@@ -16,20 +16,20 @@
 // GEMM2, the off-diagonal product and the skip term are fused in one kernel:
 // the masked score tile never leaves registers.
 //
-// Work split: one workgroup per (b, h, c) covering the whole chunk, one
-// wavefront per 16-row tile (16 wavefronts for Q = 256); the four wavefronts
-// that share a SIMD take tiles {s, 7-s, 8+s, 15-s}, which balances the causal
-// triangle across the SIMDs.  The prologue stages the chunk's X (fp16,
-// row-major as it arrives) and the entering state (fp16) in LDS and the decay
-// tables, with one barrier; after it every wavefront runs on its own.  Per
-// 32-column step a wavefront loads its slice of G from the GEMM1 output (one
-// coalesced 2 KB read, issued a step ahead), which leaves every lane holding
-// one row i and eight columns j -- a row-slice of the GEMM2 A operand.  The
-// mask/decay/dt scaling is applied in registers and the result is rounded to
-// fp16 for GEMM2 (bf16 would round the computed scores to 2^-9, too coarse
-// for the error budget); the X operand, whose reduction index is the token,
-// is read with the transposing LDS read.  fp32 inputs store X transposed and
-// run the fp32 matrix path.  Columns above the diagonal are skipped.
+// Work split: a persistent grid (one workgroup of one wavefront per 16-row tile, 16
+// wavefronts for Q = 256, as many workgroups as the compute units hold) in which each
+// workgroup loops over a contiguous run of (b, c, h) items, the heads of a chunk in a row.
+// The four wavefronts that share a SIMD take tiles {s, 7-s, 8+s, 15-s}, which balances the
+// causal triangle across the SIMDs.  Per item the chunk's X (fp16, row-major as it arrives),
+// the entering state (fp16) and the decay tables are staged in LDS, with two barriers; after
+// them every wavefront runs on its own.  A wavefront holds the fp16 slices of G for its row
+// tile (one coalesced 1 KB read per 32-column step) and its C rows in registers, and keeps
+// them for the next head of the same chunk; every lane holds one row i and eight columns j
+// of a slice -- a row-slice of the GEMM2 A operand.  The mask/decay/dt scaling is applied in
+// registers and the result is rounded to fp16 for GEMM2 (bf16 would round the computed
+// scores to 2^-9, too coarse for the error budget); the X operand, whose reduction index is
+// the token, is read with the transposing LDS read.  fp32 inputs store X transposed and run
+// the fp32 matrix path.  Columns above the diagonal are skipped.
 #include <atomic>
 
 #include "ssd_common.h"
@@ -52,7 +52,9 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
     static constexpr int LDH = N + 8;                  // H_enter rows [P][N] (fp16), bf16 only
     static constexpr int HSZ = F32 ? 1 : P * LDH;
     static constexpr int TAB = ROWS + 32;              // tables padded past the last step
-    static constexpr int base = XSZ * (int)sizeof(op_t) + HSZ * 2 + 3 * TAB * 4;
+    // tables: dA_cum and dt in fp32, the off-diagonal column factors in fp32 (fp32 inputs) or
+    // fp16 (bf16 inputs, which scale their fp16 scores in packed fp16)
+    static constexpr int base = XSZ * (int)sizeof(op_t) + HSZ * 2 + 2 * TAB * 4 + TAB * (F32 ? 4 : 2);
     // raw staging: X rows, fp16 entering state, dA_cum and dt, and 1 KB that absorbs the
     // surplus loads of wavefronts with less to stream (every wavefront issues the same count)
     static constexpr int SX = ROWS * P * 2, SH = P * N * 2, ST = 2 * ROWS * 4, SD = 1024;
@@ -82,7 +84,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     __shared__ op_t hs[S::HSZ];
     // chunk tables: cumulative decay in log2 units, dt, and exp(a_r - a_j) dt_j with a_r the
     // last column of j's 32-column step (zero past the chunk; padding is never used unmasked)
-    __shared__ float acs[S::TAB], dts[S::TAB], ecs[S::TAB];
+    __shared__ float acs[S::TAB], dts[S::TAB];
+    __shared__ __align__(16) float ecs[F32 ? S::TAB : 1];
+    __shared__ __align__(16) f16 ech[F32 ? 1 : S::TAB];
     __shared__ __align__(16) unsigned char stg[STAGE ? S::SALL : 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -113,7 +117,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         return z;
     };
 
-    // Item k is chunk c of head h of batch entry b, k = (b H + h) nc + c.
+    // Item k is head h of chunk c of batch entry b, k = (b nc + c) H + h: consecutive items
+    // share the chunk's C rows and C.B^T slices (one group per H / G heads).
     struct Item {
         int c, h, b, g, vrows;
         size_t bhc;
@@ -121,8 +126,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     };
     auto decode = [&](int item) {
         Item it;
-        it.c = item % nc;
-        it.h = (item / nc) % H;
+        it.h = item % H;
+        it.c = (item / H) % nc;
         it.b = item / (nc * H);
         it.g = it.h / (H / G);
         it.bhc = ((size_t)it.b * H + it.h) * nc + it.c;
@@ -266,15 +271,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             }
             acs[tid] = a;
             dts[tid] = d;
-            ecs[tid] = e;
+            if constexpr (F32)
+                ecs[tid] = e;
+            else
+                ech[tid] = static_cast<f16>(e);
         }
     };
 
     // ---- per-wavefront operands of an item, held in registers: the C rows of the tile
     // (off-diagonal A operand) and, for bf16 inputs, all of the tile's fp16 slices of G
-    bf16x8 cb[F32 ? 1 : KS];
+    bf16x8 cb[F32 ? 1 : KS];  // bf16 as loaded; fp16 bit patterns once converted (cfresh false)
     float cf[F32 ? KS : 1];
     f16x8 gs[F32 ? 1 : NSMAX];
+    bool cfresh = false;  // cb holds newly loaded bf16 rows (wavefront-uniform)
     // The loads are unconditional (a wavefront without a tile reads slice 0 and C rows
     // past the buffer range, which return zeros): the wait before the next barrier then
     // knows exactly how many loads follow the staging loads it has to wait for.
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             for (int s = 0; s < NSMAX; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+            cfresh = true;
         }
     };
 
@@ -336,28 +346,72 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     // Every load and store below is issued unconditionally (empty ranges stand in for
     // the ones with nothing to do), so that each wait counts exactly the younger
     // operations it may leave in flight.
-    int item = blockIdx.x;
+    // Each workgroup takes a contiguous run of items: the heads of a chunk follow one another,
+    // so a wavefront keeps its tile operands (the C rows and the C.B^T slices of its row tile)
+    // in registers from one head to the next and loads them again only when the chunk or the
+    // group changes.  Workgroups are dispatched to the XCDs in turn; the runs are laid out so
+    // that the workgroups of one XCD take adjacent runs and share the chunks in its L2.
+    const int nwg = gridDim.x;
+    const int vw = (nwg & 7) == 0 ? (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int per = nitems / nwg, extra = nitems % nwg;
+    int item = vw * per + min(vw, extra);
+    const int last = item + per + (vw < extra ? 1 : 0);
     Item cur = decode(item), prev = cur;
     stage_issue(cur, true);
     load_tile_operands(cur);
     for (bool first = true;; first = false) {
         const float Dh = D ? D[cur.h] : 0.f;
-        __syncthreads();  // the item's staged loads have landed; the previous item's readers are done
+        // The item's staged loads have landed (they may be the youngest memory operations:
+        // the tile operand loads that follow them are conditional) ...
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        __syncthreads();  // ... and the previous item's readers are done
         stage_commit(cur);
         __syncthreads();
         store_y(prev, !first);
-        const int next = item + gridDim.x;
-        const bool more = next < nitems;
+        const int next = item + 1;
+        const bool more = next < last;
         const Item nx = more ? decode(next) : cur;
         stage_issue(nx, more);
 
         if (t >= 0) {
-#pragma unroll
-            for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
-            // ---- Step-1: the causal 32-column steps of this row tile.  All but the last lie
-            // strictly below the diagonal; the last one holds it (tile t: steps 0 .. t/2).
             const int irow = ibase + li;
             const float ai = acs[irow];
+            // ---- Step-4 first: exp(a_i) * (C_i . H_enter[p, :]) for this wavefront's rows,
+            // scaled in the accumulator that Step-1 then adds to
+            {
+                const float *hp = static_cast<const float *>(henv) + cur.bhc * P * N;  // fp32 inputs only
+                if constexpr (!F32) {
+                    // the C rows of a new chunk: to fp16 once, kept for the chunk's other heads
+                    // (exact for bf16 inputs in fp16 range)
+                    if (cfresh) {
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(cb[ks]));
+                        cfresh = false;
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int pt = 0; pt < TP; ++pt) {
+                        if constexpr (F32) {
+                            acc[pt] = mfma16x16x4_f32(cf[ks], hp[(pt * 16 + li) * N + ks * 4 + lg], acc[pt]);
+                        } else {
+                            const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
+                            acc[pt] = mfma16x16x32_f16(__builtin_bit_cast(f16x8, cb[ks]), hf, acc[pt]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(acs[ibase + 4 * lg + r]);
+#pragma unroll
+                    for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= e;
+                }
+            }
+            // ---- Step-1: the causal 32-column steps of this row tile.  All but the last lie
+            // strictly below the diagonal; the last one holds it (tile t: steps 0 .. t/2).
             const size_t slice0 = (((size_t)cur.b * G + cur.g) * nc + cur.c) * (size_t)spc + Tt;
             const float *gf = static_cast<const float *>(cbg) + (slice0 * 64 + lane) * 8;
             // Lane holds G[irow][jb + 4 lg + r] (d0) and G[irow][jb + 16 + 4 lg + r] (d1).
@@ -369,7 +423,21 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                     d1[0] = g1.x; d1[1] = g1.y; d1[2] = g1.z; d1[3] = g1.w;
                 }
             };
-            // GEMM2 of one step: k slots of lane group lg are columns {jb+4lg+r, jb+16+4lg+r}
+            // GEMM2 of one step (bf16 inputs): the fp16 score fragment a times X, k slots of lane
+            // group lg being columns {jb+4lg+r, jb+16+4lg+r}
+            auto gemm2h = [&](int jb, const f16x8 &a) {
+                if constexpr (!F32) {
+#pragma unroll
+                    for (int pt = 0; pt < TP; ++pt) {
+                        // lane li receives X[jb + 4 lg + r][16 pt + li] and X[jb + 16 + 4 lg + r][16 pt + li]
+                        const int ox = tr16_offset(lane, jb, pt * 16, LDX);
+                        const f16x4 lo = lds_read_tr16(&xs[ox]);
+                        const f16x4 hi = lds_read_tr16(&xs[ox + 16 * LDX]);
+                        const f16x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        acc[pt] = mfma16x16x32_f16(a, bx, acc[pt]);
+                    }
+                }
+            };
             auto gemm2 = [&](int jb, bool has1, const float r0[4], const float r1[4]) {
                 if constexpr (F32) {
 #pragma unroll
@@ -389,15 +457,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                         a[r] = static_cast<f16>(r0[r]);
                         a[4 + r] = static_cast<f16>(r1[r]);
                     }
-#pragma unroll
-                    for (int pt = 0; pt < TP; ++pt) {
-                        // lane li receives X[jb + 4 lg + r][16 pt + li] and X[jb + 16 + 4 lg + r][16 pt + li]
-                        const int ox = tr16_offset(lane, jb, pt * 16, LDX);
-                        const f16x4 lo = lds_read_tr16(&xs[ox]);
-                        const f16x4 hi = lds_read_tr16(&xs[ox + 16 * LDX]);
-                        const f16x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        acc[pt] = mfma16x16x32_f16(a, bx, acc[pt]);
-                    }
+                    gemm2h(jb, a);
                 }
             };
 #pragma unroll
@@ -408,27 +468,28 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                     // are <= 1 (a is non-increasing for A <= 0) and any underflow drops a term
                     // smaller still; exp(a_r - a_j) dt_j is the chunk table.
                     const int jb = 32 * s;
-                    float d0[4], d1[4];
+                    const float er = __builtin_amdgcn_exp2f(ai - acs[jb + 31]);
                     if constexpr (F32) {
+                        float d0[4], d1[4];
                         slice(s, d0, d1);
-                    } else {
+                        const float4 e0 = *reinterpret_cast<const float4 *>(&ecs[jb + 4 * lg]);
+                        const float4 e1 = *reinterpret_cast<const float4 *>(&ecs[jb + 16 + 4 * lg]);
+                        const float ej0[4] = {e0.x, e0.y, e0.z, e0.w}, ej1[4] = {e1.x, e1.y, e1.z, e1.w};
+                        float r0[4], r1[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            d0[r] = static_cast<float>(gs[s][r]);
-                            d1[r] = static_cast<float>(gs[s][4 + r]);
+                            r0[r] = d0[r] * (er * ej0[r]);
+                            r1[r] = d1[r] * (er * ej1[r]);
                         }
+                        gemm2(jb, true, r0, r1);
+                    } else {
+                        // in packed fp16: G (fp16) * (exp(a_i - a_r) * table), both factors in
+                        // (0, 1] times dt; a factor below the fp16 range drops a negligible term
+                        const f16x4 e0 = *reinterpret_cast<const f16x4 *>(&ech[jb + 4 * lg]);
+                        const f16x4 e1 = *reinterpret_cast<const f16x4 *>(&ech[jb + 16 + 4 * lg]);
+                        const f16x8 ej = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+                        gemm2h(jb, gs[s] * (ej * static_cast<f16>(er)));
                     }
-                    const float er = __builtin_amdgcn_exp2f(ai - acs[jb + 31]);
-                    const float4 e0 = *reinterpret_cast<const float4 *>(&ecs[jb + 4 * lg]);
-                    const float4 e1 = *reinterpret_cast<const float4 *>(&ecs[jb + 16 + 4 * lg]);
-                    const float ej0[4] = {e0.x, e0.y, e0.z, e0.w}, ej1[4] = {e1.x, e1.y, e1.z, e1.w};
-                    float r0[4], r1[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        r0[r] = d0[r] * (er * ej0[r]);
-                        r1[r] = d1[r] * (er * ej1[r]);
-                    }
-                    gemm2(jb, true, r0, r1);
                 }
             }
             {
@@ -463,35 +524,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                                                                    : 0.f;
                 }
                 gemm2(jb, has1, r0, r1);
-            }
-
-            // ---- Step-4: exp(a_i) * (C_i . H_enter[p, :]) for this wavefront's rows, in its
-            // own accumulator, added scaled
-            {
-                const float *hp = static_cast<const float *>(henv) + cur.bhc * P * N;  // fp32 inputs only
-                f32x4 off[TP];
-#pragma unroll
-                for (int pt = 0; pt < TP; ++pt) off[pt] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    f16x8 ch;
-                    if constexpr (!F32) ch = bf16x8_to_f16x8(cb[ks]);
-#pragma unroll
-                    for (int pt = 0; pt < TP; ++pt) {
-                        if constexpr (F32) {
-                            off[pt] = mfma16x16x4_f32(cf[ks], hp[(pt * 16 + li) * N + ks * 4 + lg], off[pt]);
-                        } else {
-                            const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
-                            off[pt] = mfma16x16x32_f16(ch, hf, off[pt]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(acs[ibase + 4 * lg + r]);
-#pragma unroll
-                    for (int pt = 0; pt < TP; ++pt) acc[pt][r] += e * off[pt][r];
-                }
             }
             // ---- skip term
             if constexpr (F32) {
@@ -534,8 +566,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                     acc[pt][r] *= silu(zf);
                 }
         }
-        // the next item's tile operands, in flight while its staging completes
-        load_tile_operands(nx);
+        // the next item's tile operands when its chunk or group differs, in flight while its
+        // staging completes
+        if (more && (nx.c != cur.c || nx.b != cur.b || nx.g != cur.g)) load_tile_operands(nx);
         prev = cur;
         if (!more) break;
         item = next;
@@ -550,7 +583,7 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
                                 const SsdOpts &o, const Dims &d, int ncu, hipStream_t s)
 {
     // persistent: enough workgroups for 16 wavefronts per compute unit, each looping over
-    // the (b, h, c) items with stride gridDim.x
+    // its run of (b, c, h) items
     const int nitems = d.nc * d.H * d.B;
     const TIn *xx = static_cast<const TIn *>(x), *cc = static_cast<const TIn *>(Cm);
     // up to 16 wavefronts per compute unit, as many workgroups as the LDS holds
