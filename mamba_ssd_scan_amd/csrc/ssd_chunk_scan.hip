@@ -282,11 +282,12 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     // (off-diagonal A operand) and, for bf16 inputs, all of the tile's fp16 slices of G
     bf16x8 cb[F32 ? 1 : KS];  // bf16 as loaded; fp16 bit patterns once converted (cfresh false)
     float cf[F32 ? KS : 1];
-    f16x8 gs[F32 ? 1 : NSMAX];
+    f16x8 gs[F32 ? 1 : NSMAX - 1];  // the steps below the diagonal
+    f16x8 gdg;                      // the diagonal step
     bool cfresh = false;  // cb holds newly loaded bf16 rows (wavefront-uniform)
-    // The loads are unconditional (a wavefront without a tile reads slice 0 and C rows
-    // past the buffer range, which return zeros): the wait before the next barrier then
-    // knows exactly how many loads follow the staging loads it has to wait for.
+    // Issued when an item's chunk or group differs from the previous item's, at the end of
+    // the previous item.  A wavefront without a tile reads slice 0 and C rows past the buffer
+    // range, which return zeros.
     auto load_tile_operands = [&](const Item &it) {
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * sbc + (size_t)it.g * N,
                                                     (uint32_t)(((it.vrows - 1) * sbc + N) * sizeof(TIn)));
@@ -300,7 +301,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             const f16 *gq = static_cast<const f16 *>(cbg) + (slice0 * 64 + lane) * 8;
             const int slast = ns > 0 ? ns - 1 : 0;
 #pragma unroll
-            for (int s = 0; s < NSMAX; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
+            for (int s = 0; s < NSMAX - 1; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
+            gdg = *reinterpret_cast<const f16x8 *>(gq + (size_t)slast * 512);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
             cfresh = true;
@@ -500,14 +502,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                 if constexpr (F32) {
                     slice(sd, d0, d1);
                 } else {
-                    f16x8 gd = gs[0];
-#pragma unroll
-                    for (int s = 1; s < NSMAX; ++s)
-                        if (s == sd) gd = gs[s];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        d0[r] = static_cast<float>(gd[r]);
-                        d1[r] = static_cast<float>(gd[4 + r]);
+                        d0[r] = static_cast<float>(gdg[r]);
+                        d1[r] = static_cast<float>(gdg[4 + r]);
                     }
                 }
                 const float4 a0v = *reinterpret_cast<const float4 *>(&acs[jb + 4 * lg]);
