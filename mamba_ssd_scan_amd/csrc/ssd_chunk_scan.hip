@@ -56,7 +56,7 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
     // fp16 (bf16 inputs, which scale their fp16 scores in packed fp16)
     static constexpr int base = XSZ * (int)sizeof(op_t) + HSZ * 2 + 2 * TAB * 4 + TAB * (F32 ? 4 : 2);
     // raw staging: X rows, fp16 entering state, dA_cum and dt, and 1 KB that absorbs the
-    // surplus loads of wavefronts with less to stream (every wavefront issues the same count)
+    // surplus loads of streaming wavefronts with less to stream (each issues the same count)
     static constexpr int SX = ROWS * P * 2, SH = P * N * 2, ST = 2 * ROWS * 4, SD = 1024;
     static constexpr int SALL = SX + SH + ST + SD;
     static constexpr bool STAGE = !F32 && base + SALL <= 160 * 1024;
@@ -142,20 +142,26 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                          (uint32_t)(((it.vrows - 1) * sx + P) * sizeof(TIn)));
     };
 
-    // ---- staging (bf16 inputs): direct-to-LDS loads of the raw X rows, the raw fp32
-    // entering state and the item's dA_cum / dt, each wavefront instruction filling 1 KB
-    // (or 256 B for the tables) of the staging area.  Every wavefront issues the same
-    // number of loads; a surplus one reads an empty range into the spare 1 KB.
-    // (with live == false every load reads an empty range: the count stays the same)
+    // ---- staging (bf16 inputs): direct-to-LDS loads of the raw X rows, the fp16 entering
+    // state and the item's dA_cum / dt, each wavefront instruction filling 1 KB (or 256 B for
+    // the tables) of the staging area.  Every streaming wavefront issues the same number of
+    // loads; a surplus one reads an empty range into the spare 1 KB.  (With live == false
+    // every load reads an empty range: the count stays the same.)
     auto stage_issue = [&](const Item &it, bool live) {
         if constexpr (STAGE) {
+            // Only the wavefronts with the light row tiles (the first NL, whose tiles have at
+            // most half of the steps) stream the next item: the heavy tiles' wavefronts go
+            // straight from the barrier to their steps instead of queueing behind the store
+            // traffic at the vector-memory path.
+            constexpr int NL = NW >= 8 ? NW / 2 : NW;
+            if (wave >= NL) return;
             const int lane = (tid & 63) + opaque_zero();
             constexpr int XI = S::SX / 1024, HI = S::SH / 1024, TI = ROWS / 64;
             unsigned char *spare = stg + S::SX + S::SH + S::ST;
             const __amdgpu_buffer_rsrc_t rx = live ? x_rsrc(it) : make_rsrc(x, 0u);
 #pragma unroll
-            for (int k = 0; k < (XI + NW - 1) / NW; ++k) {
-                const int wi = k * NW + wave;
+            for (int k = 0; k < (XI + NL - 1) / NL; ++k) {
+                const int wi = k * NL + wave;
                 const int byte = 1024 * wi + 16 * lane, row = byte / (2 * P), col = byte % (2 * P);
                 buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
                                  (uint32_t)(row * sx * 2 + col));
@@ -163,15 +169,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             const f16 *hen = static_cast<const f16 *>(henv);
             const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + it.bhc * P * N, live ? (uint32_t)S::SH : 0u);
 #pragma unroll
-            for (int k = 0; k < (HI + NW - 1) / NW; ++k) {
-                const int wi = k * NW + wave;
+            for (int k = 0; k < (HI + NL - 1) / NL; ++k) {
+                const int wi = k * NL + wave;
                 buf_load_lds16(wi < HI ? rh : make_rsrc(hen, 0u), wi < HI ? stg + S::SX + 1024 * wi : spare,
                                  (uint32_t)(1024 * wi + 16 * lane));
             }
-            // tables: wavefronts 0 .. TI-1 stream dA_cum, TI .. 2TI-1 stream dt (zeros past Q)
-            {
-                const bool has = live && wave < 2 * TI;
-                const int tab = has ? wave / TI : 0, wi = has ? wave % TI : 0;
+            // tables: slots 0 .. TI-1 stream dA_cum, TI .. 2TI-1 stream dt (zeros past Q)
+#pragma unroll
+            for (int k = 0; k < (2 * TI + NL - 1) / NL; ++k) {
+                const int slot = k * NL + wave;
+                const bool has = live && slot < 2 * TI;
+                const int tab = has ? slot / TI : 0, wi = has ? slot % TI : 0;
                 const float *src = (tab == 0 ? acum : dtc) + it.bhc * Q;
                 const __amdgpu_buffer_rsrc_t rt = make_rsrc(src, has ? (uint32_t)(Q * 4) : 0u);
                 buf_load_lds4(rt, has ? stg + S::SX + S::SH + tab * ROWS * 4 + 256 * wi : spare,
@@ -309,38 +317,39 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         }
     };
 
-    // y of an item is written at the start of the next one, ahead of that item's staging
-    // loads, so that the wait for those loads never waits for the stores
-    // (buffer stores over the item's valid rows, which drop rows past the sequence and
-    // every store of a wavefront without a tile: the store count is the same for all)
+    // The output tile is formed transposed: every product takes X (or the entering state) as
+    // the A operand and the scores (or the C rows) as the B operand, so that lane (li, lg)
+    // holds y[ibase + li][16 pt + 4 lg + r], r = 0..3 -- four consecutive channels of one row,
+    // written with one 16-byte store per channel tile.  y of an item is written when the
+    // wavefront's tile is done, as its youngest memory operations (buffer stores over the
+    // item's valid rows, which drop rows past the sequence and every store of a wavefront
+    // without a tile: every wavefront issues TP of them).
     f32x4 acc[TP];
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();  // (stored, with an empty range, before the first item)
+    for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
+    // s_waitcnt with vmcnt(TP) (expcnt and lgkmcnt left at their maxima): the gfx9 encoding
+    // splits vmcnt over bits 3:0 and 15:14
+    constexpr int kWaitStores = (TP & 15) | (7 << 4) | (15 << 8) | ((TP >> 4) << 14);
     auto store_y = [&](const Item &it, bool live) {
         const int lane = (tid & 63) + opaque_zero(), li = lane & 15, lg = lane >> 4;
         const size_t base = (((size_t)it.b * L + it.tc) * H + it.h) * P;
-        const uint32_t es = OPT && opt.y_bf16 ? 2u : 4u;  // y element size
-        const __amdgpu_buffer_rsrc_t ry =
-            make_rsrc(OPT && opt.y_bf16 ? (void *)(static_cast<uint16_t *>(y) + base) : (void *)(static_cast<float *>(y) + base),
-                      live && t >= 0 ? (uint32_t)(((it.vrows - 1) * H * P + P) * es) : 0u);
-        // Both storage types issue the same 16 dword stores with no branch around them or
-        // around their data (both forms cost a few VALU operations): the waits below count
-        // on that number.  bf16: the even lane of each pair of adjacent columns stores both
-        // values (its neighbour's comes through a lane swap); the odd lane's store goes
-        // past the range and is dropped.
         const bool y16 = OPT && opt.y_bf16;
-        const bool drop = y16 && (li & 1);
+        const uint32_t es = y16 ? 2u : 4u;  // y element size
+        const __amdgpu_buffer_rsrc_t ry =
+            make_rsrc(y16 ? (void *)(static_cast<uint16_t *>(y) + base) : (void *)(static_cast<float *>(y) + base),
+                      live && t >= 0 ? (uint32_t)(((it.vrows - 1) * H * P + P) * es) : 0u);
+        // the lane's four consecutive channels 16 pt + 4 lg .. +3 of row ibase + li: one 16-byte
+        // store (8 bytes for bf16) per channel tile; rows past the sequence fall outside the range
+        const uint32_t e = (uint32_t)((ibase + li) * H * P + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = ibase + 4 * lg + r;
-#pragma unroll
-            for (int pt = 0; pt < TP; ++pt) {
-                // (copied to a scalar first: a bit cast of the vector element itself reads element 0)
-                const float v = acc[pt][r];
-                uint32_t data = __float_as_uint(v);
-                if constexpr (OPT) data = y16 ? pack_bf16x2(v, swap_adjacent_lanes(v)) : data;
-                const uint32_t e = (uint32_t)(row * H * P + pt * 16 + li);
-                __builtin_amdgcn_raw_buffer_store_b32(data, ry, (int)(drop ? 0x7ffffff0u : es * e), 0, 0);
+        for (int pt = 0; pt < TP; ++pt) {
+            if (y16) {
+                const uint2 d = {pack_bf16x2(acc[pt][0], acc[pt][1]), pack_bf16x2(acc[pt][2], acc[pt][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, d), ry,
+                                                      (int)(2u * (e + 16 * pt)), 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, acc[pt]), ry,
+                                                       (int)(4u * (e + 16 * pt)), 0, 0);
             }
         }
     };
@@ -358,18 +367,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     const int per = nitems / nwg, extra = nitems % nwg;
     int item = vw * per + min(vw, extra);
     const int last = item + per + (vw < extra ? 1 : 0);
-    Item cur = decode(item), prev = cur;
+    Item cur = decode(item);
     stage_issue(cur, true);
     load_tile_operands(cur);
-    for (bool first = true;; first = false) {
+    store_y(cur, false);  // empty range: the same youngest operations as every later item sees
+    for (;;) {
         const float Dh = D ? D[cur.h] : 0.f;
-        // The item's staged loads have landed (they may be the youngest memory operations:
-        // the tile operand loads that follow them are conditional) ...
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-        __syncthreads();  // ... and the previous item's readers are done
+        // Every memory operation but this wavefront's y stores of the previous item (its TP
+        // youngest) has completed: the item's staged loads have landed, and so have the tile
+        // operand loads issued before those stores.  The stores drain during this item.
+        __builtin_amdgcn_s_waitcnt(kWaitStores);
+        __syncthreads();  // ... and every wavefront's staged loads have landed; the previous item's readers are done
         stage_commit(cur);
         __syncthreads();
-        store_y(prev, !first);
         const int next = item + 1;
         const bool more = next < last;
         const Item nx = more ? decode(next) : cur;
@@ -398,25 +408,25 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
                     for (int pt = 0; pt < TP; ++pt) {
                         if constexpr (F32) {
-                            acc[pt] = mfma16x16x4_f32(cf[ks], hp[(pt * 16 + li) * N + ks * 4 + lg], acc[pt]);
+                            acc[pt] = mfma16x16x4_f32(hp[(pt * 16 + li) * N + ks * 4 + lg], cf[ks], acc[pt]);
                         } else {
                             const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
-                            acc[pt] = mfma16x16x32_f16(__builtin_bit_cast(f16x8, cb[ks]), hf, acc[pt]);
+                            acc[pt] = mfma16x16x32_f16(hf, __builtin_bit_cast(f16x8, cb[ks]), acc[pt]);
                         }
                     }
                 }
+                const float e = __builtin_amdgcn_exp2f(ai);  // the lane's row: exp(a_i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(acs[ibase + 4 * lg + r]);
+                for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
-                    for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= e;
-                }
+                    for (int r = 0; r < 4; ++r) acc[pt][r] *= e;
             }
             // ---- Step-1: the causal 32-column steps of this row tile.  All but the last lie
             // strictly below the diagonal; the last one holds it (tile t: steps 0 .. t/2).
             const size_t slice0 = (((size_t)cur.b * G + cur.g) * nc + cur.c) * (size_t)spc + Tt;
             const float *gf = static_cast<const float *>(cbg) + (slice0 * 64 + lane) * 8;
-            // Lane holds G[irow][jb + 4 lg + r] (d0) and G[irow][jb + 16 + 4 lg + r] (d1).
+            // Lane holds G[irow][jb + 4 lg + r] (d0) and G[irow][jb + 16 + 4 lg + r] (d1): the B
+            // operand of the transposed product, column irow of the score tile.
             auto slice = [&](int s, float d0[4], float d1[4]) {
                 if constexpr (F32) {
                     const float4 g0 = reinterpret_cast<const float4 *>(gf + (size_t)s * 512)[0];
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                         const f16x4 lo = lds_read_tr16(&xs[ox]);
                         const f16x4 hi = lds_read_tr16(&xs[ox + 16 * LDX]);
                         const f16x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        acc[pt] = mfma16x16x32_f16(a, bx, acc[pt]);
+                        acc[pt] = mfma16x16x32_f16(bx, a, acc[pt]);
                     }
                 }
             };
@@ -446,10 +456,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                     for (int pt = 0; pt < TP; ++pt) {
                         const op_t *xr = &xs[(pt * 16 + li) * LDX + jb + 4 * lg];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[pt] = mfma16x16x4_f32(r0[r], xr[r], acc[pt]);
+                        for (int r = 0; r < 4; ++r) acc[pt] = mfma16x16x4_f32(xr[r], r0[r], acc[pt]);
                         if (has1) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[pt] = mfma16x16x4_f32(r1[r], xr[16 + r], acc[pt]);
+                            for (int r = 0; r < 4; ++r) acc[pt] = mfma16x16x4_f32(xr[16 + r], r1[r], acc[pt]);
                         }
                     }
                 } else {
@@ -528,13 +538,13 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * xs[(pt * 16 + li) * LDX + ibase + 4 * lg + r];
+                    for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * xs[(pt * 16 + 4 * lg + r) * LDX + irow];
             } else {
-                // the transposing read hands lane li the values X[ibase + 4 lg + r][16 pt + li],
-                // exactly the accumulator positions (exact for bf16 inputs in fp16 range)
+                // the lane's four channels of its row, one 8-byte read (exact for bf16 inputs in
+                // fp16 range)
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) {
-                    const f16x4 xv = lds_read_tr16(&xs[tr16_offset(lane, ibase, pt * 16, LDX)]);
+                    const f16x4 xv = *reinterpret_cast<const f16x4 *>(&xs[irow * LDX + pt * 16 + 4 * lg]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * static_cast<float>(xv[r]);
                 }
@@ -550,7 +560,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) {
-                    const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * sz + pt * 16 + li);
+                    const uint32_t e = (uint32_t)((ibase + li) * sz + pt * 16 + 4 * lg + r);
                     if constexpr (F32)
                         zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)(4u * e), 0, 0);
                     else
@@ -567,12 +577,13 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         // the next item's tile operands when its chunk or group differs, in flight while its
         // staging completes
         if (more && (nx.c != cur.c || nx.b != cur.b || nx.g != cur.g)) load_tile_operands(nx);
-        prev = cur;
+        // y last: a wavefront's stores go out when its own tile is done (the light tiles'
+        // first), after every load that the next item's wait must see completed
+        store_y(cur, true);
         if (!more) break;
         item = next;
         cur = nx;
     }
-    store_y(prev, true);
 }
 
 template <typename TIn, int P>
