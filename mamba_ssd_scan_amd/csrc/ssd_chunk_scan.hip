@@ -31,6 +31,7 @@
 // the token, is read with the transposing LDS read.  fp32 inputs store X transposed and run
 // the fp32 matrix path.  Columns above the diagonal are skipped.
 #include <atomic>
+#include <type_traits>
 
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -586,6 +587,347 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     }
 }
 
+// ---- The pipelined chunk scan (bf16 inputs, P = 64, N = 128, 256-token chunks): the same
+// arithmetic in the same order as chunk_scan_kernel (the compiler may contract the decay
+// table's multiply-add differently, a last-bit difference in a few table entries), with one
+// barrier per item instead of two.  The compute layout is double-buffered: while every
+// wavefront forms item k from one buffer set, the wavefronts with the light row tiles (the
+// first eight, whose tiles have at most four 32-column steps) stream item k+1 with
+// direct-to-LDS loads -- X rows raw into a staging area, the fp16 entering state straight
+// into the other set's padded rows (one 256-byte row per load), the decay tables raw -- and,
+// once their own tile is done, convert the X rows and tables they loaded themselves into the
+// other set.  The heavy tiles' wavefronts only compute and store.  Each buffer set is its own
+// LDS array and the set an item uses is fixed at compile time (the item loop is unrolled by
+// two), so the compiler can tell the loads in flight from the reads of the current set.
+template <int P, int N, int NW> struct PipeLds {
+    static constexpr int ROWS = 16 * NW, LDX = P + 16, LDH = N + 8, TAB = ROWS + 32;
+    static constexpr int XS = ROWS * LDX, HS = P * LDH;           // halves per set
+    static constexpr int SX = ROWS * P * 2, ST = 2 * ROWS * 4;    // raw X rows, raw tables
+    static constexpr int bytes = 2 * (XS * 2 + HS * 2 + TAB * (4 + 4 + 2)) + SX + ST;
+    static constexpr bool fits = bytes <= 160 * 1024;
+};
+
+template <int P, int N, int NW, bool OPT>
+__global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
+    const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
+    const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sz,
+    int Q, int nc, int nitems)
+{
+    typedef PipeLds<P, N, NW> S;
+    constexpr int ROWS = S::ROWS, LDX = S::LDX, LDH = S::LDH, TAB = S::TAB;
+    constexpr int TP = P / 16, KS = N / 32, NSMAX = NW / 2;
+    constexpr int NL = NW / 2;            // streaming wavefronts: the light row tiles
+    constexpr int XI = S::SX / 1024;      // 1 KB X slots; wavefront q owns slots q, q + NL, ...
+    constexpr int TI = ROWS / 64;         // 64-row table blocks; wavefront q < TI owns block q
+    static_assert(NW == 16 && 2 * N == 256 && XI % NL == 0 && P % NL == 0 && TI <= NL, "pipelined scan shape");
+    __shared__ __align__(16) f16 xs0[S::XS];
+    __shared__ __align__(16) f16 xs1[S::XS];
+    __shared__ __align__(16) f16 hs0[S::HS];
+    __shared__ __align__(16) f16 hs1[S::HS];
+    __shared__ __align__(16) float acs0[TAB];
+    __shared__ __align__(16) float acs1[TAB];
+    __shared__ __align__(16) float dts0[TAB];
+    __shared__ __align__(16) float dts1[TAB];
+    __shared__ __align__(16) f16 ech0[TAB];
+    __shared__ __align__(16) f16 ech1[TAB];
+    __shared__ __align__(16) unsigned char stg[S::SX + S::ST];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    // row tile: the k-th wavefront on SIMD s (wave = 4k + s) takes tile 8(k/2) + s for even k
+    // and 8(k/2) + 7 - s for odd k (tiles 0..7 for the first eight wavefronts)
+    const int t = [&] {
+        const int s = wave & 3, k = wave >> 2;
+        return 8 * (k >> 1) + ((k & 1) ? 7 - s : s);
+    }();
+    const int ibase = 16 * t;
+    const int ns = (ibase + 15) / 32 + 1;  // 32-column steps up to the diagonal
+    const int nt = Q >> 4;
+    const int spc = (nt >> 1) * ((nt >> 1) + 1);
+    const int Tt = (t & 1) ? ((t >> 1) + 1) * ((t >> 1) + 1) : (t >> 1) * ((t >> 1) + 1);
+    const bool light = wave < NL;
+
+    auto opaque_zero = [] {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        return z;
+    };
+    struct Item {
+        int c, h, b, g, vrows;
+        size_t bhc;
+        long tc;
+    };
+    auto decode = [&](int item) __attribute__((always_inline)) {
+        Item it;
+        it.h = item % H;
+        it.c = (item / H) % nc;
+        it.b = item / (nc * H);
+        it.g = it.h / (H / G);
+        it.bhc = ((size_t)it.b * H + it.h) * nc + it.c;
+        it.tc = (long)it.c * Q;
+        it.vrows = (int)((L - it.tc) < Q ? (L - it.tc) : Q);
+        return it;
+    };
+
+    // the table rows past the chunk (read, always masked or zero-weighted, by the last steps)
+    if (tid < TAB - ROWS) {
+        acs0[ROWS + tid] = 0.f;
+        acs1[ROWS + tid] = 0.f;
+        dts0[ROWS + tid] = 0.f;
+        dts1[ROWS + tid] = 0.f;
+        ech0[ROWS + tid] = static_cast<f16>(0.f);
+        ech1[ROWS + tid] = static_cast<f16>(0.f);
+    }
+
+    // ---- streaming (light wavefronts): X rows raw into the staging slots this wavefront
+    // owns, the entering state's rows straight into the next set, and (the first TI) the raw
+    // dA_cum / dt block they own.  live == false: empty ranges (nothing is read).
+    auto stream = [&](const Item &it, bool live, f16 *hsn) __attribute__((always_inline)) {
+        const int ln = lane + opaque_zero();
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(x + ((size_t)it.b * L + it.tc) * sx + (size_t)it.h * P,
+                      live ? (uint32_t)(((it.vrows - 1) * sx + P) * 2) : 0u);
+#pragma unroll
+        for (int k = 0; k < XI / NL; ++k) {
+            const int wi = k * NL + wave;
+            const int byte = 1024 * wi + 16 * ln, row = byte / (2 * P), col = byte % (2 * P);
+            buf_load_lds16(rx, stg + 1024 * wi, (uint32_t)(row * sx * 2 + col));
+        }
+        const __amdgpu_buffer_rsrc_t rh =
+            make_rsrc(static_cast<const f16 *>(henv) + it.bhc * P * N, live ? (uint32_t)(P * N * 2) : 0u);
+#pragma unroll
+        for (int k = 0; k < P / NL; ++k) {
+            const int p = k * NL + wave;
+            buf_load_lds4(rh, hsn + p * LDH, (uint32_t)(p * N * 2 + 4 * ln));
+        }
+        if (wave < TI) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(acum + it.bhc * Q, live ? (uint32_t)(Q * 4) : 0u);
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(dtc + it.bhc * Q, live ? (uint32_t)(Q * 4) : 0u);
+            buf_load_lds4(ra, stg + S::SX + 256 * wave, (uint32_t)(4 * (64 * wave + ln)));
+            buf_load_lds4(rd, stg + S::SX + ROWS * 4 + 256 * wave, (uint32_t)(4 * (64 * wave + ln)));
+        }
+    };
+    // ---- conversion (light wavefronts, after their own loads have landed): the X rows of the
+    // slots they own to fp16, and the tables of the block they own
+    auto convert = [&](f16 *xsn, float *acsn, float *dtsn, f16 *echn) __attribute__((always_inline)) {
+        const int ln = lane + opaque_zero();
+#pragma unroll
+        for (int k = 0; k < XI / NL; ++k) {
+            const int u = 64 * (k * NL + wave) + ln;  // 16-byte unit: row u / (P / 8), channels 8 (u % (P / 8))
+            Raw8<bf16_t> r;
+            r.v = *reinterpret_cast<const uint4 *>(stg + 16 * u);
+            *reinterpret_cast<uint4 *>(&xsn[(u / (P / 8)) * LDX + 8 * (u % (P / 8))]) = raw8_to_f16x8(r);
+        }
+        if (wave < TI) {
+            const float *sta = reinterpret_cast<const float *>(stg + S::SX);
+            const float *std_ = reinterpret_cast<const float *>(stg + S::SX + ROWS * 4);
+            const int j = 64 * wave + ln;
+            float a = 0.f, d = 0.f, e = 0.f;
+            if (j < Q) {
+                const int ir = min(32 * (j >> 5) + 31, Q - 1);
+                a = sta[j] * kLog2e;
+                d = std_[j];
+                e = __builtin_amdgcn_exp2f(sta[ir] * kLog2e - a) * d;
+            }
+            acsn[j] = a;
+            dtsn[j] = d;
+            echn[j] = static_cast<f16>(e);
+        }
+    };
+
+    // ---- tile operands in registers, kept while the chunk and group stay the same
+    bf16x8 cb[KS];  // bf16 as loaded; fp16 bit patterns once converted (cfresh false)
+    f16x8 gs[NSMAX - 1];
+    f16x8 gdg;
+    bool cfresh = false;
+    auto load_tile_operands = [&](const Item &it) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * sbc + (size_t)it.g * N,
+                                                    (uint32_t)(((it.vrows - 1) * sbc + N) * 2));
+        const uint32_t row = (uint32_t)((ibase + li) * sbc);
+        const size_t slice0 = (((size_t)it.b * G + it.g) * nc + it.c) * (size_t)spc + Tt;
+        const f16 *gq = static_cast<const f16 *>(cbg) + (slice0 * 64 + lane) * 8;
+        const int slast = ns - 1;
+#pragma unroll
+        for (int s = 0; s < NSMAX - 1; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
+        gdg = *reinterpret_cast<const f16x8 *>(gq + (size_t)slast * 512);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+        cfresh = true;
+    };
+
+    // ---- the output tile, transposed (lane (li, lg) holds y[ibase + li][16 pt + 4 lg + r]),
+    // stored when the wavefront's tile is done, as its TP youngest memory operations
+    f32x4 acc[TP];
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
+    constexpr int kWaitStores = (TP & 15) | (7 << 4) | (15 << 8) | ((TP >> 4) << 14);  // vmcnt(TP)
+    auto store_y = [&](const Item &it, bool live) __attribute__((always_inline)) {
+        const int ln = lane + opaque_zero(), lli = ln & 15, llg = ln >> 4;
+        const size_t base = (((size_t)it.b * L + it.tc) * H + it.h) * P;
+        const bool y16 = OPT && opt.y_bf16;
+        const uint32_t es = y16 ? 2u : 4u;
+        const __amdgpu_buffer_rsrc_t ry =
+            make_rsrc(y16 ? (void *)(static_cast<uint16_t *>(y) + base) : (void *)(static_cast<float *>(y) + base),
+                      live ? (uint32_t)(((it.vrows - 1) * H * P + P) * es) : 0u);
+        const uint32_t e = (uint32_t)((ibase + lli) * H * P + 4 * llg);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+            if (y16) {
+                const uint2 d = {pack_bf16x2(acc[pt][0], acc[pt][1]), pack_bf16x2(acc[pt][2], acc[pt][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, d), ry,
+                                                      (int)(2u * (e + 16 * pt)), 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, acc[pt]),
+                                                       ry, (int)(4u * (e + 16 * pt)), 0, 0);
+            }
+        }
+    };
+
+    // ---- one item from one buffer set: Step-4, Step-1 (off-diagonal steps, diagonal step),
+    // skip term, optional gate -- chunk_scan_kernel's bf16 arithmetic
+    auto compute = [&](const Item &cur, const f16 *xs, const f16 *hs, const float *acs, const float *dts,
+                       const f16 *ech) __attribute__((always_inline)) {
+        const float Dh = D ? D[cur.h] : 0.f;
+        const int irow = ibase + li;
+        const float ai = acs[irow];
+        if (cfresh) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(cb[ks]));
+            cfresh = false;
+        }
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) acc[pt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int pt = 0; pt < TP; ++pt) {
+                const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
+                acc[pt] = mfma16x16x32_f16(hf, __builtin_bit_cast(f16x8, cb[ks]), acc[pt]);
+            }
+        }
+        {
+            const float e = __builtin_amdgcn_exp2f(ai);
+#pragma unroll
+            for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pt][r] *= e;
+        }
+        auto gemm2h = [&](int jb, const f16x8 &a) __attribute__((always_inline)) {
+#pragma unroll
+            for (int pt = 0; pt < TP; ++pt) {
+                const int ox = tr16_offset(lane, jb, pt * 16, LDX);
+                const f16x4 lo = lds_read_tr16(&xs[ox]);
+                const f16x4 hi = lds_read_tr16(&xs[ox + 16 * LDX]);
+                const f16x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[pt] = mfma16x16x32_f16(bx, a, acc[pt]);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s + 1 < NSMAX; ++s) {
+            if (s + 1 < ns) {
+                const int jb = 32 * s;
+                const float er = __builtin_amdgcn_exp2f(ai - acs[jb + 31]);
+                const f16x4 e0 = *reinterpret_cast<const f16x4 *>(&ech[jb + 4 * lg]);
+                const f16x4 e1 = *reinterpret_cast<const f16x4 *>(&ech[jb + 16 + 4 * lg]);
+                const f16x8 ej = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+                gemm2h(jb, gs[s] * (ej * static_cast<f16>(er)));
+            }
+        }
+        {
+            const int jb = 32 * (ns - 1);
+            const bool has1 = jb + 16 <= ibase + 15;
+            float d0[4], d1[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                d0[r] = static_cast<float>(gdg[r]);
+                d1[r] = static_cast<float>(gdg[4 + r]);
+            }
+            const float4 a0v = *reinterpret_cast<const float4 *>(&acs[jb + 4 * lg]);
+            const float4 t0v = *reinterpret_cast<const float4 *>(&dts[jb + 4 * lg]);
+            const float4 a1v = *reinterpret_cast<const float4 *>(&acs[jb + 16 + 4 * lg]);
+            const float4 t1v = *reinterpret_cast<const float4 *>(&dts[jb + 16 + 4 * lg]);
+            const float aj0[4] = {a0v.x, a0v.y, a0v.z, a0v.w}, tj0[4] = {t0v.x, t0v.y, t0v.z, t0v.w};
+            const float aj1[4] = {a1v.x, a1v.y, a1v.z, a1v.w}, tj1[4] = {t1v.x, t1v.y, t1v.z, t1v.w};
+            f16x8 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float r0 = (jb + 4 * lg + r <= irow) ? d0[r] * __builtin_amdgcn_exp2f(ai - aj0[r]) * tj0[r] : 0.f;
+                const float r1 =
+                    (has1 && jb + 16 + 4 * lg + r <= irow) ? d1[r] * __builtin_amdgcn_exp2f(ai - aj1[r]) * tj1[r] : 0.f;
+                a[r] = static_cast<f16>(r0);
+                a[4 + r] = static_cast<f16>(r1);
+            }
+            gemm2h(jb, a);
+        }
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+            const f16x4 xv = *reinterpret_cast<const f16x4 *>(&xs[irow * LDX + pt * 16 + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * static_cast<float>(xv[r]);
+        }
+        if (OPT && opt.z) {
+            const bf16_t *zp = static_cast<const bf16_t *>(opt.z) + ((size_t)cur.b * L + cur.tc) * sz + (size_t)cur.h * P;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * sz + P) * 2));
+            uint32_t zr[TP][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt)
+                    zr[pt][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rz, (int)(2u * (uint32_t)((ibase + li) * sz + pt * 16 + 4 * lg + r)), 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= silu(__uint_as_float(zr[pt][r] << 16));
+        }
+    };
+
+    // ---- the run of items (contiguous, heads of a chunk in a row, XCD-adjacent runs)
+    const int nwg = gridDim.x;
+    const int vw = (nwg & 7) == 0 ? (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int per = nitems / nwg, extra = nitems % nwg;
+    int item = vw * per + min(vw, extra);
+    const int last = item + per + (vw < extra ? 1 : 0);
+    Item cur = decode(item);
+    if (light) {
+        stream(cur, true, hs0);
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's loads have landed
+        convert(xs0, acs0, dts0, ech0);
+    }
+    load_tile_operands(cur);
+    store_y(cur, false);  // empty range: the same youngest operations as every later item leaves
+    __builtin_amdgcn_s_waitcnt(kWaitStores);
+    __syncthreads();
+    auto body = [&](auto parity) __attribute__((always_inline)) {
+        constexpr bool ODD = decltype(parity)::value;
+        const bool more = item + 1 < last;
+        const Item nx = more ? decode(item + 1) : cur;
+        if (light) stream(nx, more, ODD ? hs0 : hs1);
+        compute(cur, ODD ? xs1 : xs0, ODD ? hs1 : hs0, ODD ? acs1 : acs0, ODD ? dts1 : dts0, ODD ? ech1 : ech0);
+        if (light) {
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's loads of the next item have landed
+            convert(ODD ? xs0 : xs1, ODD ? acs0 : acs1, ODD ? dts0 : dts1, ODD ? ech0 : ech1);
+        }
+        if (more && (nx.c != cur.c || nx.b != cur.b || nx.g != cur.g)) load_tile_operands(nx);
+        store_y(cur, true);
+        // everything but the y stores has completed: the next set is converted and the tile
+        // operands are in; the barrier hands the set over and retires this one
+        __builtin_amdgcn_s_waitcnt(kWaitStores);
+        __syncthreads();
+        if (more) {
+            ++item;
+            cur = nx;
+        }
+        return more;
+    };
+    for (;;) {
+        if (!body(std::integral_constant<bool, false>{})) break;
+        if (!body(std::integral_constant<bool, true>{})) break;
+    }
+}
+
 template <typename TIn, int P>
 static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, const float *acum,
                                 const float *dtc, const void *hen, const float *D, void *y,
@@ -595,6 +937,22 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
     // its run of (b, c, h) items
     const int nitems = d.nc * d.H * d.B;
     const TIn *xx = static_cast<const TIn *>(x), *cc = static_cast<const TIn *>(Cm);
+    // bf16, P = 64, N = 128, 256-token chunks: the pipelined kernel, one workgroup per CU
+    if constexpr (std::is_same<TIn, bf16_t>::value && P == 64) {
+        if (d.N == 128 && d.Q == 256) {
+            static_assert(PipeLds<64, 128, 16>::fits, "pipelined chunk scan LDS");
+            const int nwg = nitems < ncu ? nitems : ncu;
+            if (o.z || o.y_bf16)
+                chunk_scan_pipe_kernel<64, 128, 16, true><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L,
+                                                                              d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc,
+                                                                              nitems);
+            else
+                chunk_scan_pipe_kernel<64, 128, 16, false><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L,
+                                                                               d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc,
+                                                                               nitems);
+            return hipGetLastError();
+        }
+    }
     // up to 16 wavefronts per compute unit, as many workgroups as the LDS holds
 #define SSD_SCAN_LAUNCH(NN, NWV)                                                                          \
     do {                                                                                                  \
