@@ -38,7 +38,8 @@ EXTRA_WORKLOADS = (1, 2)          # also timed, each with its own roofline
 DECODE_WORKLOAD = 4
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_state_kernel": "ssd_chunk_state.hip",
+    "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_scan_pipe_kernel": "ssd_chunk_scan.hip",
+    "chunk_state_kernel": "ssd_chunk_state.hip",
     "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
     "step_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
     "chunk_scan_small_kernel": "ssd_chunk_scan_small.hip", "chunk_state_pair_kernel": "ssd_chunk_state_pair.hip",
@@ -49,14 +50,18 @@ KERNEL_SOURCES = {
 def scan_kernel_name(s, ncu=None) -> str:
     """The chunk-scan kernel the library launches for this shape: the one-round kernel when
     every (b, h, chunk) item fits at two per compute unit (bf16, 256-token chunks, P = 64),
-    else the persistent one (the same rule as the library's launcher).  ncu: compute units
-    (default: the current device's)."""
+    else the pipelined persistent one (bf16, 256-token chunks, P = 64, N = 128) or the
+    persistent one (the same rule as the library's launcher).  ncu: compute units (default:
+    the current device's)."""
     if ncu is None:
         import torch
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
     nitems = s.batch * s.nheads * -(-s.seqlen // s.chunk)
     small = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and nitems <= 2 * ncu
-    return "chunk_scan_small_kernel" if small else "chunk_scan_kernel"
+    if small:
+        return "chunk_scan_small_kernel"
+    pipe = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and s.dstate == 128
+    return "chunk_scan_pipe_kernel" if pipe else "chunk_scan_kernel"
 
 
 def passing_in_scan(s, ncu=None) -> bool:
@@ -116,7 +121,8 @@ def alg_counts(s: synth.PrefillShape, ncu=None) -> dict:
         "chunk_scan_kernel": dict(bytes=x + bc + cb + chunk_tab + hen + y,
                                   flops=B * nc * H * P * tri + 2 * B * H * L * P * N),
     }
-    k["chunk_scan_small_kernel"] = k["chunk_scan_kernel"]
+    k["chunk_scan_small_kernel"] = dict(k["chunk_scan_kernel"])
+    k["chunk_scan_pipe_kernel"] = dict(k["chunk_scan_kernel"])
     # the prefill's fused first launch: dt in, dA_cum / dt_c and the chunk states out, and
     # the GEMM1 products (B and C in, cb out); x and B are read once
     k["chunk_state_pair_kernel"] = dict(bytes=x + dt + 2 * bc + chunk_tab + states + cb,
@@ -138,6 +144,7 @@ def alg_counts(s: synth.PrefillShape, ncu=None) -> dict:
         "state_passing_kernel": h0 + st,
         "chunk_gemm1_kernel": 2 * bc,
         "chunk_scan_kernel": x + bc + y,
+        "chunk_scan_pipe_kernel": x + bc + y,
         "chunk_scan_small_kernel": x + bc + y + (h0 + st if passing_in_scan(s, ncu) else 0),
     }
     for name, b in method.items():
@@ -609,7 +616,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
-    ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_state_kernel", "state_passing_kernel",
+    ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_scan_pipe_kernel", "chunk_state_kernel", "state_passing_kernel",
                                        "chunk_cumsum_kernel", "chunk_gemm1_kernel", "chunk_scan_small_kernel",
                                        "single_pass", "step", "cached", "copy"],
                     help="profiling aid: launch only this work --steps times (cold), print nothing else")

@@ -31,7 +31,7 @@ def test_launches_of_the_benchmarked_prefill():
 @pytest.mark.parametrize("w,expect", [
     (0, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # fp32, Q = 64
     (2, ["chunk_state_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # Q = 64
-    (3, ["chunk_state_pair_kernel", "state_passing_kernel", "chunk_scan_kernel"]),  # 5120 items
+    (3, ["chunk_state_pair_kernel", "state_passing_kernel", "chunk_scan_pipe_kernel"]),  # 5120 items
 ])
 def test_launches_of_the_other_workloads(w, expect):
     assert bench.step_kernels(synth.WORKLOADS[w], NCU) == expect
@@ -42,8 +42,10 @@ def test_launch_rules_at_their_edges():
     s = _shape(1, 21 * 256 - 5, 24, 1)
     assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "state_passing_kernel",
                                           "chunk_scan_small_kernel"]
-    # 513 items: the persistent scan
-    assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1), NCU) == "chunk_scan_kernel"
+    # 513 items: the persistent scan, pipelined at N = 128 and P = 64
+    assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1), NCU) == "chunk_scan_pipe_kernel"
+    assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1, N=64), NCU) == "chunk_scan_kernel"
+    assert bench.scan_kernel_name(_shape(1, 19 * 256, 27, 1, P=128), NCU) == "chunk_scan_kernel"
     assert bench.scan_kernel_name(_shape(1, 16 * 256, 32, 1), NCU) == "chunk_scan_small_kernel"  # 512 items
     # an odd number of heads per group keeps one head per workgroup
     assert not bench.chunk_state_pair(_shape(1, 12 * 256 - 100, 25, 5))
@@ -76,7 +78,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_method_bytes_of_the_headline_prefill():
     """The 2.7B-shaped 16384-token layer: the method's own bytes per step (inputs, y, initial
-    and final state) are the 519.6 MB of the roofline floor; the persistent chunk scan's share is
+    and final state) are the 519.6 MB of the roofline floor; the pipelined chunk scan's share is
     x + C + y, without the entering states and GEMM1 products it also reads."""
     s = synth.WORKLOADS[3]
     c = bench.alg_counts(s, NCU)
@@ -84,8 +86,8 @@ def test_method_bytes_of_the_headline_prefill():
     x, dt, bc, y, st = L * H * P * 2, L * H * 2, L * N * 2, L * H * P * 4, H * P * N * 4
     assert c["fused_bytes"] == x + dt + 2 * bc + y + 2 * st == 519569408
     k = c["kernels"]
-    assert k["chunk_scan_kernel"]["method_bytes"] == x + bc + y
-    assert k["chunk_scan_kernel"]["bytes"] > k["chunk_scan_kernel"]["method_bytes"]
+    assert k["chunk_scan_pipe_kernel"]["method_bytes"] == x + bc + y
+    assert k["chunk_scan_pipe_kernel"]["bytes"] > k["chunk_scan_pipe_kernel"]["method_bytes"]
     assert k["chunk_state_pair_kernel"]["method_bytes"] == x + dt + 2 * bc
     assert k["state_passing_kernel"]["method_bytes"] == 2 * st
-    assert bench.step_kernels(s, NCU)[-1] == "chunk_scan_kernel"
+    assert bench.step_kernels(s, NCU)[-1] == "chunk_scan_pipe_kernel"
