@@ -607,7 +607,9 @@ template <int P, int N, int NW> struct PipeLds {
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
-template <int P, int N, int NW, bool OPT>
+// GATE: the z gate is applied; Y16: y is stored as bf16.  Each combination is its own
+// instantiation, so the plain and the bf16-y kernels carry no registers for the gate.
+template <int P, int N, int NW, bool GATE, bool Y16>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
@@ -766,15 +768,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
     auto store_y = [&](const Item &it, bool live) __attribute__((always_inline)) {
         const int ln = lane + opaque_zero(), lli = ln & 15, llg = ln >> 4;
         const size_t base = (((size_t)it.b * L + it.tc) * H + it.h) * P;
-        const bool y16 = OPT && opt.y_bf16;
-        const uint32_t es = y16 ? 2u : 4u;
+        constexpr bool y16 = Y16;
+        constexpr uint32_t es = y16 ? 2u : 4u;
         const __amdgpu_buffer_rsrc_t ry =
             make_rsrc(y16 ? (void *)(static_cast<uint16_t *>(y) + base) : (void *)(static_cast<float *>(y) + base),
                       live ? (uint32_t)(((it.vrows - 1) * H * P + P) * es) : 0u);
         const uint32_t e = (uint32_t)((ibase + lli) * H * P + 4 * llg);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-            if (y16) {
+            if constexpr (y16) {
                 const uint2 d = {pack_bf16x2(acc[pt][0], acc[pt][1]), pack_bf16x2(acc[pt][2], acc[pt][3])};
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, d), ry,
                                                       (int)(2u * (e + 16 * pt)), 0, 0);
@@ -867,7 +869,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[pt][r] += Dh * static_cast<float>(xv[r]);
         }
-        if (OPT && opt.z) {
+        if constexpr (GATE) {
             const bf16_t *zp = static_cast<const bf16_t *>(opt.z) + ((size_t)cur.b * L + cur.tc) * sz + (size_t)cur.h * P;
             const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * sz + P) * 2));
             uint32_t zr[TP][4];
@@ -942,14 +944,18 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
         if (d.N == 128 && d.Q == 256) {
             static_assert(PipeLds<64, 128, 16>::fits, "pipelined chunk scan LDS");
             const int nwg = nitems < ncu ? nitems : ncu;
-            if (o.z || o.y_bf16)
-                chunk_scan_pipe_kernel<64, 128, 16, true><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L,
-                                                                              d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc,
-                                                                              nitems);
+#define SSD_PIPE_LAUNCH(GT, YB)                                                                          \
+    chunk_scan_pipe_kernel<64, 128, 16, GT, YB><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L, d.H, \
+                                                                     d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
+            if (o.z && o.y_bf16)
+                SSD_PIPE_LAUNCH(true, true);
+            else if (o.z)
+                SSD_PIPE_LAUNCH(true, false);
+            else if (o.y_bf16)
+                SSD_PIPE_LAUNCH(false, true);
             else
-                chunk_scan_pipe_kernel<64, 128, 16, false><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L,
-                                                                               d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc,
-                                                                               nitems);
+                SSD_PIPE_LAUNCH(false, false);
+#undef SSD_PIPE_LAUNCH
             return hipGetLastError();
         }
     }
