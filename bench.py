@@ -41,7 +41,7 @@ KERNEL_SOURCES = {
     "chunk_scan_kernel": "ssd_chunk_scan.hip", "chunk_scan_pipe_kernel": "ssd_chunk_scan.hip",
     "chunk_state_kernel": "ssd_chunk_state.hip",
     "state_passing_kernel": "ssd_state_passing.hip", "chunk_cumsum_kernel": "ssd_cumsum.hip",
-    "step_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
+    "step_kernel": "ssd_step.hip", "step_heads_kernel": "ssd_step.hip", "chunk_gemm1_kernel": "ssd_chunk_gemm1.hip",
     "chunk_scan_small_kernel": "ssd_chunk_scan_small.hip", "chunk_state_pair_kernel": "ssd_chunk_state_pair.hip",
     "chunk_fused_kernel": "ssd_prefill_fused.hip", "fused_prep_kernel": "ssd_prefill_fused.hip",
 }
@@ -403,7 +403,8 @@ def bench_decode(torch, steps, flush):
     us_graph = time_back_to_back(torch, graph.launch, 3) / steps
     graph.close()
     nbytes = decode_bytes_per_step(s)
-    traffic = counter_traffic("step_kernel", synth.WORKLOAD_NAMES[DECODE_WORKLOAD])
+    # the batch-64 x 80-head step runs one workgroup per head (step_heads_kernel)
+    traffic = counter_traffic("step_heads_kernel", synth.WORKLOAD_NAMES[DECODE_WORKLOAD])
     return {
         "counter_traffic_bytes_per_step": traffic,
         "workload": synth.WORKLOAD_NAMES[DECODE_WORKLOAD], "steps": steps,
