@@ -4,13 +4,15 @@ One step = one full chunked prefill (every prefill stage: cumulative decay, chun
 inter-chunk state passing, intra-chunk + off-diagonal output) over the Mamba-2-2.7B-shaped
 long-context layer (batch 1, 16384 tokens, 80 heads, headdim 64, d_state 128, chunk 256,
 bf16 inputs, fp32 state and output, random initial state), with inputs resident in HBM.
-Each timed step starts cold: a 512 MiB read evicts the 256 MiB Infinity Cache and the L2s
-first, outside the timed events.  The 130M- and 370M-shaped layers are timed the same way
-and reported under "workloads"; the decode update (batch 64, 80 heads, 1024 tokens) under
-"decode".
+The timed steps run back to back, rotating over copies of the buffers that together span
+over 1 GiB (4x the 256 MiB Infinity Cache), so that no step finds its data in that cache
+from the step before; one marker pair brackets the block.  Each step goes through
+ssd_prefill_timed, which binds HIP events to every kernel launch itself (the kernel's own
+start and end, no marker between launches): the per-kernel durations and the roofline come
+from them.  The 130M- and 370M-shaped layers are timed the same way and reported under
+"workloads"; the decode update (batch 64, 80 heads, 1024 tokens) under "decode".
 
-Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on the stream
-the kernels run on.  The oracle (fp64 CPU recurrence) is timed on the host's cores on the
+Prints ONE JSON line.  The oracle (fp64 CPU recurrence) is timed on the host's cores on the
 same workload as "cpu_baseline".
 """
 from __future__ import annotations
@@ -216,55 +218,125 @@ def settle_clocks(torch, flush, seconds=0.3):
         torch.cuda.synchronize()
 
 
-def time_launches(torch, fn, n, flush=None, before=None):
-    """Duration (us) of ``fn``: mean and min over n launches, from HIP events on the current stream.
+CACHE_SPAN = 1 << 30  # bytes a rotation of buffer sets spans: 4x the 256 MiB Infinity Cache
 
-    With ``flush``, every launch is preceded by the cache eviction.  A pair of
-    events costs a few microseconds of dispatch and completion signalling, so
-    the events bracket [eviction + fn] and, on interleaved iterations,
-    [eviction] alone; the difference of the means is fn's duration with the
-    event overhead cancelled (the eviction itself is outside the result).
 
-    An interval also counts any time the GPU waits for the host to enqueue the next
-    command, so the host must stay ahead: evictions are put in flight before the first
-    timed launch (the GPU works through them while the loop enqueues), and Python's
-    garbage collector, whose pauses can drain the queue, is off during the loop.
-    (Without this a single stalled interval moved a 200-launch mean by over 100 us.)
-    """
+def lead_flushes(torch, flush, host_us, steps):
+    """Evictions to queue ahead of a timed block so that the host, which enqueues the block's
+    calls at ``host_us`` each, stays ahead of the GPU for all ``steps`` of them (an interval
+    also counts any time the GPU waits for the host)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    flush()
+    b.record()
+    torch.cuda.synchronize()
+    per = max(a.elapsed_time(b) * 1e3, 1.0)
+    return int(min(400, max(8, 2.0 * steps * host_us / per)))
+
+
+def host_us_per_call(torch, fn, n=8):
+    """Host time to enqueue one call of fn (mean of n, after one untimed call)."""
+    fn()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    us = (time.perf_counter() - t0) * 1e6 / n
+    torch.cuda.synchronize()
+    return us
+
+
+def time_block(torch, fns, steps, flush):
+    """Mean time (us) of ``steps`` calls in a row, fns[k % len(fns)](), between one marker
+    pair: the step time of a caller that runs them back to back.  Evictions queued before the
+    block keep the host ahead; Python's garbage collector is off during the block."""
+    k = [0]
+
+    def one():
+        fns[k[0] % len(fns)]()
+        k[0] += 1
+    lead = lead_flushes(torch, flush, host_us_per_call(torch, one), steps)
     stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    with_fn, alone = [], []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gc_on = gc.isenabled()
     gc.disable()
     try:
-        if flush is not None:
-            for _ in range(8):
-                flush()
-        for _ in range(n):
-            if before is not None:
-                before()
-            a, b = ev(), ev()
-            a.record(stream)
-            if flush is not None:
-                flush()
-            fn()
-            b.record(stream)
-            with_fn.append((a, b))
-            if flush is not None:
-                c, d = ev(), ev()
-                c.record(stream)
-                flush()
-                d.record(stream)
-                alone.append((c, d))
+        torch.cuda.synchronize()
+        for _ in range(lead):
+            flush()
+        a.record(stream)
+        for _ in range(steps):
+            one()
+        b.record(stream)
         torch.cuda.synchronize()
     finally:
         if gc_on:
             gc.enable()
-    t = np.array([a.elapsed_time(b) * 1e3 for a, b in with_fn])
-    if flush is None:
-        return float(t.mean()), float(t.min()), float(np.median(t))
-    f = np.array([c.elapsed_time(d) * 1e3 for c, d in alone])
-    return float(t.mean() - f.mean()), float(t.min() - f.mean()), float(np.median(t) - np.median(f))
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def time_steps(torch, calls, steps, flush, pairs=8):
+    """``steps`` prefills in a row, calls[k % len(calls)](events_k), each through
+    ssd_prefill_timed: every kernel launch is bound to an event pair of its own (HIP's
+    launch-with-events extension, the kernel's own start and end), so the kernels'
+    durations and the gaps between them are read with no marker between launches.  One
+    marker pair brackets the block; block / steps is the step time back to back.
+
+    Returns the block's step time, each step's span (first kernel's start to last kernel's
+    end), per launch position its kernel name and durations, and the gaps inside a step
+    and between steps (us)."""
+    evs = [ssd.LaunchEvents(pairs) for _ in range(steps)]
+    k = [0]
+
+    def one(ev=None):
+        calls[k[0] % len(calls)](ev if ev is not None else evs[0])
+        k[0] += 1
+    lead = lead_flushes(torch, flush, host_us_per_call(torch, one), steps)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc_on = gc.isenabled()
+    gc.disable()
+    try:
+        torch.cuda.synchronize()
+        k[0] = 0
+        t0 = time.perf_counter()
+        for _ in range(lead):
+            flush()
+        a.record(stream)
+        for i in range(steps):
+            one(evs[i])
+        b.record(stream)
+        host = time.perf_counter() - t0
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
+    n = len(evs[0].names)
+    names = evs[0].names
+    if any(e.names != names for e in evs):
+        raise RuntimeError("the timed steps did not all make the same launches")
+    per = [e.durations_ms() for e in evs]
+    dur = [[p[j] * 1e3 for p in per] for j in range(n)]
+    span = [e.span_ms() * 1e3 for e in evs]
+    inner = [sum(e.gaps_ms()) * 1e3 for e in evs]
+    between = [evs[i + 1].since_ms(evs[i]) * 1e3 for i in range(steps - 1)]
+    return {"block_us_per_step": a.elapsed_time(b) * 1e3 / steps, "span_us": span, "names": names,
+            "launch_us": dur, "gaps_in_step_us": inner, "gaps_between_steps_us": between,
+            "host_enqueue_us_per_step": host * 1e6 / steps, "lead_evictions": lead}
+
+
+def stats(v):
+    v = sorted(v)
+    return {"mean": sum(v) / len(v), "median": v[len(v) // 2], "min": v[0], "max": v[-1]}
+
+
+def launch_cold(torch, fn, n, flush, before=None):
+    """Profiling aid: n launches of fn, each after a 512 MiB eviction (nothing timed)."""
+    for _ in range(n):
+        if before is not None:
+            before()
+        flush()
+        fn()
+    torch.cuda.synchronize()
 
 
 def prefill_buffers(torch, s, inp):
@@ -290,6 +362,42 @@ def prefill_buffers(torch, s, inp):
 def run_prefill(g, s):
     ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk, y=g["y"],
                 final_state=g["final"], workspace=g["ws"])
+
+
+def plain_prefill(g, s, **kw):
+    """The prefill with options (prefill_ex; a path through ssd_prefill_forced), untimed."""
+    def run():
+        ssd.prefill_ex(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk,
+                       y=g.get("y_out", g["y"]), final_state=g["final"], workspace=g["ws"], **kw)
+    return run
+
+
+def timed_prefill(g, s, **kw):
+    """The same prefill through ssd_prefill_timed (every launch bound to an event pair)."""
+    def run(ev):
+        ssd.prefill_timed(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], events=ev, chunk=s.chunk,
+                          y=g.get("y_out", g["y"]), final_state=g["final"], workspace=g["ws"], **kw)
+    return run
+
+
+def rotation(torch, g, s):
+    """Buffer sets to rotate over: copies of the workload's inputs (same values, other
+    addresses) with outputs and a workspace of their own, as many as span CACHE_SPAN bytes
+    together (at least one), so that a step does not find its data in the Infinity Cache
+    from the steps just before it."""
+    per = alg_counts(s)["fused_bytes"] + g["ws"].numel() * g["ws"].element_size()
+    r = max(1, min(32, -(-CACHE_SPAN // per)))
+    sets = []
+    for i in range(r):
+        h = dict(g)
+        if i:
+            for k in ("x", "dt", "B", "C"):
+                h[k] = g[k].clone()
+            h["h0"] = None if g["h0"] is None else g["h0"].clone()
+            h["y"], h["final"], h["ws"] = (torch.empty_like(g["y"]), torch.empty_like(g["final"]),
+                                           torch.empty_like(g["ws"]))
+        sets.append(h)
+    return sets
 
 
 def stage_fns(torch, g, s):
@@ -378,29 +486,33 @@ def bench_decode(torch, steps, flush):
     for t in range(min(8, steps)):  # warm-up
         ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for t in range(steps):
-        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us_loop = a.elapsed_time(b) * 1e3 / steps
-    # cold: flush before each step (64 sampled steps)
+    # the timed tokens: back to back, each batch of sequences on a state of its own, rotating
+    # over as many states as span CACHE_SPAN bytes (a step does not find its state in the
+    # Infinity Cache from the step before)
+    nst = max(1, -(-CACHE_SPAN // (state.numel() * 4)))
+    states = [state] + [state.clone() for _ in range(nst - 1)]
     k = [0]
 
     def one():
         t = k[0] % steps
+        ssd.step(states[k[0] % nst], xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
         k[0] += 1
-        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+    us_loop = time_block(torch, [one], steps, flush)
+    # one state carried through every token (it can stay in the Infinity Cache between steps)
+    k2 = [0]
 
-    us_cold = time_launches(torch, one, min(64, steps), flush=flush)[0]
+    def same():
+        t = k2[0] % steps
+        ssd.step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+        k2[0] += 1
+    us_same = time_block(torch, [same], steps, flush)
+    del states[1:]
     # the same tokens as one HIP graph (ssd_decode_graph): one launch for all of them
     y_all = torch.empty((steps, s.batch, s.nheads, s.headdim), dtype=torch.float32, device="cuda")
     graph = ssd.DecodeGraph(state, xs, dts, A, Bs, Cs, D, y=y_all)
     graph.launch()
     torch.cuda.synchronize()
-    us_graph = time_back_to_back(torch, graph.launch, 3) / steps
+    us_graph = time_block(torch, [graph.launch], 3, flush) / steps
     graph.close()
     nbytes = decode_bytes_per_step(s)
     # the batch-64 x 80-head step runs one workgroup per head (step_heads_kernel)
@@ -410,33 +522,21 @@ def bench_decode(torch, steps, flush):
         "workload": synth.WORKLOAD_NAMES[DECODE_WORKLOAD], "steps": steps,
         "us_per_step": us_loop, "tokens_per_s": s.batch / (us_loop * 1e-6),
         "alg_bytes_per_step": nbytes, "gbps": nbytes / (us_loop * 1e-6) / 1e9,
-        "hbm_frac": nbytes / (us_loop * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "cold_us_per_step": us_cold, "cold_gbps": nbytes / (us_cold * 1e-6) / 1e9,
-        "cold_hbm_frac": nbytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "hbm_frac": nbytes / (us_loop * 1e-6) / 1e9 / HBM_PEAK_GBS, "states_rotated": nst,
+        "one_state_us_per_step": us_same, "one_state_gbps": nbytes / (us_same * 1e-6) / 1e9,
         "graph_us_per_step": us_graph, "graph_gbps": nbytes / (us_graph * 1e-6) / 1e9,
-        "note": "us_per_step: 1024 back-to-back ssd_step launches on one state (the 168 MB state can stay in "
-                "the 256 MiB Infinity Cache between steps); cold: 512 MiB cache eviction before each step; "
-                "graph: the 1024 tokens as one ssd_decode_graph launch (per-token outputs in their own slots)",
+        "note": f"us_per_step: {steps} back-to-back ssd_step launches rotating over {nst} states (each "
+                f"{state.numel() * 4 / 1e6:.0f} MB); one_state: the same launches on one state (it can stay in "
+                "the 256 MiB Infinity Cache between steps); graph: the tokens as one ssd_decode_graph launch "
+                "on one state (per-token outputs in their own slots)",
     }
-
-
-def time_back_to_back(torch, fn, n):
-    """Mean duration (us) of ``fn`` over n back-to-back launches between two events (warm caches)."""
-    stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(n):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / n
 
 
 def bench_layer_rows(torch, s, g, flush, steps):
     """The prefill with its inputs where a Mamba-2 layer holds them: x, B and C in the
     convolved [x | B | C] rows, dt in the input-projection [z | x | B | C | dt] rows.
-    Cold, like the step: read in place through token strides, against copying the four
-    inputs out to dense tensors first (what a dense-only call needs)."""
+    Read in place through token strides, against copying the four inputs out to dense
+    tensors first (what a dense-only call needs)."""
     B, L, H, P, N, G = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups
     hp, gn = H * P, G * N
     xbc = torch.empty((B, L, hp + 2 * gn), dtype=g["x"].dtype, device="cuda")
@@ -460,14 +560,15 @@ def bench_layer_rows(torch, s, g, flush, steps):
         in_place()
         copied()
     torch.cuda.synchronize()
-    us_in = time_launches(torch, in_place, steps, flush=flush)[0]
-    us_cp = time_launches(torch, copied, steps, flush=flush)[0]
+    us_in = time_block(torch, [in_place], steps, flush)
+    us_cp = time_block(torch, [copied], steps, flush)
     return {"in_place_us": us_in, "copy_then_dense_us": us_cp,
             "rows": f"x|B|C rows of {hp + 2 * gn} and z|x|B|C|dt rows of {2 * hp + 2 * gn + H} elements",
-            "note": "cold, events on the launch stream; the copies are torch's, outside the library"}
+            "note": "back to back on one set of rows (a step's data exceeds the Infinity Cache); the copies "
+                    "are torch's, outside the library"}
 
 
-def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
+def bench_cached_vs_recompute(torch, flush, context=4096, ntok=256, reps=20):
     """Per generated token at a ``context``-token context, batch 1, for the five Mamba-2 shapes:
     cached decode (the state carried over; ``ntok`` tokens as one decode graph, and as eager
     ssd_step launches) against full-prefix recomputation (an ssd_prefill over context + 1 tokens,
@@ -479,7 +580,7 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
         g = prefill_buffers(torch, s, inp)
         run_prefill(g, s)
         torch.cuda.synchronize()
-        us_re = time_back_to_back(torch, lambda: run_prefill(g, s), reps)
+        us_re = time_block(torch, [lambda: run_prefill(g, s)], reps, flush)
         ds = synth.DecodeShape(1, H, 64, 128, 1, ntok, "bf16")
         dinp = synth.decode_inputs(ds, synth.SEED_BASE + 200 + H)
         xs, dts = synth.to_torch(dinp["x"], "bf16"), synth.to_torch(dinp["dt"], "bf16")
@@ -488,7 +589,7 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
         graph = ssd.DecodeGraph(state, xs, dts, g["A"], Bs, Cs, g["D"])
         graph.launch()
         torch.cuda.synchronize()
-        us_graph = time_back_to_back(torch, graph.launch, max(2, reps // 4)) / ntok
+        us_graph = time_block(torch, [graph.launch], max(2, reps // 4), flush) / ntok
         graph.close()
         y1 = torch.empty((1, H, 64), dtype=torch.float32, device="cuda")
         k = [0]
@@ -499,7 +600,7 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
             ssd.step(state, xs[t], dts[t], g["A"], Bs[t], Cs[t], g["D"], y=y1)
         eager()
         torch.cuda.synchronize()
-        us_eager = time_back_to_back(torch, eager, ntok)
+        us_eager = time_block(torch, [eager], ntok, flush)
         out[name] = {"nheads": H, "recompute_us": us_re, "cached_graph_us": us_graph, "cached_eager_us": us_eager,
                      "speedup_graph": us_re / us_graph, "speedup_eager": us_re / us_eager}
         del g, xs, dts, Bs, Cs, state
@@ -511,99 +612,136 @@ def bench_cached_vs_recompute(torch, context=4096, ntok=256, reps=20):
 
 # ---------------------------------------------------------------------------- main
 
-def bench_prefill_workload(torch, wl, steps, warmup, flush, headline=False):
-    """Cold prefill steps of one workload, its kernels one by one, and the rooflines.
+def launch_counts(counts, j, name):
+    """Algorithmic counts of launch j of a prefill: the first launch of the three- and two-launch
+    paths is the fused one (cumulative decay, chunk states and GEMM1, counted under
+    chunk_state_pair_kernel whichever instantiation runs it)."""
+    if j == 0 and name in ("chunk_state_pair_kernel", "chunk_state_kernel"):
+        return counts["kernels"]["chunk_state_pair_kernel"]
+    return counts["kernels"].get(name)
 
-    Returns (record, inputs, buffers, wall seconds of the timed steps)."""
-    s = synth.WORKLOADS[wl]
-    inp = synth.prefill_inputs(s, synth.SEED_BASE + wl)
-    g = prefill_buffers(torch, s, inp)
-    settle_clocks(torch, flush)
-    for _ in range(warmup):
-        run_prefill(g, s)
-    torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` cold steps, bracketed by synchronisations
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    us_step, us_step_min, us_step_med = time_launches(torch, lambda: run_prefill(g, s), steps, flush=flush)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
+def launch_table(t, counts):
+    """Per launch position of a time_steps result: the kernel, its durations and its rates."""
+    out = []
+    for j, name in enumerate(t["names"]):
+        st = stats(t["launch_us"][j])
+        r = {"kernel": name, "us": st["mean"], "us_median": st["median"], "us_min": st["min"], "us_max": st["max"]}
+        c = launch_counts(counts, j, name)
+        if c is not None:
+            sec = st["mean"] * 1e-6
+            r.update({"method_bytes": c["method_bytes"], "alg_bytes_incl_intermediates": c["bytes"],
+                      "alg_flops": c["flops"], "method_gbps": c["method_bytes"] / sec / 1e9,
+                      "hbm_frac_method_bytes": c["method_bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+                      "tflops": c["flops"] / sec / 1e12})
+        out.append(r)
+    return out
+
+
+def step_summary(us, t, s, counts):
+    """The step figures: ``us`` per step of the plain block, the launches of a time_steps result."""
     tokens = s.batch * s.seqlen
-    us_warm = time_back_to_back(torch, lambda: run_prefill(g, s), steps)
+    launches = launch_table(t, counts)
+    fb, ff = counts["fused_bytes"], counts["fused_flops"]
+    sp = stats(t["span_us"])
+    return {
+        "us_per_step": us, "tokens_per_s": tokens / (us * 1e-6),
+        "timed_launch_us_per_step": t["block_us_per_step"],
+        "span_us_mean": sp["mean"], "span_us_median": sp["median"], "span_us_min": sp["min"],
+        "kernel_us_sum": sum(r["us"] for r in launches),
+        "gaps_in_step_us": stats(t["gaps_in_step_us"])["mean"],
+        "gap_between_steps_us": stats(t["gaps_between_steps_us"])["mean"] if t["gaps_between_steps_us"] else None,
+        "gap_between_steps_us_max": max(t["gaps_between_steps_us"]) if t["gaps_between_steps_us"] else None,
+        "host_enqueue_us_per_step": t["host_enqueue_us_per_step"], "lead_evictions": t["lead_evictions"],
+        "method_bytes": fb, "alg_flops": ff,
+        "method_gbps": fb / (us * 1e-6) / 1e9, "hbm_frac_method_bytes": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "alg_tflops": ff / (us * 1e-6) / 1e12, "alg_mfma_frac": ff / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "hbm_floor_us": fb / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "launches": launches,
+    }
 
-    # ---- per-kernel durations (cold), events on the launch stream
-    counts = alg_counts(s)
-    stages = stage_fns(torch, g, s)
-    kernels = {}
-    for name, (fn, before) in stages.items():
-        us, us_min, us_med = time_launches(torch, fn, steps, flush=flush, before=before)
-        c = counts["kernels"][name]
-        kernels[name] = {"us": us, "us_min": us_min, "us_median": us_med, "method_bytes": c["method_bytes"],
-                         "alg_bytes_incl_intermediates": c["bytes"], "alg_flops": c["flops"],
-                         "method_gbps": c["method_bytes"] / (us * 1e-6) / 1e9, "tflops": c["flops"] / (us * 1e-6) / 1e12}
-    # the step's longest launch among those timed on their own (the fused first launch has no
-    # entry point of its own; its duration is in the kernel trace)
-    dom = max((k for k in step_kernels(s) if k in kernels), key=lambda k: kernels[k]["us"])
-    d = kernels[dom]
-    roof = {"bound": "hbm", "achieved": d["method_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+
+def roofline_of(step, s, wl):
+    """The roofline object of a step: its longest launch, on the method's own bytes."""
+    d = max((r for r in step["launches"] if "method_bytes" in r), key=lambda r: r["us"])
+    dom = d["kernel"]
+    return {"bound": "hbm", "achieved": d["method_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": d["method_gbps"] / HBM_PEAK_GBS, "traffic": counter_traffic(dom, synth.WORKLOAD_NAMES[wl]),
             "kernel": dom,
-            "variant": ("with Step-3 (ssd_chunk_scan_passing)" if dom == "chunk_scan_small_kernel"
-                        and passing_in_scan(s) else "as launched by the stage entry point"),
-            "us_per_launch": d["us"], "method_bytes_per_launch": d["method_bytes"],
+            "variant": ("with Step-3 inside (two-launch prefill)" if dom == "chunk_scan_small_kernel"
+                        and passing_in_scan(s) else "as ssd_prefill launches it"),
+            "us_per_launch": d["us"], "us_per_launch_median": d["us_median"],
+            "timing": "HIP events bound to the kernel's own launch in each timed step (ssd_prefill_timed), "
+                      "mean over the steps",
+            "method_bytes_per_launch": d["method_bytes"],
             "alg_bytes_incl_intermediates_per_launch": d["alg_bytes_incl_intermediates"],
             "alg_flops_per_launch": d["alg_flops"], "mfma_tflops": d["tflops"],
             "mfma_frac": d["tflops"] / MFMA_BF16_PEAK_TFLOPS,
             "intensity_flop_per_method_byte": d["alg_flops"] / d["method_bytes"]}
 
-    sec = us_step * 1e-6
-    fb, ff = counts["fused_bytes"], counts["fused_flops"]
-    prefill = {
-        "us_per_step_cold": us_step, "us_per_step_cold_median": us_step_med, "us_per_step_cold_min": us_step_min,
-        "us_per_step_warm": us_warm, "tokens_per_s": tokens / sec, "warm_tokens_per_s": tokens / (us_warm * 1e-6),
-        "method_bytes": fb, "alg_flops": ff,
-        "method_gbps": fb / sec / 1e9, "hbm_frac_method_bytes": fb / sec / 1e9 / HBM_PEAK_GBS,
-        "alg_tflops": ff / sec / 1e12, "alg_mfma_frac": ff / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "hbm_floor_us": fb / (HBM_PEAK_GBS * 1e9) * 1e6,
-        "step_launches": step_kernels(s),
-        "kernel_us_sum": sum(kernels[k]["us"] for k in step_kernels(s) if k in kernels),
-    }
+
+def bench_prefill_workload(torch, wl, steps, warmup, flush):
+    """Timed prefill steps of one workload, every launch timed, and its roofline.
+
+    The timed region is ``steps`` prefills back to back over a rotation of buffer sets, each
+    through ssd_prefill_timed.  Returns (record, inputs, buffer sets, wall seconds of the
+    timed region)."""
+    s = synth.WORKLOADS[wl]
+    inp = synth.prefill_inputs(s, synth.SEED_BASE + wl)
+    g = prefill_buffers(torch, s, inp)
+    sets = rotation(torch, g, s)
+    plain = [lambda h=h: run_prefill(h, s) for h in sets]
+    calls = [timed_prefill(h, s) for h in sets]
+    settle_clocks(torch, flush)
+    ev = ssd.LaunchEvents(8)
+    for i in range(max(warmup, len(sets))):
+        plain[i % len(plain)]()
+        calls[i % len(calls)](ev)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps through ssd_prefill, bracketed by synchronisations
+    t_wall = time.perf_counter()
+    us = time_block(torch, plain, steps, flush)
+    wall = time.perf_counter() - t_wall
+    # ---- the same steps through ssd_prefill_timed: every kernel's own duration.  Events bound
+    # to a launch put a few microseconds of dispatch between kernels (the block's step time
+    # shows it), not into the kernels.
+    t = time_steps(torch, calls, steps, flush)
+    counts = alg_counts(s)
+    step = step_summary(us, t, s, counts)
+    step["buffer_sets"] = len(sets)
+    roof = roofline_of(step, s, wl)
+    # on one buffer set: what stays in the Infinity Cache between steps helps
+    step["one_buffer_set_us_per_step"] = time_block(torch, [lambda: run_prefill(g, s)], steps, flush)
     # bf16 y (the fp32 result rounded once): halves the largest stream
     if s.dtype == "bf16":
-        yb = torch.empty((s.batch, s.seqlen, s.nheads, s.headdim), dtype=torch.bfloat16, device="cuda")
-        fbf = lambda: ssd.prefill_ex(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], y_dtype=torch.bfloat16,
-                                     chunk=s.chunk, y=yb, final_state=g["final"], workspace=g["ws"])
-        for _ in range(3):
-            fbf()
-        torch.cuda.synchronize()
-        ub = time_launches(torch, fbf, steps, flush=flush)
-        bb = fb - s.batch * s.seqlen * s.nheads * s.headdim * 2
-        prefill["bf16_y"] = {"us_per_step_cold": ub[0], "us_per_step_cold_median": ub[2],
-                             "tokens_per_s": tokens / (ub[0] * 1e-6), "method_bytes": bb,
-                             "hbm_frac_method_bytes": bb / (ub[0] * 1e-6) / 1e9 / HBM_PEAK_GBS}
-    rec = {"workload": synth.WORKLOAD_NAMES[wl], "value": tokens / sec, "unit": "tokens/s",
-           "roofline": roof, "prefill": prefill, "kernels": kernels}
-    return rec, inp, g, wall
+        bsets = [dict(h, y_out=torch.empty(h["y"].shape, dtype=torch.bfloat16, device="cuda")) for h in sets]
+        ub = time_block(torch, [plain_prefill(h, s, y_dtype=torch.bfloat16) for h in bsets], steps, flush)
+        tb = time_steps(torch, [timed_prefill(h, s, y_dtype=torch.bfloat16) for h in bsets], steps, flush)
+        bb = counts["fused_bytes"] - s.batch * s.seqlen * s.nheads * s.headdim * 2
+        step["bf16_y"] = {"us_per_step": ub, "tokens_per_s": s.batch * s.seqlen / (ub * 1e-6), "method_bytes": bb,
+                          "hbm_frac_method_bytes": bb / (ub * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "launches": [{"kernel": n, "us": stats(v)["mean"]} for n, v in zip(tb["names"], tb["launch_us"])]}
+        del bsets
+    rec = {"workload": synth.WORKLOAD_NAMES[wl], "value": step["tokens_per_s"], "unit": "tokens/s",
+           "roofline": roof, "prefill": step}
+    return rec, inp, sets, wall
 
 
-def bench_single_pass(torch, wl, g, steps, flush):
-    """The single-pass prefill (only selected on request) on the same workload, cold."""
+def bench_single_pass(torch, wl, sets, steps, flush):
+    """The single-pass prefill (only selected on request) on the same workload and buffers."""
     s = synth.WORKLOADS[wl]
-    ws = ssd.alloc_workspace(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk)
-    f = lambda: ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk, y=g["y"],
-                            final_state=g["final"], workspace=ws, path=ssd.PATH_SINGLE_PASS)
+    calls = [timed_prefill(h, s, path=ssd.PATH_SINGLE_PASS) for h in sets]
     try:
-        f()
+        calls[0](ssd.LaunchEvents(8))
     except ssd.SsdError:
         return None
-    for _ in range(2):
-        f()
     torch.cuda.synchronize()
-    us = time_launches(torch, f, steps, flush=flush)
-    return {"us_per_step_cold": us[0], "us_per_step_cold_median": us[2],
-            "tokens_per_s": s.batch * s.seqlen / (us[0] * 1e-6),
-            "note": "ssd_prefill_forced with SSD_PATH_SINGLE_PASS; the library's own path is the step above"}
+    us = time_block(torch, [plain_prefill(h, s, path=ssd.PATH_SINGLE_PASS) for h in sets], steps, flush)
+    t = time_steps(torch, calls, steps, flush)
+    return {"us_per_step": us, "tokens_per_s": s.batch * s.seqlen / (us * 1e-6),
+            "launches": [{"kernel": n, "us": stats(v)["mean"]} for n, v in zip(t["names"], t["launch_us"])],
+            "note": "ssd_prefill_forced's SSD_PATH_SINGLE_PASS; the library's own path is the step above"}
 
 
 def main():
@@ -620,7 +758,9 @@ def main():
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_scan_pipe_kernel", "chunk_state_kernel", "state_passing_kernel",
                                        "chunk_cumsum_kernel", "chunk_gemm1_kernel", "chunk_scan_small_kernel",
                                        "single_pass", "step", "cached", "copy"],
-                    help="profiling aid: launch only this work --steps times (cold), print nothing else")
+                    help="profiling aid: launch only this work --steps times, print nothing else (prefill and "
+                         "single_pass: back to back over the rotating buffer sets, as timed; a stage kernel: "
+                         "through its entry point, each launch after a cache eviction)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -655,7 +795,7 @@ def main():
         print(json.dumps(bench_decode(torch, args.decode_steps, flush)))
         return 0
     if args.only == "cached":
-        print(json.dumps(bench_cached_vs_recompute(torch)))
+        print(json.dumps(bench_cached_vs_recompute(torch, flush)))
         return 0
     if args.only is not None:
         inp = synth.prefill_inputs(s, synth.SEED_BASE + args.workload)
@@ -664,17 +804,21 @@ def main():
         for _ in range(args.warmup):
             run_prefill(g, s)
         torch.cuda.synchronize()
-        if args.only == "prefill":
-            time_launches(torch, lambda: run_prefill(g, s), args.steps, flush=flush)
-        elif args.only == "single_pass":
-            bench_single_pass(torch, args.workload, g, args.steps, flush)
+        if args.only in ("prefill", "single_pass"):
+            path = ssd.PATH_SINGLE_PASS if args.only == "single_pass" else ssd.PATH_AUTO
+            sets = rotation(torch, g, s)
+            for i in range(args.steps):
+                h = sets[i % len(sets)]
+                ssd.prefill(h["x"], h["dt"], h["A"], h["B"], h["C"], h["D"], h["h0"], chunk=s.chunk, y=h["y"],
+                            final_state=h["final"], workspace=h["ws"], path=path)
+            torch.cuda.synchronize()
         else:
             fn, before = stage_fns(torch, g, s)[args.only]
-            time_launches(torch, fn, args.steps, flush=flush, before=before)
+            launch_cold(torch, fn, args.steps, flush, before)
         return 0
 
-    rec, inp, g, wall = bench_prefill_workload(torch, args.workload, args.steps, args.warmup, flush, headline=True)
-    us_step = rec["prefill"]["us_per_step_cold"]
+    rec, inp, sets, wall = bench_prefill_workload(torch, args.workload, args.steps, args.warmup, flush)
+    us_step = rec["prefill"]["us_per_step"]
     out = {
         "metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us_step / 1e3, "higher_is_better": True, "scaling": "weak",
@@ -682,18 +826,20 @@ def main():
         "config": {"workload": wname, "batch": s.batch, "seqlen": s.seqlen, "nheads": s.nheads,
                    "headdim": s.headdim, "dstate": s.dstate, "ngroups": s.ngroups, "chunk": s.chunk,
                    "initial_state": s.init_state,
-                   "cache": "cold (512 MiB eviction before each step, outside the events)",
+                   "timing": f"{args.steps} steps back to back over {len(sets)} rotating buffer set(s) of "
+                             f"the inputs, outputs and workspace (together over 1 GiB, 4x the Infinity Cache), "
+                             f"one marker pair around the block; every kernel launch bound to HIP events of "
+                             f"its own (ssd_prefill_timed)",
                    "parallelism": "single GPU"},
         "roofline": rec["roofline"],
         "prefill": rec["prefill"],
-        "kernels": rec["kernels"],
         "timed_wall_s": wall,
     }
-    sp = bench_single_pass(torch, args.workload, g, args.steps, flush)
+    sp = bench_single_pass(torch, args.workload, sets, args.steps, flush)
     if sp is not None:
         out["single_pass"] = sp
-    out["layer_rows"] = bench_layer_rows(torch, s, g, flush, args.steps)
-    del g
+    out["layer_rows"] = bench_layer_rows(torch, s, sets[0], flush, args.steps)
+    del sets
     if not args.no_extra:
         out["workloads"] = {}
         for wl in EXTRA_WORKLOADS:
@@ -704,7 +850,7 @@ def main():
             del gx
     if not args.no_decode:
         out["decode"] = bench_decode(torch, args.decode_steps, flush)
-        out["cached_vs_recompute"] = bench_cached_vs_recompute(torch)
+        out["cached_vs_recompute"] = bench_cached_vs_recompute(torch, flush)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, inp)
     print(json.dumps(out))

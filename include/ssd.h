@@ -23,8 +23,9 @@
  * - The caller owns all memory.  The library never allocates or frees device
  *   memory; scratch comes from the caller's workspace, except for
  *   ssd_prefill_noalloc, whose scratch is a device array of the library's own (one per
- *   GPU, see there).  Apart from that array and its per-device address, no global state:
- *   calls are reentrant and thread-safe.
+ *   GPU, see there).  Apart from that array, its per-device address and the per-thread
+ *   pointer through which ssd_prefill_timed reaches its own launches (set for the length
+ *   of that call only), no global state: calls are reentrant and thread-safe.
  *   The one object the library creates is a decode graph, owned by the
  *   caller through its handle (ssd_decode_graph_create / _destroy).
  * - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
@@ -221,6 +222,34 @@ int ssd_prefill_forced(const void *x, const void *dt, const float *A, const void
                        long long x_stride, long long bc_stride, long long dt_stride,
                        long long z_stride, void *workspace, size_t workspace_bytes,
                        void *hip_stream, int path, long long spin_limit);
+/*
+ * Measurement entry point: ssd_prefill_forced with each kernel launch of the call timed
+ * on the device.  Launch i (in the order the call enqueues them) is made with
+ * start_events[i] and stop_events[i] bound to the kernel itself (HIP's launch-with-events
+ * extension), so hipEventElapsedTime(start_events[i], stop_events[i]) is that kernel's own
+ * execution time, and the stop event of one launch and the start event of the next bound
+ * the gap between them; no marker is enqueued between launches.  The results are those
+ * of ssd_prefill_forced with the same arguments.
+ *   start_events, stop_events  hipEvent_t[capacity], created by the caller with timing
+ *                              enabled (owned by the caller; each call rebinds them)
+ *   kernel_names               const char *[capacity] or NULL: receives the name of each
+ *                              timed launch's kernel (static strings of the library)
+ *   capacity                   >= 0; launches past it run untimed
+ *   n_launches                 NULL, or receives the number of kernel launches the call made
+ * Errors: those of ssd_prefill_forced; SSD_ERR_INVALID_ARG for capacity < 0 or a NULL
+ * array or event within capacity.  The timing is per calling thread and lasts for the
+ * call only.
+ */
+int ssd_prefill_timed(const void *x, const void *dt, const float *A, const void *Bm,
+                      const void *Cm, const float *D, const float *dt_bias, int dt_softplus,
+                      const void *z, const float *initial_state, float *final_state, void *y,
+                      ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                      int nheads, int headdim, int dstate, int ngroups, int chunk,
+                      long long x_stride, long long bc_stride, long long dt_stride,
+                      long long z_stride, void *workspace, size_t workspace_bytes,
+                      void *hip_stream, int path, long long spin_limit,
+                      void *const *start_events, void *const *stop_events,
+                      const char **kernel_names, int capacity, int *n_launches);
 /*
  * Whether the last prefill that used `workspace` completed its waits between workgroups
  * (a prefill with seqlen == 0 does not touch the workspace and is not that prefill).

@@ -14,6 +14,14 @@
 
 #include "ssd_launch.h"
 
+namespace ssd {
+LaunchTiming *&launch_timing()
+{
+    static thread_local LaunchTiming *t = nullptr;
+    return t;
+}
+}  // namespace ssd
+
 namespace {
 
 
@@ -203,7 +211,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (4 << 16) | 2; }
+int ssd_version(void) { return (4 << 16) | 3; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -504,6 +512,30 @@ int ssd_prefill_forced(const void *x, const void *dt, const float *A, const void
     return prefill_impl(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype, y_dtype,
                         batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x_stride, bc_stride, dt_stride,
                         z_stride, workspace, workspace_bytes, hip_stream, path, spin_limit);
+}
+
+int ssd_prefill_timed(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                      const float *dt_bias, int dt_softplus, const void *z, const float *initial_state,
+                      float *final_state, void *y, ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int seqlen,
+                      int nheads, int headdim, int dstate, int ngroups, int chunk, long long x_stride,
+                      long long bc_stride, long long dt_stride, long long z_stride, void *workspace,
+                      size_t workspace_bytes, void *hip_stream, int path, long long spin_limit,
+                      void *const *start_events, void *const *stop_events, const char **kernel_names,
+                      int capacity, int *n_launches)
+{
+    if (capacity < 0 || (capacity > 0 && (!start_events || !stop_events))) return SSD_ERR_INVALID_ARG;
+    for (int i = 0; i < capacity; i++)
+        if (!start_events[i] || !stop_events[i]) return SSD_ERR_INVALID_ARG;
+    ssd::LaunchTiming t = {start_events, stop_events, kernel_names, capacity, 0};
+    ssd::LaunchTiming *&cur = ssd::launch_timing();
+    ssd::LaunchTiming *const prev = cur;
+    cur = &t;
+    const int r = prefill_impl(x, dt, A, Bm, Cm, D, dt_bias, dt_softplus, z, initial_state, final_state, y, in_dtype,
+                               y_dtype, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, x_stride, bc_stride,
+                               dt_stride, z_stride, workspace, workspace_bytes, hip_stream, path, spin_limit);
+    cur = prev;
+    if (n_launches) *n_launches = t.n;
+    return r;
 }
 
 int ssd_prefill_check(const void *workspace, size_t workspace_bytes, void *hip_stream)

@@ -49,7 +49,8 @@ static hipError_t launch_gemm1_t(const void *Bm, const void *Cm, void *cb, const
     const dim3 grid(d.nc, d.G, d.B);
     const TIn *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
 #define SSD_G1_LAUNCH(NN, NWV) \
-    chunk_gemm1_kernel<TIn, NN, NWV><<<grid, 64 * NWV, 0, s>>>(bb, cc, cb, d.L, d.G, d.Q, d.nc)
+    launch_kernel("chunk_gemm1_kernel", chunk_gemm1_kernel<TIn, NN, NWV>, grid, 64 * NWV, s, bb, cc, cb, d.L, \
+                  d.G, d.Q, d.nc)
 #define SSD_G1_BY_Q(NN)          \
     if (d.Q == 256)              \
         SSD_G1_LAUNCH(NN, 16);   \

@@ -945,8 +945,8 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
             static_assert(PipeLds<64, 128, 16>::fits, "pipelined chunk scan LDS");
             const int nwg = nitems < ncu ? nitems : ncu;
 #define SSD_PIPE_LAUNCH(GT, YB)                                                                          \
-    chunk_scan_pipe_kernel<64, 128, 16, GT, YB><<<nwg, 1024, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, d.L, d.H, \
-                                                                     d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
+    launch_kernel("chunk_scan_pipe_kernel", chunk_scan_pipe_kernel<64, 128, 16, GT, YB>, nwg, 1024, s, xx, cc, \
+                  cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
             if (o.z && o.y_bf16)
                 SSD_PIPE_LAUNCH(true, true);
             else if (o.z)
@@ -965,11 +965,13 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
         const int fit = (160 * 1024) / ScanLds<TIn, P, NN, NWV>::bytes, per_cu = fit < 16 / NWV ? fit : 16 / NWV; \
         const int nwg = nitems < ncu * per_cu ? nitems : ncu * per_cu;                                   \
         if (o.z || o.y_bf16)                                                                              \
-            chunk_scan_kernel<TIn, P, NN, NWV, true><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
-                                                                              d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems); \
+            launch_kernel("chunk_scan_kernel", chunk_scan_kernel<TIn, P, NN, NWV, true>, nwg, 64 * NWV, s, xx, \
+                          cc, cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc,       \
+                          nitems);                                                                             \
         else                                                                                              \
-            chunk_scan_kernel<TIn, P, NN, NWV, false><<<nwg, 64 * NWV, 0, s>>>(xx, cc, cbg, acum, dtc, hen, D, y, o, \
-                                                                               d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems); \
+            launch_kernel("chunk_scan_kernel", chunk_scan_kernel<TIn, P, NN, NWV, false>, nwg, 64 * NWV, s,  \
+                          xx, cc, cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, \
+                          nitems);                                                                           \
     } while (0)
 #define SSD_SCAN_BY_Q(NN)                                  \
     if (d.Q == 256)                                        \

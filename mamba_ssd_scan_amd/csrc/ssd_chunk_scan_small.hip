@@ -492,9 +492,9 @@ hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb
     const bf16_t *xx = static_cast<const bf16_t *>(x), *cc = static_cast<const bf16_t *>(Cm);
     f16 *hh = static_cast<f16 *>(h);
 #define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                        \
-    chunk_scan_small_kernel<64, NN, OO, PP><<<nitems, 512, 0, s>>>(xx, cc, cb, acum, dtc, hh, init, fin, o.sync, \
-                                                                    D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc, \
-                                                                    nwhole)
+    launch_kernel("chunk_scan_small_kernel", chunk_scan_small_kernel<64, NN, OO, PP>, nitems, 512, s, xx, cc, \
+                  cb, acum, dtc, hh, init, fin, o.sync, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc,      \
+                  nwhole)
 #define SSD_SMALL_LAUNCH2(NN, PP)                                                                            \
     do {                                                                                                     \
         if (o.z || o.y_bf16) SSD_SMALL_LAUNCH3(NN, true, PP);                                                \

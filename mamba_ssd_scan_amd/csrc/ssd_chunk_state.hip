@@ -404,8 +404,8 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
     const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
               *cc = static_cast<const TIn *>(Cm);
 #define SSD_CS_LAUNCH(NN, JJ)                                                                                      \
-    chunk_state_kernel<TIn, P, NN, FUSE, GR, JJ><<<grid, 256, 0, s>>>(xx, bb, dd, A, acum, dtc, states, cc, cb, o, \
-                                                                      d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.Q, d.nc)
+    launch_kernel("chunk_state_kernel", chunk_state_kernel<TIn, P, NN, FUSE, GR, JJ>, grid, 256, s, xx, bb, \
+                  dd, A, acum, dtc, states, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.Q, d.nc)
 #define SSD_CS_BY_JB(NN)          \
     if (big || sizeof(TIn) == 4)  \
         SSD_CS_LAUNCH(NN, 32);    \

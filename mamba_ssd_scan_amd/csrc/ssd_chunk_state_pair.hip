@@ -243,8 +243,8 @@ hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt
                  *dd = static_cast<const bf16_t *>(dt), *cc = static_cast<const bf16_t *>(Cm);
     f16 *st = static_cast<f16 *>(states);
 #define SSD_CSP_LAUNCH(NN) \
-    chunk_state_pair_kernel<NN><<<grid, 512, 0, s>>>(xx, bb, dd, A, acum, dtc, st, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, \
-                                                     d.sdt, d.nc)
+    launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<NN>, grid, 512, s, xx, bb, dd, A, acum, \
+                  dtc, st, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc)
     switch (d.N) {
     case 32: SSD_CSP_LAUNCH(32); break;
     case 64: SSD_CSP_LAUNCH(64); break;

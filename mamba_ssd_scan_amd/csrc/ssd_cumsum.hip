@@ -70,11 +70,11 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, floa
 {
     dim3 grid(d.nc, d.H, d.B);
     if (d.bf16)
-        chunk_cumsum_kernel<bf16_t><<<grid, 64, 0, s>>>(static_cast<const bf16_t *>(dt), A, acum,
-                                                        dtc, d.L, d.H, d.Q, d.nc);
+        launch_kernel("chunk_cumsum_kernel", chunk_cumsum_kernel<bf16_t>, grid, 64, s,
+                      static_cast<const bf16_t *>(dt), A, acum, dtc, d.L, d.H, d.Q, d.nc);
     else
-        chunk_cumsum_kernel<float><<<grid, 64, 0, s>>>(static_cast<const float *>(dt), A, acum, dtc,
-                                                       d.L, d.H, d.Q, d.nc);
+        launch_kernel("chunk_cumsum_kernel", chunk_cumsum_kernel<float>, grid, 64, s,
+                      static_cast<const float *>(dt), A, acum, dtc, d.L, d.H, d.Q, d.nc);
     return hipGetLastError();
 }
 

@@ -3,12 +3,47 @@
 // each launcher only picks the template instance and the grid.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
 #include "ssd_common.h"
 
 namespace ssd {
+
+// Per-launch timing of a prefill (ssd_prefill_timed).  While such a call runs on a thread,
+// every kernel launch of that thread binds the next caller event pair to the kernel itself
+// (HIP's launch-with-events extension: the events take the kernel's own start and end, with
+// no marker packets between launches) and records the kernel's name.
+struct LaunchTiming {
+    void *const *start;  // hipEvent_t[cap]
+    void *const *stop;   // hipEvent_t[cap]
+    const char **names;  // [cap] or nullptr
+    int cap;             // event pairs available
+    int n;               // launches made so far (may pass cap: those are not timed)
+};
+// The calling thread's current timing, nullptr outside a timed call.
+LaunchTiming *&launch_timing();
+
+// Launch of `k` on `s`, timed when the calling thread has a timing in place.  Launch errors
+// are left for the caller's hipGetLastError(), as with the <<< >>> form.
+template <typename... P, typename... A>
+inline void launch_kernel(const char *name, void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A... a)
+{
+    LaunchTiming *t = launch_timing();
+    if (t == nullptr) {
+        k<<<grid, block, 0, s>>>(a...);
+        return;
+    }
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (t->n < t->cap) {
+        e0 = static_cast<hipEvent_t>(t->start[t->n]);
+        e1 = static_cast<hipEvent_t>(t->stop[t->n]);
+        if (t->names) t->names[t->n] = name;
+    }
+    t->n++;
+    hipExtLaunchKernelGGL(k, grid, block, 0, s, e0, e1, 0u, a...);
+}
 
 struct Dims {
     int B, L, H, P, N, G, Q, nc;  // batch, seqlen, heads, headdim, dstate, groups, chunk, chunks

@@ -39,11 +39,13 @@ hipError_t launch_pad_copy(const void *src, void *dst, int elem_bytes, long long
     const long long want = (total + 255) / 256;
     const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
     if (elem_bytes == 2)
-        pad_copy_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst),
-                                                        nout, nin_src, nin_dst, slen, dlen, so, si, sk);
+        launch_kernel("pad_copy_kernel", pad_copy_kernel<uint16_t>, grid, 256, s,
+                      static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), nout, nin_src, nin_dst,
+                      slen, dlen, so, si, sk);
     else if (elem_bytes == 4)
-        pad_copy_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t *>(src), static_cast<uint32_t *>(dst),
-                                                        nout, nin_src, nin_dst, slen, dlen, so, si, sk);
+        launch_kernel("pad_copy_kernel", pad_copy_kernel<uint32_t>, grid, 256, s,
+                      static_cast<const uint32_t *>(src), static_cast<uint32_t *>(dst), nout, nin_src, nin_dst,
+                      slen, dlen, so, si, sk);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

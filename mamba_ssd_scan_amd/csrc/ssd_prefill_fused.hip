@@ -595,10 +595,11 @@ hipError_t launch_prefill_fused(const void *x, const void *Bm, const void *Cm, c
     const unsigned items = (unsigned)BH * (unsigned)d.nc;
 #define SSD_FUSED_LAUNCH(NN, OO)                                                                                   \
     do {                                                                                                           \
-        fused_prep_kernel<NN><<<pgrid, 256, 0, s>>>(bb, cc, cb, ctl, flags, BH * 64, d.L, d.G, d.sbc, d.nc);       \
-        chunk_fused_kernel<NN, OO, kFusedDepth><<<items, 512, 0, s>>>(xx, bb, cc, dd, A, D, init, fin, cb, y, ctl, \
-                                                                      flags, ring, o, d.L, d.H, d.G, BH, d.sx,     \
-                                                                      d.sbc, d.sdt, d.sz, d.nc);              \
+        launch_kernel("fused_prep_kernel", fused_prep_kernel<NN>, pgrid, 256, s, bb, cc, cb, ctl, flags, \
+                      BH * 64, d.L, d.G, d.sbc, d.nc);                                                   \
+        launch_kernel("chunk_fused_kernel", chunk_fused_kernel<NN, OO, kFusedDepth>, items, 512, s, xx, bb, \
+                      cc, dd, A, D, init, fin, cb, y, ctl, flags, ring, o, d.L, d.H, d.G, BH, d.sx, d.sbc,  \
+                      d.sdt, d.sz, d.nc);                                                                   \
     } while (0)
 #define SSD_FUSED_LAUNCH2(NN)                                      \
     do {                                                           \

@@ -99,11 +99,11 @@ hipError_t launch_state_passing(void *states, const float *acum, const float *in
     const int PN4 = d.P * d.N / 4;
     dim3 grid((PN4 + kPassThreads - 1) / kPassThreads, d.H, d.B);
     if (d.bf16)
-        state_passing_kernel<f16><<<grid, kPassThreads, 0, s>>>(static_cast<f16 *>(states), acum, init, fin, d.H,
-                                                               d.nc, d.Q, PN4);
+        launch_kernel("state_passing_kernel", state_passing_kernel<f16>, grid, kPassThreads, s,
+                      static_cast<f16 *>(states), acum, init, fin, d.H, d.nc, d.Q, PN4);
     else
-        state_passing_kernel<float><<<grid, kPassThreads, 0, s>>>(static_cast<float *>(states), acum, init, fin,
-                                                                 d.H, d.nc, d.Q, PN4);
+        launch_kernel("state_passing_kernel", state_passing_kernel<float>, grid, kPassThreads, s,
+                      static_cast<float *>(states), acum, init, fin, d.H, d.nc, d.Q, PN4);
     return hipGetLastError();
 }
 
@@ -121,7 +121,8 @@ hipError_t launch_fill_state(float *dst, const float *src, size_t n, hipStream_t
     const size_t n4 = n / 4;
     if (n4 == 0) return hipSuccess;
     if (dst == src) return hipSuccess;
-    fill_state_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, s>>>(dst, src, n4);
+    launch_kernel("fill_state_kernel", fill_state_kernel, dim3((unsigned)((n4 + 255) / 256)), 256, s, dst, src,
+                  n4);
     return hipGetLastError();
 }
 

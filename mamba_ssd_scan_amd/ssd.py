@@ -19,7 +19,8 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_prefill_workspace_size", "ssd_prefill", "ssd_step",
-           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_prefill_forced", "ssd_prefill_check", "ssd_prefill_noalloc",
+           "ssd_prefill_ex", "ssd_prefill_strided", "ssd_prefill_forced", "ssd_prefill_timed", "ssd_prefill_check",
+           "ssd_prefill_noalloc",
            "ssd_step_ex", "ssd_step_strided",
            "ssd_decode_graph_create", "ssd_decode_graph_launch", "ssd_decode_graph_steps", "ssd_decode_graph_destroy",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gemm1_size",
@@ -62,6 +63,9 @@ def lib() -> ctypes.CDLL:
     L.ssd_prefill_strided.restype = i
     L.ssd_prefill_forced.argtypes = [vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [ll] * 4 + [vp, sz, vp, i, ll]
     L.ssd_prefill_forced.restype = i
+    L.ssd_prefill_timed.argtypes = ([vp] * 7 + [i] + [vp] * 4 + [i] * 9 + [ll] * 4 + [vp, sz, vp, i, ll]
+                                    + [vp, vp, vp, i, ctypes.POINTER(i)])
+    L.ssd_prefill_timed.restype = i
     L.ssd_prefill_check.argtypes = [vp, sz, vp]
     L.ssd_prefill_check.restype = i
     L.ssd_prefill_noalloc.argtypes = [vp] * 9 + [i] * 8 + [vp]
@@ -245,7 +249,7 @@ def _on_stream(stream):
 
 
 def _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state, workspace,
-             stream, path, spin_limit, plain):
+             stream, path, spin_limit, plain, timing=None):
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
@@ -273,7 +277,13 @@ def _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype,
     shape = (batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
     opts = (_ptr(dt_bias), int(bool(dt_softplus)), _ptr(z))
     ins = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D))
-    if path != PATH_AUTO or spin_limit is not None:
+    if timing is not None:
+        starts, stops, names, n = timing
+        _check(lib().ssd_prefill_timed(*ins, *opts, _ptr(initial_state), _ptr(final_state), _ptr(y), code, ycode,
+                                       *shape, *strides, _ptr(workspace), wbytes, _stream(stream), int(path),
+                                       -1 if spin_limit is None else int(spin_limit), starts, stops, names,
+                                       len(starts), ctypes.byref(n)), "ssd_prefill_timed")
+    elif path != PATH_AUTO or spin_limit is not None:
         _check(lib().ssd_prefill_forced(*ins, *opts, _ptr(initial_state), _ptr(final_state), _ptr(y), code, ycode,
                                         *shape, *strides, _ptr(workspace), wbytes, _stream(stream), int(path),
                                         -1 if spin_limit is None else int(spin_limit)), "ssd_prefill_forced")
@@ -316,6 +326,94 @@ def prefill_ex(x, dt, A, B, C, D=None, initial_state=None, *, dt_bias=None, dt_s
     Returns (y, final_state or None)."""
     return _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state,
                     workspace, stream, path, spin_limit, plain=False)
+
+
+class LaunchEvents:
+    """Event pairs for prefill_timed: ``pairs`` (start, stop) HIP timing events, created through
+    the HIP runtime that libssd.so links with the flag hipEventDisableSystemFence.  An event
+    bound to a launch otherwise gives that kernel a system-scope release (a write-back and
+    invalidation of the L2s at its end), which plain back-to-back launches on a stream do not
+    pay: with the flag a timed kernel runs as it does untimed.  Read the times after a
+    synchronisation of the device (the events themselves do not synchronise-with the work)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, pairs: int):
+        rt = lib()  # its dependency, the HIP runtime, resolves the hipEvent* symbols
+        self._rt = rt
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventCreateWithFlags.restype = ctypes.c_int
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventElapsedTime.restype = ctypes.c_int
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        rt.hipEventDestroy.restype = ctypes.c_int
+        arr = ctypes.c_void_p * pairs
+        self._starts, self._stops = arr(), arr()
+        for a in (self._starts, self._stops):
+            for i in range(pairs):
+                e = ctypes.c_void_p()
+                r = rt.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+                if r != 0:
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({r})")
+                a[i] = e.value
+        self._names = (ctypes.c_char_p * pairs)()
+        self._n = ctypes.c_int(0)
+        self.pairs = pairs
+        self.names = []
+
+    def __del__(self):
+        rt = getattr(self, "_rt", None)
+        if rt is None:
+            return
+        for a in (self._starts, self._stops):
+            for e in a:
+                if e:
+                    rt.hipEventDestroy(e)
+
+    def _args(self):
+        return self._starts, self._stops, self._names, self._n
+
+    def _done(self):
+        k = min(self._n.value, self.pairs)
+        self.names = [self._names[i].decode() for i in range(k)]
+        return self._n.value
+
+    def _ms(self, a, b):
+        t = ctypes.c_float()
+        r = self._rt.hipEventElapsedTime(ctypes.byref(t), a, b)
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return t.value
+
+    def durations_ms(self):
+        """Per timed launch of the last call: its kernel's execution time in ms."""
+        return [self._ms(self._starts[i], self._stops[i]) for i in range(len(self.names))]
+
+    def gaps_ms(self):
+        """Between consecutive timed launches of the last call: end of one to start of the next."""
+        return [self._ms(self._stops[i], self._starts[i + 1]) for i in range(len(self.names) - 1)]
+
+    def span_ms(self):
+        """First timed launch's start to the last one's end."""
+        return self._ms(self._starts[0], self._stops[len(self.names) - 1])
+
+    def since_ms(self, other: "LaunchEvents"):
+        """End of ``other``'s last timed launch to the start of this call's first."""
+        return self._ms(other._stops[len(other.names) - 1], self._starts[0])
+
+
+def prefill_timed(x, dt, A, B, C, D=None, initial_state=None, *, events: LaunchEvents, dt_bias=None,
+                  dt_softplus=False, z=None, y_dtype=None, chunk: int = 256, y=None, final_state="new",
+                  workspace=None, stream=None, path=PATH_AUTO, spin_limit=None):
+    """ssd_prefill_timed: prefill_ex (on the path ``path``) with each kernel launch bound to the
+    next event pair of ``events``.  Returns (y, final_state or None, launches made); after a
+    synchronisation, ``events.names`` and ``events.durations_ms()`` hold each timed launch's
+    kernel and its execution time."""
+    if y is not None and y_dtype is None:
+        _f32(y)
+    r = _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype, chunk, y, final_state,
+                 workspace, stream, path, spin_limit, plain=False, timing=events._args())
+    return r[0], r[1], events._done()
 
 
 NOALLOC_MAX_BYTES = 64 << 20  # SSD_PREFILL_NOALLOC_MAX_BYTES

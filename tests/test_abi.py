@@ -121,6 +121,25 @@ def test_forced_path_and_check_reject_before_any_hip_call():
     assert L.ssd_prefill_check(P0, 255, None) == WS           # smaller than the control block
 
 
+def test_timed_prefill_rejects_before_any_hip_call():
+    import ctypes
+    L = ssd.lib()
+    args = [P0, P0, P0, P0, P0, None, None, 0, None, None, None, P0, BF, F, 1, 300, 4, 64, 64, 1, 64, 0, 0, 0, 0,
+            P0, 1 << 30, None, ssd.PATH_AUTO, -1]
+    ev = (ctypes.c_void_p * 2)(P0, P0)
+    null_in = (ctypes.c_void_p * 2)(P0, None)
+    n = ctypes.c_int(-7)
+    assert L.ssd_prefill_timed(*args, ev, ev, None, -1, ctypes.byref(n)) == INV   # negative capacity
+    assert L.ssd_prefill_timed(*args, None, ev, None, 2, ctypes.byref(n)) == INV  # no start events
+    assert L.ssd_prefill_timed(*args, ev, None, None, 2, ctypes.byref(n)) == INV  # no stop events
+    assert L.ssd_prefill_timed(*args, ev, null_in, None, 2, ctypes.byref(n)) == INV  # a NULL event
+    assert n.value == -7                                    # untouched by a rejected call
+    bad = list(args)
+    bad[-2] = 9                                             # no such path: the prefill's own check
+    assert L.ssd_prefill_timed(*bad, ev, ev, None, 2, ctypes.byref(n)) == INV
+    assert n.value == 0                                     # nothing launched
+
+
 def _prefill(**kw):
     a = dict(x=P0, dt=P0, A=P0, B=P0, C=P0, D=None, h0=None, hT=None, y=P0, dtype=BF, batch=1, seqlen=300,
              nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, ws=P0, wsb=1 << 30, stream=None)
