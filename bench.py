@@ -459,16 +459,17 @@ def cpu_baseline(s, inp, min_seconds=10.0, max_reps=2000):
     f64 = {k: (None if inp[k] is None else np.ascontiguousarray(inp[k], np.float64))
            for k in ("x", "dt", "A", "B", "C", "D", "h0")}
     ref.load()
-    reps, total = 0, 0.0
-    while reps < max_reps and (total < min_seconds or reps == 0):
+    times = []
+    while len(times) < max_reps and (sum(times) < min_seconds or not times):
         t0 = time.perf_counter()
         ref.prefill(f64["x"], f64["dt"], f64["A"], f64["B"], f64["C"], f64["D"], f64["h0"], nthreads=cores)
-        total += time.perf_counter() - t0
-        reps += 1
-    tokens = s.batch * s.seqlen * reps
-    return {"value": tokens / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        times.append(time.perf_counter() - t0)
+    tokens = s.batch * s.seqlen
+    med = sorted(times)[len(times) // 2]
+    return {"value": tokens / med, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "mean_tokens_per_s": tokens * len(times) / sum(times),
             "sample": f"the full workload ({s.batch}x{s.seqlen} tokens, all {s.nheads} heads), fp64 sequential "
-                      f"recurrence, repeated {reps}x ({total:.1f} s)"}
+                      f"recurrence, repeated {len(times)}x ({sum(times):.1f} s); value: the median repetition"}
 
 
 # ---------------------------------------------------------------------------- decode
