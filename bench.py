@@ -10,7 +10,8 @@ from the step before; one marker pair brackets the block.  Each step goes throug
 ssd_prefill_timed, which binds HIP events to every kernel launch itself (the kernel's own
 start and end, no marker between launches): the per-kernel durations and the roofline come
 from them.  The 130M- and 370M-shaped layers are timed the same way and reported under
-"workloads"; the decode update (batch 64, 80 heads, 1024 tokens) under "decode".
+"workloads"; the same 2.7B-shaped step with x, B and C stored as fp8 e4m3 under
+"fp8_inputs"; the decode update (batch 64, 80 heads, 1024 tokens) under "decode".
 
 Prints ONE JSON line.  The oracle (fp64 CPU recurrence) is timed on the host's cores on the
 same workload as "cpu_baseline".
@@ -18,6 +19,7 @@ same workload as "cpu_baseline".
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import gc
 import hashlib
 import json
@@ -51,18 +53,18 @@ KERNEL_SOURCES = {
 
 def scan_kernel_name(s, ncu=None) -> str:
     """The chunk-scan kernel the library launches for this shape: the one-round kernel when
-    every (b, h, chunk) item fits at two per compute unit (bf16, 256-token chunks, P = 64),
-    else the pipelined persistent one (bf16, 256-token chunks, P = 64, N = 128) or the
+    every (b, h, chunk) item fits at two per compute unit (bf16 or fp8, 256-token chunks,
+    P = 64), else the pipelined persistent one (bf16 or fp8, 256-token chunks, P = 64, N = 128) or the
     persistent one (the same rule as the library's launcher).  ncu: compute units (default:
     the current device's)."""
     if ncu is None:
         import torch
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
     nitems = s.batch * s.nheads * -(-s.seqlen // s.chunk)
-    small = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and nitems <= 2 * ncu
+    small = s.dtype in ("bf16", "fp8") and s.chunk == 256 and s.headdim == 64 and nitems <= 2 * ncu
     if small:
         return "chunk_scan_small_kernel"
-    pipe = s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and s.dstate == 128
+    pipe = s.dtype in ("bf16", "fp8") and s.chunk == 256 and s.headdim == 64 and s.dstate == 128
     return "chunk_scan_pipe_kernel" if pipe else "chunk_scan_kernel"
 
 
@@ -74,9 +76,9 @@ def passing_in_scan(s, ncu=None) -> bool:
 
 def chunk_state_pair(s) -> bool:
     """Whether ssd_prefill's first launch (cumulative decay, chunk states and GEMM1) takes two
-    heads of a group per workgroup: bf16, 256-token chunks, P = 64 and an even number of heads
+    heads of a group per workgroup: bf16 or fp8, 256-token chunks, P = 64 and an even number of heads
     per group (the same rule as the library)."""
-    return s.dtype == "bf16" and s.chunk == 256 and s.headdim == 64 and (s.nheads // s.ngroups) % 2 == 0
+    return s.dtype in ("bf16", "fp8") and s.chunk == 256 and s.headdim == 64 and (s.nheads // s.ngroups) % 2 == 0
 
 
 def step_kernels(s, ncu=None) -> list:
@@ -99,22 +101,24 @@ def alg_counts(s: synth.PrefillShape, ncu=None) -> dict:
     chunk), C.B^T once per group, multiply-add = 2 flops.
     """
     B, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
-    ib = 2 if s.dtype == "bf16" else 4
+    ib = {"bf16": 2, "fp8": 1, "f32": 4}[s.dtype]   # x, B and C
+    db = 4 if s.dtype == "f32" else 2               # dt (bf16 beside fp8 inputs)
+    hb = 4 if s.dtype == "f32" else 2               # intermediates: fp16 for bf16 and fp8 inputs
     nc = -(-L // Q)
     x = B * L * H * P * ib
-    dt = B * L * H * ib
+    dt = B * L * H * db
     bc = B * L * G * N * ib            # one of B or C
     y = B * L * H * P * 4
     chunk_tab = 2 * B * H * nc * Q * 4  # dA_cum + dt regrouped per chunk
-    states = B * H * nc * P * N * ib   # chunk / entering states: fp16 for bf16 inputs, fp32 otherwise
+    states = B * H * nc * P * N * hb   # chunk / entering states
     hen = states
     st = B * H * P * N * 4
     h0 = st if s.init_state != "zero" else 0
     tri = Q * (Q + 1)                  # 2 flops x Q(Q+1)/2 pairs
     # C.B^T products as the GEMM1 kernel stores them: per (b, g, chunk), 512 values per
     # 32-column step of each 16-row tile (the steps on or below the diagonal), fp16 for
-    # bf16 inputs and fp32 for fp32 inputs
-    cb = B * G * nc * sum(t // 2 + 1 for t in range(Q // 16)) * 512 * (2 if s.dtype == "bf16" else 4)
+    # bf16 and fp8 inputs and fp32 for fp32 inputs
+    cb = B * G * nc * sum(t // 2 + 1 for t in range(Q // 16)) * 512 * hb
     k = {
         "chunk_cumsum_kernel": dict(bytes=dt + chunk_tab, flops=2 * B * L * H),
         "chunk_state_kernel": dict(bytes=x + bc + chunk_tab + states, flops=2 * B * H * L * P * N),
@@ -340,7 +344,8 @@ def launch_cold(torch, fn, n, flush, before=None):
 
 
 def prefill_buffers(torch, s, inp):
-    g = {k: synth.to_torch(inp[k], s.dtype) for k in ("x", "dt", "B", "C")}
+    g = {k: synth.to_torch(inp[k], s.dtype) for k in ("x", "B", "C")}
+    g["dt"] = synth.to_torch(inp["dt"], synth.dt_dtype(s.dtype))
     g["A"] = torch.from_numpy(inp["A"]).cuda()
     g["D"] = torch.from_numpy(inp["D"]).cuda()
     g["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).cuda()
@@ -352,7 +357,7 @@ def prefill_buffers(torch, s, inp):
     g["dtc"] = torch.empty_like(g["acum"])
     # chunk states, then (in place) entering states: fp16 for bf16 inputs, fp32 otherwise
     g["states"] = torch.empty((s.batch, s.nheads, nc, s.headdim, s.dstate),
-                              dtype=torch.float16 if s.dtype == "bf16" else torch.float32, device="cuda")
+                              dtype=torch.float32 if s.dtype == "f32" else torch.float16, device="cuda")
     g["hen"] = g["states"]
     g["cb"] = torch.empty(ssd.chunk_gemm1_size(s.batch, s.seqlen, s.ngroups, s.chunk) // 4, dtype=torch.float32,
                           device="cuda")
@@ -681,13 +686,15 @@ def roofline_of(step, s, wl):
             "intensity_flop_per_method_byte": d["alg_flops"] / d["method_bytes"]}
 
 
-def bench_prefill_workload(torch, wl, steps, warmup, flush):
+def bench_prefill_workload(torch, wl, steps, warmup, flush, dtype=None):
     """Timed prefill steps of one workload, every launch timed, and its roofline.
 
     The timed region is ``steps`` prefills back to back over a rotation of buffer sets, each
-    through ssd_prefill_timed.  Returns (record, inputs, buffer sets, wall seconds of the
-    timed region)."""
+    through ssd_prefill_timed.  ``dtype`` stores the inputs in another type (the same draw,
+    rounded to it).  Returns (record, inputs, buffer sets, wall seconds of the timed region)."""
     s = synth.WORKLOADS[wl]
+    if dtype is not None:
+        s = dataclasses.replace(s, dtype=dtype)
     inp = synth.prefill_inputs(s, synth.SEED_BASE + wl)
     g = prefill_buffers(torch, s, inp)
     sets = rotation(torch, g, s)
@@ -712,6 +719,8 @@ def bench_prefill_workload(torch, wl, steps, warmup, flush):
     step = step_summary(us, t, s, counts)
     step["buffer_sets"] = len(sets)
     roof = roofline_of(step, s, wl)
+    if dtype is not None:  # the committed counter summaries are of the workload's own input type
+        roof["traffic"] = None
     # on one buffer set: what stays in the Infinity Cache between steps helps
     step["one_buffer_set_us_per_step"] = time_block(torch, [lambda: run_prefill(g, s)], steps, flush)
     # bf16 y (the fp32 result rounded once): halves the largest stream
@@ -756,6 +765,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-input variant of the step")
     ap.add_argument("--only", choices=["prefill", "chunk_scan_kernel", "chunk_scan_pipe_kernel", "chunk_state_kernel", "state_passing_kernel",
                                        "chunk_cumsum_kernel", "chunk_gemm1_kernel", "chunk_scan_small_kernel",
                                        "single_pass", "step", "cached", "copy"],
@@ -841,6 +851,16 @@ def main():
         out["single_pass"] = sp
     out["layer_rows"] = bench_layer_rows(torch, s, sets[0], flush, args.steps)
     del sets
+    if s.dtype == "bf16" and not args.no_fp8:
+        # the same workload with x, B and C stored as fp8 e4m3 (dt bf16): the same kernels,
+        # half the bytes of the largest inputs
+        r8, _, g8, _ = bench_prefill_workload(torch, args.workload, args.steps, args.warmup, flush, dtype="fp8")
+        p8 = r8["prefill"]
+        out["fp8_inputs"] = {"us_per_step": p8["us_per_step"], "tokens_per_s": p8["tokens_per_s"],
+                             "method_bytes": p8["method_bytes"], "hbm_frac_method_bytes": p8["hbm_frac_method_bytes"],
+                             "kernel_us_sum": p8["kernel_us_sum"], "roofline": r8["roofline"],
+                             "launches": p8["launches"]}
+        del g8
     if not args.no_extra:
         out["workloads"] = {}
         for wl in EXTRA_WORKLOADS:

@@ -35,9 +35,13 @@
  *   SSD_ERR_HIP means a launch failed; faults inside a kernel surface at the
  *   caller's next synchronisation.
  * - `in_dtype` selects the storage type of x, dt, B, C (and z): SSD_BF16 (uint16 bit
- *   patterns of bfloat16) or SSD_F32.  A and D are always fp32; the initial and final
- *   states and y are fp32 (y may be bf16 through the _ex calls).  Accumulation is fp32.
- * - Precision inside a prefill (bf16 inputs): the matrix-core operands are fp16 (the inputs
+ *   patterns of bfloat16) or SSD_F32; or SSD_FP8_E4M3, where x, B and C are OCP fp8 e4m3
+ *   codes (one byte: sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities, the
+ *   codes 0x7f and 0xff are NaN) and dt and z stay bf16.  fp8 inputs take the bf16 paths
+ *   (they widen exactly to fp16) and halve the bytes of x, B and C; the single-pass prefill
+ *   path does not take them.  A and D are always fp32; the initial and final states and y are
+ *   fp32 (y may be bf16 through the _ex calls, never fp8).  Accumulation is fp32.
+ * - Precision inside a prefill (bf16 and fp8 inputs): the matrix-core operands are fp16 (the inputs
  *   convert exactly; computed operands -- the masked scores, the weighted B or X, the
  *   entering state of the off-diagonal product -- are rounded once).  Between kernels the
  *   staged and one-round paths keep the chunk and entering states in fp16; the single-pass
@@ -66,7 +70,7 @@
 extern "C" {
 #endif
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_FP8_E4M3 = 2 } ssd_dtype_t;
 
 enum {
     SSD_OK = 0,

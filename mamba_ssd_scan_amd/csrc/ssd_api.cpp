@@ -62,9 +62,16 @@ int check_shape(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     return SSD_OK;
 }
 
-int check_dtype(ssd_dtype_t t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK : SSD_ERR_INVALID_ARG; }
+// input storage (x, B, C): fp32, bf16 or fp8 e4m3; y: fp32 or bf16
+int check_dtype(ssd_dtype_t t)
+{
+    return (t == SSD_F32 || t == SSD_BF16 || t == SSD_FP8_E4M3) ? SSD_OK : SSD_ERR_INVALID_ARG;
+}
+int check_ydtype(ssd_dtype_t t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK : SSD_ERR_INVALID_ARG; }
 
-size_t in_size(ssd_dtype_t t) { return t == SSD_BF16 ? 2 : 4; }
+// bytes of one x, B or C element; of one dt or z element (bf16 beside fp8 inputs)
+size_t in_size(ssd_dtype_t t) { return t == SSD_BF16 ? 2 : t == SSD_FP8_E4M3 ? 1 : 4; }
+size_t dt_size(ssd_dtype_t t) { return t == SSD_F32 ? 4 : 2; }
 
 struct WsLayout {
     size_t ctl, acum, dtc, states, cb, sync, total;  // byte offsets of each region, then total bytes
@@ -157,7 +164,7 @@ ssd::Dims make_dims(int batch, int seqlen, int nheads, int headdim, int dstate, 
     ssd::Dims d;
     d.B = batch; d.L = seqlen; d.H = nheads; d.P = headdim; d.N = dstate; d.G = ngroups; d.Q = chunk;
     d.nc = chunk > 0 ? (int)(((long long)seqlen + chunk - 1) / chunk) : 0;
-    d.bf16 = (t == SSD_BF16);
+    d.in = t == SSD_FP8_E4M3 ? ssd::kInFp8 : t == SSD_BF16 ? ssd::kInBf16 : ssd::kInF32;
     d.sx = nheads * headdim; d.sbc = ngroups * dstate; d.sdt = nheads; d.sz = nheads * headdim;
     return d;
 }
@@ -170,13 +177,13 @@ int check_step_args(const float *state, const void *x, const void *dt, const flo
                     ssd_dtype_t in_dtype, ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int dstate,
                     int ngroups)
 {
-    if (check_dtype(in_dtype) != SSD_OK || check_dtype(y_dtype) != SSD_OK) return SSD_ERR_INVALID_ARG;
+    if (check_dtype(in_dtype) != SSD_OK || check_ydtype(y_dtype) != SSD_OK) return SSD_ERR_INVALID_ARG;
     const int st = check_shape(batch, -1, nheads, headdim, dstate, ngroups, 0, false);
     if (st != SSD_OK) return st;
     if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
-    const size_t es = in_size(in_dtype);
-    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, es) || !aligned(Bm, es) || !aligned(Cm, es) ||
-        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, in_size(y_dtype)) || !aligned(dt_bias, 4) || !aligned(z, es))
+    const size_t es = in_size(in_dtype), ds = dt_size(in_dtype);
+    if (!aligned(state, 16) || !aligned(x, es) || !aligned(dt, ds) || !aligned(Bm, es) || !aligned(Cm, es) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, in_size(y_dtype)) || !aligned(dt_bias, 4) || !aligned(z, ds))
         return SSD_ERR_INVALID_ARG;
     return SSD_OK;
 }
@@ -190,7 +197,7 @@ int check_step_args(const float *state, const void *x, const void *dt, const flo
 int check_seq_inputs(const void *x, const void *dt, const void *Bm, ssd_dtype_t t)
 {
     if (!x || !dt || !Bm) return SSD_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(Bm, 16) || !aligned(dt, in_size(t))) return SSD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(Bm, 16) || !aligned(dt, dt_size(t))) return SSD_ERR_INVALID_ARG;
     return SSD_OK;
 }
 
@@ -211,7 +218,7 @@ const char *ssd_status_string(int status)
     }
 }
 
-int ssd_version(void) { return (4 << 16) | 3; }
+int ssd_version(void) { return (4 << 16) | 4; }
 
 size_t ssd_prefill_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                   int ngroups, int chunk)
@@ -228,7 +235,7 @@ int ssd_chunk_cumsum(const void *dt, const float *A, float *dA_cum, float *dt_c,
     SSD_TRY(check_shape(batch, seqlen, nheads, 64, 64, 1, chunk, true));
     if (seqlen == 0) return SSD_OK;
     if (!dt || !A || !dA_cum || !dt_c) return SSD_ERR_INVALID_ARG;
-    if (!aligned(dt, in_size(in_dtype)) || !aligned(A, 4) || !aligned(dA_cum, 16) || !aligned(dt_c, 16))
+    if (!aligned(dt, dt_size(in_dtype)) || !aligned(A, 4) || !aligned(dA_cum, 16) || !aligned(dt_c, 16))
         return SSD_ERR_INVALID_ARG;
     const ssd::Dims d = make_dims(batch, seqlen, nheads, 64, 64, 1, chunk, in_dtype);
     return hip_status(ssd::launch_chunk_cumsum(dt, A, dA_cum, dt_c, d, (hipStream_t)hip_stream));
@@ -355,7 +362,7 @@ int prefill_padded(const void *x, const void *dt, const float *A, const void *Bm
     const PadWs w = pad_ws(batch, seqlen, nheads, headdim, dstate, ngroups, chunk);
     if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    const int es = (int)in_size(in_dtype), ys = (int)in_size(y_dtype);
+    const int es = (int)in_size(in_dtype), ds = (int)dt_size(in_dtype), ys = (int)in_size(y_dtype);
     const long long tok = (long long)batch * seqlen;
     const int Pp = q.P * q.split;  // padded channels of one head
     auto pad = [&](const void *src, size_t off, int e, long long nout, int nin_s, int nin_d, int slen, int dlen,
@@ -363,7 +370,7 @@ int prefill_padded(const void *x, const void *dt, const float *A, const void *Bm
         return hip_status(ssd::launch_pad_copy(src, ws + off, e, nout, nin_s, nin_d, slen, dlen, so, si, sk, s));
     };
     SSD_TRY(pad(x, w.x, es, tok, nheads, nheads, headdim, Pp, sx, headdim, 1));
-    if (z) SSD_TRY(pad(z, w.z, es, tok, nheads, nheads, headdim, Pp, sz, headdim, 1));
+    if (z) SSD_TRY(pad(z, w.z, ds, tok, nheads, nheads, headdim, Pp, sz, headdim, 1));
     SSD_TRY(pad(Bm, w.b, es, tok, ngroups, ngroups, dstate, q.N, sbc, dstate, 1));
     SSD_TRY(pad(Cm, w.c, es, tok, ngroups, ngroups, dstate, q.N, sbc, dstate, 1));
     // per-head parameters of split heads: each value twice, in place for both halves
@@ -371,7 +378,7 @@ int prefill_padded(const void *x, const void *dt, const float *A, const void *Bm
     const float *A2 = A, *D2 = D, *bias2 = dt_bias;
     long long dt_stride2 = sdt;
     if (q.split == 2) {
-        SSD_TRY(pad(dt, w.dt, es, tok, nheads, nheads, 2, 2, sdt, 1, 0));
+        SSD_TRY(pad(dt, w.dt, ds, tok, nheads, nheads, 2, 2, sdt, 1, 0));
         SSD_TRY(pad(A, w.A, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
         if (D) SSD_TRY(pad(D, w.D, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
         if (dt_bias) SSD_TRY(pad(dt_bias, w.bias, 4, 1, nheads, nheads, 2, 2, 0, 1, 0));
@@ -407,9 +414,9 @@ int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, 
                  long long spin_limit)
 {
     SSD_TRY(check_dtype(in_dtype));
-    SSD_TRY(check_dtype(y_dtype));
+    SSD_TRY(check_ydtype(y_dtype));
     if (path < SSD_PATH_AUTO || path > SSD_PATH_STAGED_ONE_HEAD) return SSD_ERR_INVALID_ARG;
-    if (!aligned(dt_bias, 4) || !aligned(z, in_size(in_dtype))) return SSD_ERR_INVALID_ARG;
+    if (!aligned(dt_bias, 4) || !aligned(z, dt_size(in_dtype))) return SSD_ERR_INVALID_ARG;
     SSD_TRY(check_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, true));
     // token strides: 0 = dense; x, B and C rows are read with 16-byte loads
     const long long esz = (long long)in_size(in_dtype), hp = (long long)nheads * headdim,
@@ -418,8 +425,9 @@ int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, 
                     sdt = dt_stride ? dt_stride : nheads, sz = z_stride ? z_stride : hp;
     if (sx < hp || sbc < gn || sdt < nheads || sz < hp) return SSD_ERR_INVALID_ARG;
     if ((sx * esz) % 16 != 0 || (sbc * esz) % 16 != 0) return SSD_ERR_INVALID_ARG;
-    const long long smax = std::max(std::max(sx, sbc), std::max(sdt, sz));
-    if ((long long)chunk * esz * smax >= 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;  // 32-bit offsets per chunk
+    const long long dsz = (long long)dt_size(in_dtype);
+    const long long smax = std::max(std::max(sx * esz, sbc * esz), std::max(sdt * dsz, sz * dsz));  // bytes
+    if ((long long)chunk * smax >= 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;  // 32-bit offsets per chunk
     if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)hip_stream;
     if (seqlen == 0) {
@@ -623,8 +631,9 @@ int ssd_decode_graph_create(ssd_decode_graph **out, int nsteps, float *state, co
     SSD_TRY(check_step_args(state, x, dt, A, Bm, Cm, D, dt_bias, z, y, in_dtype, y_dtype, batch, nheads, headdim,
                             dstate, ngroups));
     // Byte strides of one token's slot in the step-major buffers.
-    const size_t es = in_size(in_dtype);
-    const size_t sx = (size_t)batch * nheads * headdim * es, sdt = (size_t)batch * nheads * es;
+    const size_t es = in_size(in_dtype), ds = dt_size(in_dtype);
+    const size_t sx = (size_t)batch * nheads * headdim * es, sdt = (size_t)batch * nheads * ds;
+    const size_t sz = (size_t)batch * nheads * headdim * ds;
     const size_t sbc = (size_t)batch * ngroups * dstate * es;
     const size_t sy = (size_t)batch * nheads * headdim * in_size(y_dtype);
     const ssd::Dims d = make_dims(batch, 1, nheads, headdim, dstate, ngroups, 1, in_dtype);
@@ -639,7 +648,7 @@ int ssd_decode_graph_create(ssd_decode_graph **out, int nsteps, float *state, co
     if (e == hipSuccess) {
         hipError_t le = hipSuccess;
         for (int t = 0; t < nsteps && le == hipSuccess; ++t) {
-            const char *zt = z ? static_cast<const char *>(z) + t * sx : nullptr;
+            const char *zt = z ? static_cast<const char *>(z) + t * sz : nullptr;
             const ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, zt, y_dtype == SSD_BF16 ? 1 : 0};
             le = ssd::launch_step(state, static_cast<const char *>(x) + t * sx, static_cast<const char *>(dt) + t * sdt,
                                   A, static_cast<const char *>(Bm) + t * sbc, static_cast<const char *>(Cm) + t * sbc,

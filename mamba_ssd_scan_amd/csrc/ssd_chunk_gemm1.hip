@@ -72,7 +72,8 @@ static hipError_t launch_gemm1_t(const void *Bm, const void *Cm, void *cb, const
 
 hipError_t launch_chunk_gemm1(const void *Bm, const void *Cm, void *cb, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_gemm1_t<bf16_t>(Bm, Cm, cb, d, s) : launch_gemm1_t<float>(Bm, Cm, cb, d, s);
+    if (d.in == kInFp8) return launch_gemm1_t<fp8_t>(Bm, Cm, cb, d, s);
+    return d.in == kInBf16 ? launch_gemm1_t<bf16_t>(Bm, Cm, cb, d, s) : launch_gemm1_t<float>(Bm, Cm, cb, d, s);
 }
 
 }  // namespace ssd

@@ -60,7 +60,8 @@ template <typename TIn, int P, int N, int NW> struct ScanLds {
     // surplus loads of streaming wavefronts with less to stream (each issues the same count)
     static constexpr int SX = ROWS * P * 2, SH = P * N * 2, ST = 2 * ROWS * 4, SD = 1024;
     static constexpr int SALL = SX + SH + ST + SD;
-    static constexpr bool STAGE = !F32 && base + SALL <= 160 * 1024;
+    // (fp8 inputs: no staging; their rows are loaded into registers and widened)
+    static constexpr bool STAGE = !F32 && std::is_same<TIn, bf16_t>::value && base + SALL <= 160 * 1024;
     static constexpr int bytes = base + (STAGE ? SALL : 0);
 };
 
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     float cf[F32 ? KS : 1];
     f16x8 gs[F32 ? 1 : NSMAX - 1];  // the steps below the diagonal
     f16x8 gdg;                      // the diagonal step
-    bool cfresh = false;  // cb holds newly loaded bf16 rows (wavefront-uniform)
+    bool cfresh = false;  // cb holds newly loaded raw rows (wavefront-uniform)
     // Issued when an item's chunk or group differs from the previous item's, at the end of
     // the previous item.  A wavefront without a tile reads slice 0 and C rows past the buffer
     // range, which return zeros.
@@ -312,8 +313,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
 #pragma unroll
             for (int s = 0; s < NSMAX - 1; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
             gdg = *reinterpret_cast<const f16x8 *>(gq + (size_t)slast * 512);
+            if constexpr (std::is_same<TIn, fp8_t>::value) {
+                // e4m3 rows (8 bytes per 8 elements) in the low half, widened with the bf16 rows
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint2 v = buf_load8(rc, row + ks * 32 + 8 * lg);
+                    cb[ks] = __builtin_bit_cast(bf16x8, make_uint4(v.x, v.y, 0u, 0u));
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+            }
             cfresh = true;
         }
     };
@@ -398,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
                     // (exact for bf16 inputs in fp16 range)
                     if (cfresh) {
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(cb[ks]));
+                        for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, held_to_f16x8<TIn>(cb[ks]));
                         cfresh = false;
                     }
                 }
@@ -553,8 +563,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
         }
         // ---- optional output gate: y <- y * z * sigmoid(z), z laid out as x
         if (OPT && opt.z && t >= 0) {
-            const TIn *zp = static_cast<const TIn *>(opt.z) + ((size_t)cur.b * L + cur.tc) * sz + (size_t)cur.h * P;
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * sz + P) * sizeof(TIn)));
+            typedef typename Traits<TIn>::dt_t zt;  // bf16 beside fp8 inputs
+            const zt *zp = static_cast<const zt *>(opt.z) + ((size_t)cur.b * L + cur.tc) * sz + (size_t)cur.h * P;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zp, (uint32_t)(((cur.vrows - 1) * sz + P) * sizeof(zt)));
             // all of the lane's z values are requested before the first is used
             uint32_t zr[TP][4];
 #pragma unroll
@@ -587,7 +598,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
     }
 }
 
-// ---- The pipelined chunk scan (bf16 inputs, P = 64, N = 128, 256-token chunks): the same
+// ---- The pipelined chunk scan (bf16 or fp8 inputs, P = 64, N = 128, 256-token chunks): the same
 // arithmetic in the same order as chunk_scan_kernel (the compiler may contract the decay
 // table's multiply-add differently, a last-bit difference in a few table entries), with one
 // barrier per item instead of two.  The compute layout is double-buffered: while every
@@ -607,11 +618,12 @@ template <int P, int N, int NW> struct PipeLds {
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
-// GATE: the z gate is applied; Y16: y is stored as bf16.  Each combination is its own
-// instantiation, so the plain and the bf16-y kernels carry no registers for the gate.
-template <int P, int N, int NW, bool GATE, bool Y16>
+// TX: storage of x and C (bf16, or fp8 e4m3: half the raw X bytes to stream; both widen to
+// fp16 exactly).  GATE: the z gate is applied; Y16: y is stored as bf16.  Each combination is
+// its own instantiation, so the plain and the bf16-y kernels carry no registers for the gate.
+template <typename TX, int P, int N, int NW, bool GATE, bool Y16>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
+    const TX *__restrict__ x, const TX *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
     const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sz,
     int Q, int nc, int nitems)
@@ -620,7 +632,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
     constexpr int ROWS = S::ROWS, LDX = S::LDX, LDH = S::LDH, TAB = S::TAB;
     constexpr int TP = P / 16, KS = N / 32, NSMAX = NW / 2;
     constexpr int NL = NW / 2;            // streaming wavefronts: the light row tiles
-    constexpr int XI = S::SX / 1024;      // 1 KB X slots; wavefront q owns slots q, q + NL, ...
+    constexpr bool F8 = std::is_same<TX, fp8_t>::value;
+    constexpr int RB = P * (int)sizeof(TX);                  // bytes of one raw X row
+    constexpr int XI = ROWS * RB / 1024;  // 1 KB X slots; wavefront q owns slots q, q + NL, ...
     constexpr int TI = ROWS / 64;         // 64-row table blocks; wavefront q < TI owns block q
     static_assert(NW == 16 && 2 * N == 256 && XI % NL == 0 && P % NL == 0 && TI <= NL, "pipelined scan shape");
     __shared__ __align__(16) f16 xs0[S::XS];
@@ -690,12 +704,12 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
         const int ln = lane + opaque_zero();
         const __amdgpu_buffer_rsrc_t rx =
             make_rsrc(x + ((size_t)it.b * L + it.tc) * sx + (size_t)it.h * P,
-                      live ? (uint32_t)(((it.vrows - 1) * sx + P) * 2) : 0u);
+                      live ? (uint32_t)(((it.vrows - 1) * sx + P) * sizeof(TX)) : 0u);
 #pragma unroll
         for (int k = 0; k < XI / NL; ++k) {
             const int wi = k * NL + wave;
-            const int byte = 1024 * wi + 16 * ln, row = byte / (2 * P), col = byte % (2 * P);
-            buf_load_lds16(rx, stg + 1024 * wi, (uint32_t)(row * sx * 2 + col));
+            const int byte = 1024 * wi + 16 * ln, row = byte / RB, col = byte % RB;
+            buf_load_lds16(rx, stg + 1024 * wi, (uint32_t)(row * sx * (int)sizeof(TX) + col));
         }
         const __amdgpu_buffer_rsrc_t rh =
             make_rsrc(static_cast<const f16 *>(henv) + it.bhc * P * N, live ? (uint32_t)(P * N * 2) : 0u);
@@ -717,10 +731,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
         const int ln = lane + opaque_zero();
 #pragma unroll
         for (int k = 0; k < XI / NL; ++k) {
-            const int u = 64 * (k * NL + wave) + ln;  // 16-byte unit: row u / (P / 8), channels 8 (u % (P / 8))
-            Raw8<bf16_t> r;
-            r.v = *reinterpret_cast<const uint4 *>(stg + 16 * u);
-            *reinterpret_cast<uint4 *>(&xsn[(u / (P / 8)) * LDX + 8 * (u % (P / 8))]) = raw8_to_f16x8(r);
+            const int u = 64 * (k * NL + wave) + ln;  // 16-byte unit of the staged rows
+            const uint4 r = *reinterpret_cast<const uint4 *>(stg + 16 * u);
+            if constexpr (F8) {
+                // 16 channels: row u / (P / 16), channels 16 (u % (P / 16)) onwards
+                f16 *dst = &xsn[(u / (P / 16)) * LDX + 16 * (u % (P / 16))];
+                *reinterpret_cast<uint4 *>(dst) = f8x8_to_f16x8(make_uint2(r.x, r.y));
+                *reinterpret_cast<uint4 *>(dst + 8) = f8x8_to_f16x8(make_uint2(r.z, r.w));
+            } else {
+                // 8 channels: row u / (P / 8), channels 8 (u % (P / 8)) onwards
+                Raw8<bf16_t> rr;
+                rr.v = r;
+                *reinterpret_cast<uint4 *>(&xsn[(u / (P / 8)) * LDX + 8 * (u % (P / 8))]) = raw8_to_f16x8(rr);
+            }
         }
         if (wave < TI) {
             const float *sta = reinterpret_cast<const float *>(stg + S::SX);
@@ -746,7 +769,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
     bool cfresh = false;
     auto load_tile_operands = [&](const Item &it) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)it.b * L + it.tc) * sbc + (size_t)it.g * N,
-                                                    (uint32_t)(((it.vrows - 1) * sbc + N) * 2));
+                                                    (uint32_t)(((it.vrows - 1) * sbc + N) * sizeof(TX)));
         const uint32_t row = (uint32_t)((ibase + li) * sbc);
         const size_t slice0 = (((size_t)it.b * G + it.g) * nc + it.c) * (size_t)spc + Tt;
         const f16 *gq = static_cast<const f16 *>(cbg) + (slice0 * 64 + lane) * 8;
@@ -754,8 +777,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
 #pragma unroll
         for (int s = 0; s < NSMAX - 1; ++s) gs[s] = *reinterpret_cast<const f16x8 *>(gq + (size_t)min(s, slast) * 512);
         gdg = *reinterpret_cast<const f16x8 *>(gq + (size_t)slast * 512);
+        if constexpr (F8) {
+            // e4m3 rows (8 bytes per 8 elements) in the low half, widened with the bf16 rows
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint2 v = buf_load8(rc, row + ks * 32 + 8 * lg);
+                cb[ks] = __builtin_bit_cast(bf16x8, make_uint4(v.x, v.y, 0u, 0u));
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+        }
         cfresh = true;
     };
 
@@ -796,7 +828,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
         const float ai = acs[irow];
         if (cfresh) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(cb[ks]));
+            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, held_to_f16x8<TX>(cb[ks]));
             cfresh = false;
         }
 #pragma unroll
@@ -940,12 +972,12 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
     const int nitems = d.nc * d.H * d.B;
     const TIn *xx = static_cast<const TIn *>(x), *cc = static_cast<const TIn *>(Cm);
     // bf16, P = 64, N = 128, 256-token chunks: the pipelined kernel, one workgroup per CU
-    if constexpr (std::is_same<TIn, bf16_t>::value && P == 64) {
+    if constexpr ((std::is_same<TIn, bf16_t>::value || std::is_same<TIn, fp8_t>::value) && P == 64) {
         if (d.N == 128 && d.Q == 256) {
             static_assert(PipeLds<64, 128, 16>::fits, "pipelined chunk scan LDS");
             const int nwg = nitems < ncu ? nitems : ncu;
 #define SSD_PIPE_LAUNCH(GT, YB)                                                                          \
-    launch_kernel("chunk_scan_pipe_kernel", chunk_scan_pipe_kernel<64, 128, 16, GT, YB>, nwg, 1024, s, xx, cc, \
+    launch_kernel("chunk_scan_pipe_kernel", chunk_scan_pipe_kernel<TIn, 64, 128, 16, GT, YB>, nwg, 1024, s, xx, cc, \
                   cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
             if (o.z && o.y_bf16)
                 SSD_PIPE_LAUNCH(true, true);
@@ -1037,8 +1069,9 @@ hipError_t launch_chunk_scan(const void *x, const void *Cm, const void *cb, cons
         return launch_chunk_scan_small(x, Cm, cb, acum, dtc, const_cast<void *>(h_enter), nullptr, nullptr, D, y, po,
                                        d, ncu, s);
     }
-    return d.bf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
-                  : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
+    if (d.in == kInFp8) return launch_scan_t<fp8_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
+    return d.in == kInBf16 ? launch_scan_t<bf16_t>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s)
+                           : launch_scan_t<float>(x, Cm, cb, acum, dtc, h_enter, D, y, o, d, ncu, s);
 }
 
 }  // namespace ssd

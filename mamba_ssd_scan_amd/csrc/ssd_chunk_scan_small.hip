@@ -41,9 +41,10 @@ constexpr int kDeviceCoherent = 16;
 // state to fin), then counts itself done in sync[b, h] (zeroed by the chunk-state launch) and
 // waits until all nc workgroups of the head are; all items are resident at once, so the wait
 // ends.
-template <int P, int N, bool OPT, int PNC>
+// TX: storage of x and C (bf16, or fp8 e4m3; both widen to fp16 exactly).
+template <typename TX, int P, int N, bool OPT, int PNC>
 __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves per SIMD: <= 128 VGPRs
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Cm, const void *__restrict__ cbg,
+    const TX *__restrict__ x, const TX *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, f16 *hen, const float *init, float *fin,
     unsigned *sync, const float *__restrict__ D, void *__restrict__ y, SsdOpts opt, int L, int H, int G, int sx, int sbc,
     int sz, int nc,
@@ -156,10 +157,10 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     // ---- the item's X rows (fp16), entering state and decay tables into LDS
     {
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * sx + (size_t)h * P,
-                                                    (uint32_t)(((vrows - 1) * sx + P) * 2));
+                                                    (uint32_t)(((vrows - 1) * sx + P) * sizeof(TX)));
         constexpr int XU = ROWS * (P / 8), XPT = XU / NT;
         constexpr int HU = P * N / 8, HPT = (HU + NT - 1) / NT;
-        Raw8<bf16_t> px[XPT];
+        Raw8<TX> px[XPT];
         uint4 ph[HPT];
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     }
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + ((size_t)b * L + tc) * sbc + (size_t)g * N,
-                                                (uint32_t)(((vrows - 1) * sbc + N) * 2));
+                                                (uint32_t)(((vrows - 1) * sbc + N) * sizeof(TX)));
     const size_t base_y = (((size_t)b * L + tc) * H + h) * P;
     const bool y16 = OPT && opt.y_bf16;
     const uint32_t es = y16 ? 2u : 4u;
@@ -358,13 +359,20 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             bf16x8 cb[KS];
             const uint32_t row = (uint32_t)((ibase + li) * sbc);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (std::is_same<TX, fp8_t>::value) {  // e4m3: 8 bytes, in the low half
+                    const uint2 v = buf_load8(rc, row + ks * 32 + 8 * lg);
+                    cb[ks] = __builtin_bit_cast(bf16x8, make_uint4(v.x, v.y, 0u, 0u));
+                } else {
+                    cb[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
+                }
+            }
             f32x4 off[TP];
 #pragma unroll
             for (int pt = 0; pt < TP; ++pt) off[pt] = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 ch = bf16x8_to_f16x8(cb[ks]);
+                const f16x8 ch = held_to_f16x8<TX>(cb[ks]);
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) {
                     const f16x8 hf = *reinterpret_cast<const f16x8 *>(&hs[(pt * 16 + li) * LDH + ks * 32 + 8 * lg]);
@@ -427,7 +435,7 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
 
 // Whether the one-round kernel takes this problem: bf16 inputs, chunks of 256 tokens,
 // supported P, and no more items than two per compute unit.
-bool chunk_scan_small_shape(const Dims &d) { return d.bf16 && d.Q == 256 && d.P == 64 && d.N <= 128; }
+bool chunk_scan_small_shape(const Dims &d) { return d.half() && d.Q == 256 && d.P == 64 && d.N <= 128; }
 bool chunk_scan_small_fits(const Dims &d, int ncu)
 {
     return chunk_scan_small_shape(d) && (long)d.nc * d.H * d.B <= 2L * ncu;
@@ -451,7 +459,11 @@ hipError_t chunk_scan_small_resident(const Dims &d, const SsdOpts &o, int ncu, b
     hipError_t e = hipSuccess;
     const bool opt = o.z || o.y_bf16;
 #define SSD_SMALL_OCC(NN, OO, PP) \
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_scan_small_kernel<64, NN, OO, PP>, 512, 0)
+    e = d.in == kInFp8                                                                                    \
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_scan_small_kernel<fp8_t, 64, NN, OO, PP>, \
+                                                           512, 0)                                                 \
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_scan_small_kernel<bf16_t, 64, NN, OO, PP>, \
+                                                           512, 0)
 #define SSD_SMALL_OCC2(NN, PP)              \
     do {                                    \
         if (opt) SSD_SMALL_OCC(NN, true, PP); \
@@ -489,12 +501,18 @@ hipError_t launch_chunk_scan_small(const void *x, const void *Cm, const void *cb
     const int nsplit = (items > ncu && items <= 2 * ncu) ? min(items - ncu, 2 * ncu - items) / 8 * 8 : 0;
     const int nwhole = items - nsplit;
     const unsigned nitems = (unsigned)(nwhole + 2 * nsplit);  // workgroups
-    const bf16_t *xx = static_cast<const bf16_t *>(x), *cc = static_cast<const bf16_t *>(Cm);
     f16 *hh = static_cast<f16 *>(h);
-#define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                        \
-    launch_kernel("chunk_scan_small_kernel", chunk_scan_small_kernel<64, NN, OO, PP>, nitems, 512, s, xx, cc, \
-                  cb, acum, dtc, hh, init, fin, o.sync, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc,      \
-                  nwhole)
+#define SSD_SMALL_LAUNCH3(NN, OO, PP)                                                                            \
+    do {                                                                                                         \
+        if (d.in == kInFp8)                                                                                      \
+            launch_kernel("chunk_scan_small_kernel", chunk_scan_small_kernel<fp8_t, 64, NN, OO, PP>, nitems, 512, \
+                          s, static_cast<const fp8_t *>(x), static_cast<const fp8_t *>(Cm), cb, acum, dtc, hh,   \
+                          init, fin, o.sync, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc, nwhole);           \
+        else                                                                                                     \
+            launch_kernel("chunk_scan_small_kernel", chunk_scan_small_kernel<bf16_t, 64, NN, OO, PP>, nitems,     \
+                          512, s, static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(Cm), cb, acum, dtc, \
+                          hh, init, fin, o.sync, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.nc, nwhole);       \
+    } while (0)
 #define SSD_SMALL_LAUNCH2(NN, PP)                                                                            \
     do {                                                                                                     \
         if (o.z || o.y_bf16) SSD_SMALL_LAUNCH3(NN, true, PP);                                                \

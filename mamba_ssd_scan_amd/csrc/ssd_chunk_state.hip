@@ -44,7 +44,7 @@ namespace ssd {
 template <typename TIn, int P, int N, bool FUSE_CUMSUM, int GR, int JBT>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict__ x,
                                                           const TIn *__restrict__ Bm,
-                                                          const TIn *__restrict__ dt,
+                                                          const typename Traits<TIn>::dt_t *__restrict__ dt,
                                                           const float *__restrict__ A,
                                                           float *__restrict__ acum,
                                                           float *__restrict__ dtc,
@@ -249,12 +249,12 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
         if (wave == 0) {
             const long vq = (L - tc) < Q ? (L - tc) : Q;
             const __amdgpu_buffer_rsrc_t rd =
-                make_rsrc(dt + ((size_t)b * L + tc) * sdt + h, (uint32_t)(((vq - 1) * sdt + 1) * sizeof(TIn)));
+                make_rsrc(dt + ((size_t)b * L + tc) * sdt + h, (uint32_t)(((vq - 1) * sdt + 1) * sizeof(typename Tr::dt_t)));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 // (for k >= per this reads a neighbour's token, or zero past the range: unused,
                 // but a select here would become a branch, and a branch hides the load count)
-                const uint32_t off = (uint32_t)((lane * per + k) * sdt * sizeof(TIn));
+                const uint32_t off = (uint32_t)((lane * per + k) * sdt * sizeof(typename Tr::dt_t));
                 if constexpr (F32)
                     dtf[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)off, 0, 0));
                 else
@@ -401,8 +401,8 @@ static hipError_t launch_cs_n(const void *x, const void *Bm, const void *dt, con
                               bool big, hipStream_t s)
 {
     const dim3 grid(d.nc, d.H + (GR > 0 ? 4 * d.G : 0), d.B);
-    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *dd = static_cast<const TIn *>(dt),
-              *cc = static_cast<const TIn *>(Cm);
+    const TIn *xx = static_cast<const TIn *>(x), *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
+    const typename Traits<TIn>::dt_t *dd = static_cast<const typename Traits<TIn>::dt_t *>(dt);
 #define SSD_CS_LAUNCH(NN, JJ)                                                                                      \
     launch_kernel("chunk_state_kernel", chunk_state_kernel<TIn, P, NN, FUSE, GR, JJ>, grid, 256, s, xx, bb, \
                   dd, A, acum, dtc, states, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.Q, d.nc)
@@ -429,7 +429,7 @@ static hipError_t launch_cs_t(const void *x, const void *Bm, const void *dt, con
                               hipStream_t s)
 {
     // the kernels size their buffer ranges by the element type: never run one on the other's inputs
-    if (d.bf16 != (sizeof(TIn) == 2)) return hipErrorInvalidValue;
+    if (d.in != InOf<TIn>::v) return hipErrorInvalidValue;
     // More workgroups than two per compute unit: the smaller staged blocks (more resident
     // workgroups) pay off; otherwise the larger ones (fewer barriers).
     int dev = 0, ncu = 0;
@@ -451,8 +451,10 @@ hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, 
 {
     float *ac = const_cast<float *>(acum), *dc = const_cast<float *>(dtc);  // read-only in this mode
     const SsdOpts o = {nullptr, 0, nullptr, 0};
-    return d.bf16 ? launch_cs_t<bf16_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s)
-                  : launch_cs_t<float, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s);
+    if (d.in == kInFp8)
+        return launch_cs_t<fp8_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s);
+    return d.in == kInBf16 ? launch_cs_t<bf16_t, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s)
+                           : launch_cs_t<float, false, 0>(x, Bm, nullptr, nullptr, ac, dc, states, nullptr, nullptr, o, d, s);
 }
 
 template <typename TIn>
@@ -470,9 +472,10 @@ hipError_t launch_cumsum_chunk_state_gemm1(const void *x, const void *Bm, const 
                                            float *acum, float *dtc, void *states, const void *Cm, void *cb,
                                            const SsdOpts &o, const Dims &d, hipStream_t s, bool pair)
 {
-    if (!d.bf16) return launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    if (!d.half()) return launch_fused_t<float>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     if (pair && chunk_state_pair_fits(d))
         return launch_chunk_state_pair(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
+    if (d.in == kInFp8) return launch_fused_t<fp8_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
     return launch_fused_t<bf16_t>(x, Bm, dt, A, acum, dtc, states, Cm, cb, o, d, s);
 }
 

@@ -1,5 +1,5 @@
 // ssd_chunk_state_pair.hip -- Step-0 and Step-2 for two heads per workgroup, with the
-// Step-1 GEMM1 workgroups in the same grid: the prefill's first launch for bf16
+// Step-1 GEMM1 workgroups in the same grid: the prefill's first launch for bf16 and fp8
 // problems with 256-token chunks, P = 64 and an even number of heads per group.
 //
 // Same arithmetic, in the same order, as ssd_chunk_state.hip with the fused cumulative
@@ -23,11 +23,12 @@
 
 namespace ssd {
 
-template <int N>
+// TX: storage of x, B and C (bf16 or fp8 e4m3); dt is bf16 either way.
+template <typename TX, int N>
 __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Bm, const bf16_t *__restrict__ dt,
+    const TX *__restrict__ x, const TX *__restrict__ Bm, const bf16_t *__restrict__ dt,
     const float *__restrict__ A, float *__restrict__ acum, float *__restrict__ dtc, f16 *__restrict__ states,
-    const bf16_t *__restrict__ Cm, void *__restrict__ cb, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sdt,
+    const TX *__restrict__ Cm, void *__restrict__ cb, SsdOpts opt, int L, int H, int G, int sx, int sbc, int sdt,
     int nc)
 {
     constexpr int P = 64, Q = 256, JB = 64, NBLK = Q / JB;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     constexpr int XU = (JB / 2) * (P / 8);                      // units of two tokens x 8 channels, per head
     constexpr int BU = (JB / 2) * (N / 8), BPT = (BU + 511) / 512;  // of B, over the whole workgroup
     static_assert(XU == 256, "one X unit per thread of a head");
-    typedef Gemm1Chunk<bf16_t, N, 4, 256> G1;
+    typedef Gemm1Chunk<TX, N, 4, 256> G1;
     constexpr int kStateBytes = 2 * (2 * XSZ + BSZ) * 2 + 2 * Q * 4;
     constexpr int kBytes = G1::kLdsBytes > kStateBytes ? G1::kLdsBytes : kStateBytes;
     __shared__ __align__(16) unsigned char smem[kBytes];
@@ -77,9 +78,9 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     // the chunk: X for this thread's head, B shared by the pair
     const int vrows = (int)((L - tc) < Q ? (L - tc) : Q);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + ((size_t)b * L + tc) * sx + (size_t)h * P,
-                                                (uint32_t)(((vrows - 1) * sx + P) * 2));
+                                                (uint32_t)(((vrows - 1) * sx + P) * sizeof(TX)));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + ((size_t)b * L + tc) * sbc + (size_t)g * N,
-                                                (uint32_t)(((vrows - 1) * sbc + N) * 2));
+                                                (uint32_t)(((vrows - 1) * sbc + N) * sizeof(TX)));
     unsigned short dtraw[4];
     const float dbias = opt.dt_bias ? opt.dt_bias[h] : 0.f;  // read before the block loads
     if (lw == 0) {
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) dtraw[k] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)((lane * 4 + k) * sdt * 2), 0, 0);
     }
-    Raw8<bf16_t> px[NBLK][2], pb[NBLK][BPT][2];
+    Raw8<TX> px[NBLK][2], pb[NBLK][BPT][2];
 #pragma unroll
     for (int m = 0; m < NBLK; ++m) {
         {
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
 
 bool chunk_state_pair_fits(const Dims &d)
 {
-    return d.bf16 && d.Q == 256 && d.P == 64 && d.N <= 128 && d.G > 0 && (d.H / d.G) % 2 == 0;
+    return d.half() && d.Q == 256 && d.P == 64 && d.N <= 128 && d.G > 0 && (d.H / d.G) % 2 == 0;
 }
 
 hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt, const float *A, float *acum,
@@ -239,12 +240,19 @@ hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt
 {
     if (!chunk_state_pair_fits(d)) return hipErrorInvalidValue;
     const dim3 grid(d.nc, d.H / 2 + 4 * d.G, d.B);
-    const bf16_t *xx = static_cast<const bf16_t *>(x), *bb = static_cast<const bf16_t *>(Bm),
-                 *dd = static_cast<const bf16_t *>(dt), *cc = static_cast<const bf16_t *>(Cm);
+    const bf16_t *dd = static_cast<const bf16_t *>(dt);
     f16 *st = static_cast<f16 *>(states);
-#define SSD_CSP_LAUNCH(NN) \
-    launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<NN>, grid, 512, s, xx, bb, dd, A, acum, \
-                  dtc, st, cc, cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc)
+#define SSD_CSP_LAUNCH(NN)                                                                                          \
+    do {                                                                                                            \
+        if (d.in == kInFp8)                                                                                         \
+            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<fp8_t, NN>, grid, 512, s,            \
+                          static_cast<const fp8_t *>(x), static_cast<const fp8_t *>(Bm), dd, A, acum, dtc, st,    \
+                          static_cast<const fp8_t *>(Cm), cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc);        \
+        else                                                                                                        \
+            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<bf16_t, NN>, grid, 512, s,           \
+                          static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(Bm), dd, A, acum, dtc, st,  \
+                          static_cast<const bf16_t *>(Cm), cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc);       \
+    } while (0)
     switch (d.N) {
     case 32: SSD_CSP_LAUNCH(32); break;
     case 64: SSD_CSP_LAUNCH(64); break;

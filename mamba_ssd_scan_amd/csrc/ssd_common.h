@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssd {
 
 typedef _Float16 f16;
@@ -22,6 +24,11 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // storage: upper 16 bits of an fp32
+// storage: OCP fp8 e4m3 ("fn"): a sign bit, 4 exponent bits (bias 7) and 3 mantissa bits;
+// exponent 15 with mantissa 7 is NaN and there are no infinities (largest finite: 448)
+struct fp8_t {
+    uint8_t v;
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -32,8 +39,53 @@ __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// Input element loads: bf16 bit patterns or fp32, returned as fp32 (exact).
+// Four e4m3 values (byte k of w is element k) as four fp16 values, exactly (every e4m3 value
+// is an fp16 value).  A byte's exponent and mantissa bits are moved to the positions fp16
+// keeps them in, which reads the value scaled by 2^-8 (the exponent biases differ by 8; e4m3
+// subnormals land on fp16 subnormals with the same scale); one packed fp16 multiply by 2^8
+// undoes the scale.  The NaN codes become fp16 NaN (a rare branch).  Result: elements 0, 1 in
+// .x, 2, 3 in .y (low half first).
+__device__ __forceinline__ uint32_t f8x2_placed_to_f16x2(uint32_t t)
+{
+    // t: the two bytes in the high byte of each 16-bit half
+    const uint32_t h = (t & 0x80008000u) | ((t >> 1) & 0x3f803f80u);
+    const f16x2 v = __builtin_bit_cast(f16x2, h) * f16x2{(f16)256.0f, (f16)256.0f};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint2 f8x4_to_f16x4(uint32_t w)
+{
+    uint2 r;
+    r.x = f8x2_placed_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x010c000cu));  // bytes 0, 1 -> high bytes of each half
+    r.y = f8x2_placed_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x030c020cu));  // bytes 2, 3
+    const uint32_t nan = ((w & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;  // bit 7 of a byte: its code is NaN
+    if (__builtin_expect(nan != 0u, 0)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (nan & (0x80u << (8 * k))) {
+                uint32_t &word = k < 2 ? r.x : r.y;
+                const int sh = 16 * (k & 1);
+                const uint32_t sign = ((w >> (8 * k)) & 0x80u) << 8;
+                word = (word & ~(0xffffu << sh)) | ((0x7e00u | sign) << sh);
+            }
+        }
+    }
+    return r;
+}
+// Eight e4m3 values (8 bytes) as an fp16 operand (16 bytes).
+__device__ __forceinline__ uint4 f8x8_to_f16x8(uint2 w)
+{
+    const uint2 a = f8x4_to_f16x4(w.x), b = f8x4_to_f16x4(w.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+__device__ __forceinline__ float fp8_to_f32(uint8_t v)
+{
+    const uint2 h = f8x4_to_f16x4((uint32_t)v);
+    return static_cast<float>(__builtin_bit_cast(f16x2, h.x)[0]);
+}
+
+// Input element loads: bf16 bit patterns, e4m3 codes or fp32, returned as fp32 (exact).
 __device__ __forceinline__ float load_in(const bf16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load_in(const fp8_t *p) { return fp8_to_f32(p->v); }
 __device__ __forceinline__ float load_in(const float *p) { return *p; }
 
 // Eight consecutive inputs as fp32 (16-byte aligned for bf16, 32 for fp32).
@@ -46,6 +98,13 @@ __device__ __forceinline__ void load8(const bf16_t *p, float v[8])
         v[2 * k] = __uint_as_float(w[k] << 16);
         v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
+}
+__device__ __forceinline__ void load8(const fp8_t *p, float v[8])
+{
+    const uint4 h = f8x8_to_f16x8(*reinterpret_cast<const uint2 *>(p));
+    const f16x8 f = __builtin_bit_cast(f16x8, h);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(f[k]);
 }
 __device__ __forceinline__ void load8(const float *p, float v[8])
 {
@@ -142,16 +201,26 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 //    with a computed operand run on fp16 (11-bit significand) so that the
 //    rounding of the computed operand stays near 2^-12 relative.
 //  - fp32 inputs: every GEMM runs on the fp32 matrix path (16x16x4).
+//  - e4m3 inputs: as bf16, with the raw inputs widened to fp16 (exact) and GEMMs over
+//    them on fp16; dt (and the gate z) stay bf16.
 template <typename TIn> struct Traits;
 template <> struct Traits<bf16_t> {
     static constexpr bool kF32 = false;
     typedef f16 op_t;      // computed-operand element in LDS
     typedef bf16_t raw_t;  // raw-input element in LDS
+    typedef bf16_t dt_t;   // storage of dt and z
+};
+template <> struct Traits<fp8_t> {
+    static constexpr bool kF32 = false;
+    typedef f16 op_t;
+    typedef f16 raw_t;     // widened when staged
+    typedef bf16_t dt_t;
 };
 template <> struct Traits<float> {
     static constexpr bool kF32 = true;
     typedef float op_t;
     typedef float raw_t;
+    typedef float dt_t;
 };
 
 __device__ __forceinline__ f16 to_op(float v, f16 *) { return static_cast<f16>(v); }
@@ -215,6 +284,25 @@ template <> struct Raw8<float> {
     }
 };
 
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+template <> struct Raw8<fp8_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const fp8_t *p) { v = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e) { v = buf_load8(r, e); }
+    __device__ __forceinline__ void zero() { v = make_uint2(0u, 0u); }
+    // widened to fp16 when staged (Traits<fp8_t>::raw_t)
+    __device__ __forceinline__ void store(f16 *dst) const { *reinterpret_cast<uint4 *>(dst) = f8x8_to_f16x8(v); }
+    __device__ __forceinline__ void to_f32(float f[8]) const
+    {
+        const f16x8 h = __builtin_bit_cast(f16x8, f8x8_to_f16x8(v));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = static_cast<float>(h[k]);
+    }
+};
+
 // Store two fp32 values as an adjacent pair of operand elements (4 or 8 bytes).
 __device__ __forceinline__ void store_pair(f16 *dst, float lo, float hi)
 {
@@ -237,6 +325,18 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 v)
         h[2 * k + 1] = static_cast<f16>(__uint_as_float(w[k] & 0xFFFF0000u));
     }
     return h;
+}
+
+// Eight raw inputs held in a bf16x8 register as loaded (bf16: all 16 bytes; e4m3: the low
+// 8 bytes) as an fp16 matrix-core operand.
+template <typename TIn> __device__ __forceinline__ f16x8 held_to_f16x8(bf16x8 v)
+{
+    if constexpr (std::is_same<TIn, fp8_t>::value) {
+        const uint4 u = __builtin_bit_cast(uint4, v);
+        return __builtin_bit_cast(f16x8, f8x8_to_f16x8(make_uint2(u.x, u.y)));
+    } else {
+        return bf16x8_to_f16x8(v);
+    }
 }
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16

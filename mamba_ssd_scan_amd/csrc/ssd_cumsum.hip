@@ -69,7 +69,7 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, floa
                                const Dims &d, hipStream_t s)
 {
     dim3 grid(d.nc, d.H, d.B);
-    if (d.bf16)
+    if (d.half())  // dt is bf16 beside bf16 and fp8 inputs
         launch_kernel("chunk_cumsum_kernel", chunk_cumsum_kernel<bf16_t>, grid, 64, s,
                       static_cast<const bf16_t *>(dt), A, acum, dtc, d.L, d.H, d.Q, d.nc);
     else

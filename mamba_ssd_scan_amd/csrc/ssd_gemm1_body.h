@@ -3,6 +3,8 @@
 // the prefill's chunk-state launch.  Output layout: see ssd_chunk_gemm1.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_common.h"
 
 namespace ssd {
@@ -14,6 +16,10 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
     typedef Traits<TIn> Tr;
     typedef typename Tr::raw_t raw_t;
     static constexpr bool F32 = Tr::kF32;
+    // e4m3 inputs: B rows are widened to fp16 when staged and C rows when loaded (exact), and
+    // the products run on fp16 matrix cores; bf16 inputs run on bf16 ones
+    static constexpr bool F8 = std::is_same<TIn, fp8_t>::value;
+    typedef typename std::conditional<F8, f16x8, bf16x8>::type mop_t;
     static constexpr int LDB = N + (F32 ? 4 : 8);  // row pitch: 16 rows read together hit distinct banks
     static constexpr int KS = F32 ? N / 4 : N / 32;
     static constexpr int NT = 64 * NWAVES;
@@ -62,7 +68,7 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + row0, bytes);
 
         // C rows of a row tile (the GEMM1^T B operand), held in registers
-        bf16x8 cbf[F32 ? 1 : KS];
+        mop_t cbf[F32 ? 1 : KS];
         float cf[F32 ? KS : 1];
         auto load_c = [&](int t) {
             const uint32_t row = (uint32_t)((16 * t + li) * sbc);
@@ -70,6 +76,9 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     cf[ks] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(4u * (row + ks * 4 + lg)), 0, 0));
+            } else if constexpr (F8) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) cbf[ks] = __builtin_bit_cast(f16x8, f8x8_to_f16x8(buf_load8(rc, row + ks * 32 + 8 * lg)));
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) cbf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rc, 2u * (row + ks * 32 + 8 * lg)));
@@ -135,24 +144,30 @@ template <typename TIn, int N, int NWAVES, int ROWS> struct Gemm1Chunk {
                     }
                 } else {
                     const raw_t *b0 = &bs[(jb + li) * LDB + 8 * lg];
+                    auto mma = [](mop_t a, mop_t b, f32x4 c) {
+                        if constexpr (F8)
+                            return mfma16x16x32_f16(a, b, c);
+                        else
+                            return mfma16x16x32_bf16(a, b, c);
+                    };
                     if (has1) {
-                        bf16x8 a0[KS], a1[KS];
+                        mop_t a0[KS], a1[KS];
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) {
-                            a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
-                            a1[ks] = *reinterpret_cast<const bf16x8 *>(b0 + 16 * LDB + ks * 32);
+                            a0[ks] = *reinterpret_cast<const mop_t *>(b0 + ks * 32);
+                            a1[ks] = *reinterpret_cast<const mop_t *>(b0 + 16 * LDB + ks * 32);
                         }
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) {
-                            d0 = mfma16x16x32_bf16(a0[ks], cbf[ks], d0);
-                            d1 = mfma16x16x32_bf16(a1[ks], cbf[ks], d1);
+                            d0 = mma(a0[ks], cbf[ks], d0);
+                            d1 = mma(a1[ks], cbf[ks], d1);
                         }
                     } else {
-                        bf16x8 a0[KS];
+                        mop_t a0[KS];
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) a0[ks] = *reinterpret_cast<const bf16x8 *>(b0 + ks * 32);
+                        for (int ks = 0; ks < KS; ++ks) a0[ks] = *reinterpret_cast<const mop_t *>(b0 + ks * 32);
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) d0 = mfma16x16x32_bf16(a0[ks], cbf[ks], d0);
+                        for (int ks = 0; ks < KS; ++ks) d0 = mma(a0[ks], cbf[ks], d0);
                     }
                 }
                 const size_t slice = chunk0 + Tt + s;

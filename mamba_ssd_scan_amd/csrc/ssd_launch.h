@@ -45,9 +45,21 @@ inline void launch_kernel(const char *name, void (*k)(P...), dim3 grid, dim3 blo
     hipExtLaunchKernelGGL(k, grid, block, 0, s, e0, e1, 0u, a...);
 }
 
+// Storage type of x, B and C (the ABI's ssd_dtype_t values): fp32, bf16 or fp8 e4m3 (whose
+// dt and z are bf16).  bf16 and fp8 inputs take the same paths, with fp16 chunk and
+// entering states.
+enum InType { kInF32 = 0, kInBf16 = 1, kInFp8 = 2 };
+
+// The InType of a kernel instantiation's input element.
+template <typename T> struct InOf;
+template <> struct InOf<float> { static constexpr int v = kInF32; };
+template <> struct InOf<bf16_t> { static constexpr int v = kInBf16; };
+template <> struct InOf<fp8_t> { static constexpr int v = kInFp8; };
+
 struct Dims {
     int B, L, H, P, N, G, Q, nc;  // batch, seqlen, heads, headdim, dstate, groups, chunk, chunks
-    bool bf16;                    // input storage: bf16 (true) or fp32
+    int in;                       // InType
+    bool half() const { return in != kInF32; }  // fp16 states, fp16 matrix-core operands
     // elements between consecutive tokens of x, of B and C, of dt and of z (dense: H*P, G*N,
     // H, H*P); the prefill's kernels read their inputs with these, y is always dense
     int sx, sbc, sdt, sz;
@@ -55,7 +67,7 @@ struct Dims {
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, float *acum, float *dtc,
                                const Dims &d, hipStream_t s);
-// states: [B, H, nc, P, N], fp16 for bf16 inputs (d.bf16), fp32 otherwise; likewise below.
+// states: [B, H, nc, P, N], fp16 for bf16 and fp8 inputs (d.half()), fp32 otherwise; likewise below.
 hipError_t launch_chunk_state(const void *x, const void *Bm, const float *acum, const float *dtc,
                               void *states, const Dims &d, hipStream_t s);
 // Step-0 and Step-1 GEMM1 fused into the Step-2 launch: writes acum/dtc (same values as
@@ -112,7 +124,7 @@ hipError_t launch_prefill_fused(const void *x, const void *Bm, const void *Cm, c
                                 const float *D, const float *init, float *fin, void *y, void *ws, const SsdOpts &o,
                                 const Dims &d, hipStream_t s);
 // Zero-padding copy: dst[(o * nin_dst + i) * dlen + k] = (i < nin_src && k < slen) ?
-// src[o * so + i * si + k * sk] : 0 for o < nout, i < nin_dst, k < dlen; elements of 2 or 4 bytes.
+// src[o * so + i * si + k * sk] : 0 for o < nout, i < nin_dst, k < dlen; elements of 1, 2 or 4 bytes.
 hipError_t launch_pad_copy(const void *src, void *dst, int elem_bytes, long long nout, int nin_src, int nin_dst,
                            int slen, int dlen, long long so, long long si, long long sk, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n (n a multiple of 4, 16-byte aligned pointers).

@@ -38,7 +38,10 @@ hipError_t launch_pad_copy(const void *src, void *dst, int elem_bytes, long long
     if (total <= 0) return hipSuccess;
     const long long want = (total + 255) / 256;
     const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-    if (elem_bytes == 2)
+    if (elem_bytes == 1)  // fp8 e4m3 codes (the zero code is +0)
+        launch_kernel("pad_copy_kernel", pad_copy_kernel<uint8_t>, grid, 256, s, static_cast<const uint8_t *>(src),
+                      static_cast<uint8_t *>(dst), nout, nin_src, nin_dst, slen, dlen, so, si, sk);
+    else if (elem_bytes == 2)
         launch_kernel("pad_copy_kernel", pad_copy_kernel<uint16_t>, grid, 256, s,
                       static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), nout, nin_src, nin_dst,
                       slen, dlen, so, si, sk);

@@ -106,7 +106,7 @@ static FusedWs fused_ws(const Dims &d)
 size_t fused_prefill_ws_bytes(const Dims &d) { return fused_ws(d).total; }
 bool fused_prefill_shape(const Dims &d)
 {
-    return d.bf16 && d.Q == 256 && d.P == 64 && (d.N == 64 || d.N == 128) && d.nc >= 1 &&
+    return d.in == kInBf16 && d.Q == 256 && d.P == 64 && (d.N == 64 || d.N == 128) && d.nc >= 1 &&
            (long long)d.B * d.H * d.nc < 0x7fffffffLL;  // one workgroup (and ticket) per item
 }
 

@@ -98,7 +98,7 @@ hipError_t launch_state_passing(void *states, const float *acum, const float *in
 {
     const int PN4 = d.P * d.N / 4;
     dim3 grid((PN4 + kPassThreads - 1) / kPassThreads, d.H, d.B);
-    if (d.bf16)
+    if (d.half())
         launch_kernel("state_passing_kernel", state_passing_kernel<f16>, grid, kPassThreads, s,
                       static_cast<f16 *>(states), acum, init, fin, d.H, d.nc, d.Q, PN4);
     else

@@ -26,7 +26,8 @@ namespace ssd {
 // One workgroup per (b, h), all of its rows: the batched decode at the built state widths.
 template <typename TIn, int N>
 __global__ __launch_bounds__(256) void step_heads_kernel(float *__restrict__ state, const TIn *__restrict__ x,
-                                                   const TIn *__restrict__ dt, const float *__restrict__ A,
+                                                   const typename Traits<TIn>::dt_t *__restrict__ dt,
+                                                   const float *__restrict__ A,
                                                    const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
                                                    const float *__restrict__ D, void *__restrict__ y,
                                                    SsdOpts opt, int H, int G, int P, int sx, int sbc, int sdt,
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void step_heads_kernel(float *__restrict__ sta
             for (int off = NQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
             if (q == 0) {
                 float out = part + Dh * xs[k];
-                if (opt.z) out *= silu(load_in(static_cast<const TIn *>(opt.z) + (size_t)b * sz + (size_t)h * P + p));
+                if (opt.z) out *= silu(load_in(static_cast<const typename Traits<TIn>::dt_t *>(opt.z) + (size_t)b * sz + (size_t)h * P + p));
                 if (opt.y_bf16)
                     static_cast<uint16_t *>(y)[(size_t)bh * P + p] = f32_to_bf16_rne(out);
                 else
@@ -94,7 +95,8 @@ __global__ __launch_bounds__(256) void step_heads_kernel(float *__restrict__ sta
 // workgroup.
 template <typename TIn, int NQ, bool FULL>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, const TIn *__restrict__ x,
-                                                   const TIn *__restrict__ dt, const float *__restrict__ A,
+                                                   const typename Traits<TIn>::dt_t *__restrict__ dt,
+                                                   const float *__restrict__ A,
                                                    const TIn *__restrict__ Bm, const TIn *__restrict__ Cm,
                                                    const float *__restrict__ D, void *__restrict__ y,
                                                    SsdOpts opt, int H, int G, int P, int N, int sx, int sbc,
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ state, co
                 for (int off = NQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
                 if (q == 0) {
                     float out = part + Dh * xs[k];
-                    if (opt.z) out *= silu(load_in(static_cast<const TIn *>(opt.z) + (size_t)b * sz + (size_t)h * P + p));
+                    if (opt.z) out *= silu(load_in(static_cast<const typename Traits<TIn>::dt_t *>(opt.z) + (size_t)b * sz + (size_t)h * P + p));
                     if (opt.y_bf16)
                         static_cast<uint16_t *>(y)[(size_t)bh * P + p] = f32_to_bf16_rne(out);
                     else
@@ -180,7 +182,8 @@ static hipError_t launch_step_t(float *state, const void *x, const void *dt, con
     int ncu = 0;
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
-    const TIn *xx = static_cast<const TIn *>(x), *dd = static_cast<const TIn *>(dt);
+    const TIn *xx = static_cast<const TIn *>(x);
+    const typename Traits<TIn>::dt_t *dd = static_cast<const typename Traits<TIn>::dt_t *>(dt);
     const TIn *bb = static_cast<const TIn *>(Bm), *cc = static_cast<const TIn *>(Cm);
     const int n4 = d.N / 4;
     const int nq = n4 <= 4 ? 4 : n4 <= 8 ? 8 : n4 <= 16 ? 16 : n4 <= 32 ? 32 : 64;
@@ -227,8 +230,9 @@ static hipError_t launch_step_t(float *state, const void *x, const void *dt, con
 hipError_t launch_step(float *state, const void *x, const void *dt, const float *A, const void *Bm,
                        const void *Cm, const float *D, void *y, const SsdOpts &o, const Dims &d, hipStream_t s)
 {
-    return d.bf16 ? launch_step_t<bf16_t>(state, x, dt, A, Bm, Cm, D, y, o, d, s)
-                  : launch_step_t<float>(state, x, dt, A, Bm, Cm, D, y, o, d, s);
+    if (d.in == kInFp8) return launch_step_t<fp8_t>(state, x, dt, A, Bm, Cm, D, y, o, d, s);
+    return d.in == kInBf16 ? launch_step_t<bf16_t>(state, x, dt, A, Bm, Cm, D, y, o, d, s)
+                           : launch_step_t<float>(state, x, dt, A, Bm, Cm, D, y, o, d, s);
 }
 
 }  // namespace ssd

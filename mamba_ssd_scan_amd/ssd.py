@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
-SSD_F32, SSD_BF16 = 0, 1
+SSD_F32, SSD_BF16, SSD_FP8_E4M3 = 0, 1, 2
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_SYNC = 0, -1, -2, -3, -4, -5
 
 # Every symbol include/ssd.h declares.
@@ -128,7 +128,31 @@ def _dtype_code(t) -> int:
         return SSD_BF16
     if t.dtype == torch.float32:
         return SSD_F32
-    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+    if t.dtype == torch.float8_e4m3fn:
+        return SSD_FP8_E4M3
+    raise TypeError(f"inputs must be bfloat16, float32 or float8_e4m3fn, got {t.dtype}")
+
+
+def _check_types(x, dt, B, C, z=None) -> int:
+    """The input dtype code: B and C share x's dtype; dt and z too, except beside float8_e4m3fn
+    x, B and C, where they are bfloat16."""
+    torch = _torch()
+    code = _dtype_code(x)
+    for t in (B, C):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("x, B and C must share one dtype")
+    want = torch.bfloat16 if code == SSD_FP8_E4M3 else x.dtype
+    for t in (dt, z):
+        if t is not None and t.dtype != want:
+            raise TypeError("dt and z must share x's dtype (bfloat16 beside float8_e4m3fn x, B and C)")
+    return code
+
+
+def _y_code(y_dtype) -> int:
+    torch = _torch()
+    if y_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"y must be float32 or bfloat16, got {y_dtype}")
+    return _dtype_code(torch.empty(0, dtype=y_dtype))
 
 
 def _dev(*ts):
@@ -253,12 +277,9 @@ def _prefill(x, dt, A, B, C, D, initial_state, dt_bias, dt_softplus, z, y_dtype,
     torch = _torch()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
-    code = _dtype_code(x)
-    for t in (dt, B, C, z):
-        if t is not None and t.dtype != x.dtype:
-            raise TypeError("x, dt, B, C and z must share one dtype")
+    code = _check_types(x, dt, B, C, z)
     y_dtype = torch.float32 if y_dtype is None else y_dtype
-    ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+    ycode = _y_code(y_dtype)
     strides, dense = _seq_strides(x, dt, B, C, z)  # views into wider token rows are read in place
     _dev(A, D, initial_state, y, workspace, dt_bias)
     _f32(A, D, initial_state, dt_bias)
@@ -426,10 +447,10 @@ def prefill_noalloc(x, dt, A, B, C, D=None, initial_state=None, *, chunk: int = 
     x, dt, B and C must be dense.  Returns (y, final_state)."""
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
-    code = _dtype_code(x)
-    for t in (dt, B, C):
-        if t.dtype != x.dtype or not t.is_contiguous():
-            raise TypeError("x, dt, B and C must share one dtype and be dense")
+    code = _check_types(x, dt, B, C)
+    for t in (x, dt, B, C):
+        if not t.is_contiguous():
+            raise TypeError("x, dt, B and C must be dense")
     _dev(A, D, initial_state, y, final_state)
     _f32(A, D, initial_state, y, final_state)
     _check(lib().ssd_prefill_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
@@ -451,9 +472,9 @@ def step_ex(state, x, dt, A, B, C, D=None, *, dt_bias=None, dt_softplus=False, z
     torch = _torch()
     batch, nheads, headdim, dstate = state.shape
     ngroups = B.shape[1]
-    code = _dtype_code(x)
+    code = _check_types(x, dt, B, C, z)
     y_dtype = torch.float32 if y_dtype is None else y_dtype
-    ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+    ycode = _y_code(y_dtype)
     strides, dense = _step_strides(x, dt, B, C, z)  # views into wider rows are read in place
     _dev(state, A, D, y, dt_bias)
     _f32(state, A, D, dt_bias)
@@ -478,7 +499,7 @@ def step(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
     torch = _torch()
     batch, nheads, headdim, dstate = state.shape
     ngroups = B.shape[1]
-    code = _dtype_code(x)
+    code = _check_types(x, dt, B, C)
     strides, dense = _step_strides(x, dt, B, C, None)  # views into wider rows are read in place
     _dev(state, A, D, y)
     _f32(state, A, D, y)
@@ -516,12 +537,9 @@ class DecodeGraph:
         if tuple(dt.shape) != (nsteps, batch, nheads) or tuple(B.shape) != (nsteps, batch, ngroups, dstate) \
                 or tuple(C.shape) != tuple(B.shape) or (z is not None and tuple(z.shape) != tuple(x.shape)):
             raise ValueError("step-major inputs must be x [T,B,H,P], dt [T,B,H], B/C [T,B,G,N], z like x")
-        code = _dtype_code(x)
-        for t in (dt, B, C, z):
-            if t is not None and _dtype_code(t) != code:
-                raise TypeError("x, dt, B, C and z must share one dtype")
+        code = _check_types(x, dt, B, C, z)
         y_dtype = torch.float32 if y_dtype is None else y_dtype
-        ycode = _dtype_code(torch.empty(0, dtype=y_dtype))
+        ycode = _y_code(y_dtype)
         _dev(state, x, dt, A, B, C, D, y, dt_bias, z)
         _f32(state, A, D, dt_bias)
         if y is None:
@@ -586,7 +604,7 @@ def chunk_cumsum(dt, A, *, chunk: int, acum=None, dtc=None, stream=None):
 def _state_dtype(x):
     """Element type of the chunk / entering states for inputs like ``x``."""
     torch = _torch()
-    return torch.float16 if x.dtype == torch.bfloat16 else torch.float32
+    return torch.float32 if x.dtype == torch.float32 else torch.float16  # fp16 beside bf16 and fp8 inputs
 
 
 def chunk_state(x, B, acum, dtc, *, chunk: int, states=None, stream=None):
@@ -615,7 +633,7 @@ def state_passing(states, acum, initial_state=None, *, chunk: int, final_state="
     elif states.dtype == torch.float32:
         code = SSD_F32
     else:
-        raise TypeError("states must be float16 (bfloat16 inputs) or float32 (float32 inputs)")
+        raise TypeError("states must be float16 (bfloat16 or float8_e4m3fn inputs) or float32 (float32 inputs)")
     if isinstance(final_state, str):
         final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=states.device)
     _check(lib().ssd_state_passing(_ptr(states), _ptr(acum), _ptr(initial_state), _ptr(final_state), code, batch,
@@ -651,7 +669,7 @@ def chunk_scan(x, C, cb, acum, dtc, h_enter, D=None, *, chunk: int, y=None, stre
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = C.shape[2], C.shape[3]
     _dev(x, C, cb, acum, dtc, h_enter, D, y)
-    want = torch.float16 if x.dtype == torch.bfloat16 else torch.float32
+    want = torch.float32 if x.dtype == torch.float32 else torch.float16
     if h_enter.dtype != want:
         raise TypeError(f"h_enter must be {want} for {x.dtype} inputs")
     if y is None:
@@ -685,7 +703,7 @@ def chunk_scan_passing(x, C, cb, acum, dtc, states, sync, D=None, initial_state=
     _dev(x, C, cb, acum, dtc, states, sync, D, initial_state, y)
     _f32(D, initial_state, y)
     if states.dtype != torch.float16:
-        raise TypeError("states must be float16 (bfloat16 inputs)")
+        raise TypeError("states must be float16 (bfloat16 or float8_e4m3fn inputs)")
     if sync.numel() * sync.element_size() < batch * nheads * SYNC_WORDS_PER_HEAD * 4:
         raise ValueError("sync is smaller than batch * nheads * 256 bytes")
     if y is None:

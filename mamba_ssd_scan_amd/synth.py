@@ -39,7 +39,7 @@ class PrefillShape:
     dstate: int
     ngroups: int
     chunk: int
-    dtype: str  # "bf16" or "f32": storage type of x, dt, B, C
+    dtype: str  # "bf16", "f32" or "fp8" (x, B, C in e4m3, dt in bf16): storage of the inputs
     init_state: str = "zero"  # "zero" or "randn" (std 0.1)
 
 
@@ -101,6 +101,46 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return (a.view(np.uint32) >> 16).astype(np.uint16)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_round(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest OCP fp8 e4m3 value (ties to even); returns fp32.
+
+    e4m3: a sign, 4 exponent bits (bias 7), 3 mantissa bits; normals from 2^-6, subnormals
+    in steps of 2^-9, largest finite 448.  Values that would round past 448 are refused."""
+    a = np.asarray(a, dtype=np.float64)
+    if np.any(np.abs(a) >= 464.0):  # 464 and up round past the largest finite value
+        raise ValueError("value out of the e4m3 range")
+    _, ex = np.frexp(a)                          # |a| in [2^(ex-1), 2^ex)
+    k = np.maximum(ex - 1, -6)                   # the binade's exponent, subnormals at -6
+    q = np.ldexp(1.0, k - 3)                     # the spacing of e4m3 values there
+    return (np.round(a / q) * q).astype(np.float32)  # np.round: half to even
+
+
+def e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """The e4m3 codes (uint8) of fp32 values that are already e4m3-representable."""
+    a = np.asarray(a, dtype=np.float64)
+    sign = (np.signbit(a)).astype(np.uint8) << 7
+    m = np.abs(a)
+    _, ex = np.frexp(m)
+    k = ex - 1
+    normal = m >= 2.0 ** -6
+    e = np.where(normal, k + 7, 0)
+    mant = np.where(normal, m / np.ldexp(1.0, k) - 1.0, m / 2.0 ** -9) * np.where(normal, 8.0, 1.0)
+    return (sign | (e.astype(np.uint8) << 3) | np.rint(mant).astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_value(code) -> float:
+    """The value of one e4m3 code (NaN for 0x7f and 0xff)."""
+    code = int(code)
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    return s * (m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+
+
 def softplus(z: np.ndarray) -> np.ndarray:
     return np.logaddexp(np.float32(0.0), z).astype(np.float32)
 
@@ -108,9 +148,16 @@ def softplus(z: np.ndarray) -> np.ndarray:
 def _store(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_round(a)
+    if dtype == "fp8":
+        return e4m3_round(a)
     if dtype == "f32":
         return np.ascontiguousarray(a, dtype=np.float32)
     raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+def dt_dtype(dtype: str) -> str:
+    """Storage of dt and z beside inputs of ``dtype`` (bf16 beside fp8 x, B and C)."""
+    return "bf16" if dtype == "fp8" else dtype
 
 
 def prefill_inputs(shape: PrefillShape, seed: int, *, heads: Optional[np.ndarray] = None) -> dict:
@@ -137,7 +184,7 @@ def prefill_inputs(shape: PrefillShape, seed: int, *, heads: Optional[np.ndarray
         raise ValueError(s.init_state)
     out = dict(
         x=_store(x, s.dtype),
-        dt=_store(dt, s.dtype),
+        dt=_store(dt, dt_dtype(s.dtype)),
         A=A,
         B=_store(Bm, s.dtype),
         C=_store(Cm, s.dtype),
@@ -196,7 +243,7 @@ def random_prefill(rng: np.random.Generator, batch, seqlen, nheads, headdim, dst
         raise ValueError(dt_mode)
     D = np.zeros((nheads,), f) if D_zero else rng.standard_normal((nheads,), dtype=f)
     h0 = (0.1 * rng.standard_normal((batch, nheads, headdim, dstate), dtype=f)).astype(f) if init_state else None
-    return dict(x=_store(x, dtype), dt=_store(dt, dtype), A=A, B=_store(Bm, dtype), C=_store(Cm, dtype),
+    return dict(x=_store(x, dtype), dt=_store(dt, dt_dtype(dtype)), A=A, B=_store(Bm, dtype), C=_store(Cm, dtype),
                 D=D, h0=h0, dtype=dtype)
 
 
@@ -213,7 +260,7 @@ def option_inputs(rng: np.random.Generator, inp: dict) -> dict:
     dt_raw = rng.normal(-3.0, 1.0, size=inp["dt"].shape).astype(f)
     bias = (0.5 * rng.standard_normal((H,))).astype(f)
     z = rng.standard_normal(inp["x"].shape, dtype=f)
-    return dict(dt_raw=_store(dt_raw, d), dt_bias=bias, z=_store(z, d))
+    return dict(dt_raw=_store(dt_raw, dt_dtype(d)), dt_bias=bias, z=_store(z, dt_dtype(d)))
 
 
 def decode_inputs(shape: DecodeShape, seed: int, steps: Optional[int] = None) -> dict:
@@ -233,17 +280,19 @@ def decode_inputs(shape: DecodeShape, seed: int, steps: Optional[int] = None) ->
     A = -np.exp(rng.uniform(math.log(1.0), math.log(16.0), size=(s.nheads,))).astype(f)
     D = rng.standard_normal((s.nheads,), dtype=f)
     state = (0.1 * rng.standard_normal((s.batch, s.nheads, s.headdim, s.dstate), dtype=f)).astype(f)
-    return dict(x=_store(x, s.dtype), dt=_store(dt, s.dtype), A=A, B=_store(Bm, s.dtype),
+    return dict(x=_store(x, s.dtype), dt=_store(dt, dt_dtype(s.dtype)), A=A, B=_store(Bm, s.dtype),
                 C=_store(Cm, s.dtype), D=D, state=state, dtype=s.dtype)
 
 
 def to_torch(a: np.ndarray, dtype: str, device="cuda"):
     """Copy an fp32 array holding exact values to a torch tensor of ``dtype``.
 
-    ``dtype`` "bf16" moves the bf16 bit patterns (no re-rounding), "f32" the
-    fp32 values.
+    ``dtype`` "bf16" moves the bf16 bit patterns (no re-rounding), "fp8" the e4m3
+    codes (torch.float8_e4m3fn), "f32" the fp32 values.
     """
     import torch
+    if dtype == "fp8":
+        return torch.from_numpy(e4m3_codes(a)).to(device).view(torch.float8_e4m3fn)
     if dtype == "bf16":
         bits = bf16_bits(a).view(np.int16)
         return torch.from_numpy(bits).to(device).view(torch.bfloat16)

@@ -17,7 +17,8 @@ def torch():
 def upload(inp: dict) -> dict:
     T = torch()
     d = inp["dtype"]
-    out = {k: synth.to_torch(inp[k], d) for k in ("x", "dt", "B", "C")}
+    out = {k: synth.to_torch(inp[k], d) for k in ("x", "B", "C")}
+    out["dt"] = synth.to_torch(inp["dt"], synth.dt_dtype(d))
     out["A"] = T.from_numpy(np.ascontiguousarray(inp["A"], np.float32)).cuda()
     out["D"] = None if inp.get("D") is None else T.from_numpy(np.ascontiguousarray(inp["D"], np.float32)).cuda()
     out["h0"] = None if inp.get("h0") is None else T.from_numpy(np.ascontiguousarray(inp["h0"], np.float32)).cuda()

@@ -12,7 +12,7 @@ from mamba_ssd_scan_amd import ssd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
 
-F, BF = ssd.SSD_F32, ssd.SSD_BF16
+F, BF, F8 = ssd.SSD_F32, ssd.SSD_BF16, ssd.SSD_FP8_E4M3
 INV, UNS, WS = ssd.SSD_ERR_INVALID_ARG, ssd.SSD_ERR_UNSUPPORTED, ssd.SSD_ERR_WORKSPACE
 P0 = 0x100000  # fake, aligned "device" addresses: only used on calls that must be rejected
 
@@ -201,6 +201,11 @@ def test_option_entry_points_reject_before_launch():
     assert pf(z=P0 + 1) == INV                 # misaligned z (bf16 needs 2-byte alignment)
     assert pf(chunk=48) == UNS
     assert pf(ws=None) == WS
+    assert pf(dtype=F8, ws=None) == WS         # fp8 x, B, C with bf16 dt: accepted up to the workspace
+    assert pf(dtype=F8, ydtype=F8) == INV      # y is never fp8
+    assert pf(dtype=F8, x=P0 + 8, ws=None) == INV   # fp8 rows are read 16 bytes at a time
+    assert pf(dtype=F8, dt=P0 + 1, ws=None) == INV  # dt beside fp8 inputs is bf16
+    assert pf(dtype=F8, z=P0 + 1) == INV       # so is z
     assert pf(x=None) == INV
     assert pf(seqlen=0, y=None) == 0               # empty sequence, no final state: nothing to launch
     def st(**kw):
@@ -215,6 +220,8 @@ def test_option_entry_points_reject_before_launch():
     assert st(y=P0 + 2) == INV                 # fp32 y must be 4-byte aligned
     assert st(z=P0 + 1) == INV
     assert st(headdim=24) == UNS
+    assert st(dtype=F8, ydtype=F8) == INV
+    assert st(dtype=F8, dt=P0 + 1) == INV      # bf16 dt beside fp8 x, B, C
 
 
 def test_strided_prefill_checks_token_strides_before_launch():
@@ -244,6 +251,9 @@ def test_strided_prefill_checks_token_strides_before_launch():
     assert pf(sb=68) == INV
     assert pf(dtype=F, sx=260) == WS                    # fp32: 1040 bytes
     assert pf(dtype=F, sx=258) == INV
+    assert pf(dtype=F8, sx=272, sb=80) == WS            # fp8: rows of 272 and 80 bytes
+    assert pf(dtype=F8, sx=264) == INV                  # 264 bytes: not a multiple of 16
+    assert pf(dtype=F8, sb=72) == INV
     assert pf(sx=1 << 24) == UNS                        # 64 tokens x 2 bytes x 2^24 = 2^31 bytes per chunk
     assert pf(sd=1 << 24) == UNS
     assert L.ssd_prefill_ex(P0, P0, P0, P0, P0, None, None, 1, None, None, None, P0, BF, F, 1, 300, 4, 64, 64, 1, 64,

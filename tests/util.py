@@ -2,7 +2,9 @@
 import numpy as np
 
 # Tolerances on the normwise relative error below, per input storage type.
-TOL = {"bf16": 2e-3, "f32": 1e-4}
+# fp8 (e4m3 x, B and C; bf16 dt): the inputs are exact values, and every matrix-core operand
+# computed from them is fp16 as for bf16 inputs, so the bf16 bar applies.
+TOL = {"bf16": 2e-3, "f32": 1e-4, "fp8": 2e-3}
 
 
 def rel_err(t, o) -> float:
