@@ -77,6 +77,48 @@ def test_chunked_ragged_padding_layout():
     assert np.all(r["dt"][:, :, 2, 5:] == 0.0)
 
 
+def test_chunked_intermediates_against_recurrence_and_quadratic_form():
+    """The chunked oracle's intermediates, each pinned to another formulation (the end-to-end
+    pins only see y and the final state):
+
+    - the entering state of chunk c is the sequential recurrence's state after the first cQ
+      tokens (the C oracle run on that prefix);
+    - the chunk state S_c is the recurrence's state after chunk c alone, from a zero state;
+    - the GEMM1 product of a chunk is the quadratic form's score matrix on that chunk's block:
+      with A = 0 and dt = 1 the decay mask is 1 under the diagonal, and with one-hot x (P = L
+      channels) the form's output row t is row t of that matrix.
+    """
+    rng = np.random.Generator(np.random.PCG64(31))
+    B_, L, H, P, N, G, Q = 2, 37, 4, 5, 6, 2, 8
+    inp = synth.random_prefill(rng, B_, L, H, P, N, G, "f32", init_state="randn")
+    r = chunked.chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"], Q=Q)
+    nc = -(-L // Q)
+    for c in range(nc):
+        t0, t1 = c * Q, min(L, (c + 1) * Q)
+        if c > 0:
+            _, h_pre = ref.prefill(inp["x"][:, :t0], inp["dt"][:, :t0], inp["A"], inp["B"][:, :t0],
+                                   inp["C"][:, :t0], None, inp["h0"])
+        else:
+            h_pre = inp["h0"]
+        assert rel_err(r["h_enter"][:, :, c], h_pre) < 1e-12, c
+        _, s_c = ref.prefill(inp["x"][:, t0:t1], inp["dt"][:, t0:t1], inp["A"], inp["B"][:, t0:t1],
+                             inp["C"][:, t0:t1], None, None)
+        assert rel_err(r["states"][:, :, c], s_c) < 1e-12, c
+    # GEMM1 against the quadratic form's scores
+    Lg = 2 * Q + 3
+    Bm = rng.standard_normal((1, Lg, 1, N))
+    Cm = rng.standard_normal((1, Lg, 1, N))
+    onehot = np.eye(Lg)[None, :, None, :]               # x[0, s, 0, :] = e_s
+    ones, zero = np.ones((1, Lg, 1)), np.zeros(1)
+    yq, _ = quadratic.quadratic_form(onehot, ones, zero, Bm, Cm)
+    g1 = chunked.chunked(onehot, ones, zero, Bm, Cm, Q=Q)["gemm1"]
+    for c in range(-(-Lg // Q)):
+        t0, t1 = c * Q, min(Lg, (c + 1) * Q)
+        block = yq[0, t0:t1, 0, t0:t1]                    # scores of the chunk's own tokens
+        assert np.allclose(g1[0, 0, c, :t1 - t0, :t1 - t0], block, rtol=0, atol=1e-12), c
+        assert np.all(g1[0, 0, c, :, :][np.triu_indices(Q, 1)] == 0.0)
+
+
 # ---------------------------------------------------------------------------
 # Mutation test: plant a mistake in a copy of the oracle source, build it, and
 # check that at least one pin fails.  Each mutant is a plausible slip.
