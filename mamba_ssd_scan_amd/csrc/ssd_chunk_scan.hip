@@ -621,7 +621,10 @@ template <int P, int N, int NW> struct PipeLds {
 // TX: storage of x and C (bf16, or fp8 e4m3: half the raw X bytes to stream; both widen to
 // fp16 exactly).  GATE: the z gate is applied; Y16: y is stored as bf16.  Each combination is
 // its own instantiation, so the plain and the bf16-y kernels carry no registers for the gate.
-template <typename TX, int P, int N, int NW, bool GATE, bool Y16>
+// SCP: cache policy of the X and entering-state streams (kStream when X is too large to stay
+// in the Infinity Cache between launches: neither is read again, and streamed they leave the
+// cache to what the next launches read back).
+template <typename TX, int P, int N, int NW, bool GATE, bool Y16, int SCP>
 __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
     const TX *__restrict__ x, const TX *__restrict__ Cm, const void *__restrict__ cbg,
     const float *__restrict__ acum, const float *__restrict__ dtc, const void *__restrict__ henv,
@@ -709,14 +712,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_pipe_kernel(
         for (int k = 0; k < XI / NL; ++k) {
             const int wi = k * NL + wave;
             const int byte = 1024 * wi + 16 * ln, row = byte / RB, col = byte % RB;
-            buf_load_lds16(rx, stg + 1024 * wi, (uint32_t)(row * sx * (int)sizeof(TX) + col));
+            buf_load_lds16<SCP>(rx, stg + 1024 * wi, (uint32_t)(row * sx * (int)sizeof(TX) + col));
         }
         const __amdgpu_buffer_rsrc_t rh =
             make_rsrc(static_cast<const f16 *>(henv) + it.bhc * P * N, live ? (uint32_t)(P * N * 2) : 0u);
 #pragma unroll
         for (int k = 0; k < P / NL; ++k) {
             const int p = k * NL + wave;
-            buf_load_lds4(rh, hsn + p * LDH, (uint32_t)(p * N * 2 + 4 * ln));
+            buf_load_lds4<SCP>(rh, hsn + p * LDH, (uint32_t)(p * N * 2 + 4 * ln));
         }
         if (wave < TI) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(acum + it.bhc * Q, live ? (uint32_t)(Q * 4) : 0u);
@@ -976,9 +979,16 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
         if (d.N == 128 && d.Q == 256) {
             static_assert(PipeLds<64, 128, 16>::fits, "pipelined chunk scan LDS");
             const int nwg = nitems < ncu ? nitems : ncu;
-#define SSD_PIPE_LAUNCH(GT, YB)                                                                          \
-    launch_kernel("chunk_scan_pipe_kernel", chunk_scan_pipe_kernel<TIn, 64, 128, 16, GT, YB>, nwg, 1024, s, xx, cc, \
-                  cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
+#define SSD_PIPE_LAUNCH2(GT, YB, CP)                                                                         \
+    launch_kernel("chunk_scan_pipe_kernel", chunk_scan_pipe_kernel<TIn, 64, 128, 16, GT, YB, CP>, nwg, 1024, s, xx, \
+                  cc, cbg, acum, dtc, hen, D, y, o, d.L, d.H, d.G, d.sx, d.sbc, d.sz, d.Q, d.nc, nitems)
+#define SSD_PIPE_LAUNCH(GT, YB)                  \
+    do {                                         \
+        if (o.stream_x)                          \
+            SSD_PIPE_LAUNCH2(GT, YB, kStream);   \
+        else                                     \
+            SSD_PIPE_LAUNCH2(GT, YB, 0);         \
+    } while (0)
             if (o.z && o.y_bf16)
                 SSD_PIPE_LAUNCH(true, true);
             else if (o.z)
@@ -988,6 +998,7 @@ static hipError_t launch_scan_n(const void *x, const void *Cm, const void *cbg, 
             else
                 SSD_PIPE_LAUNCH(false, false);
 #undef SSD_PIPE_LAUNCH
+#undef SSD_PIPE_LAUNCH2
             return hipGetLastError();
         }
     }

@@ -23,8 +23,9 @@
 
 namespace ssd {
 
-// TX: storage of x, B and C (bf16 or fp8 e4m3); dt is bf16 either way.
-template <typename TX, int N>
+// TX: storage of x, B and C (bf16 or fp8 e4m3); dt is bf16 either way.  XCP: cache policy of
+// the X loads (kStream when X cannot stay in the Infinity Cache until the chunk scan reads it).
+template <typename TX, int N, int XCP>
 __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     const TX *__restrict__ x, const TX *__restrict__ Bm, const bf16_t *__restrict__ dt,
     const float *__restrict__ A, float *__restrict__ acum, float *__restrict__ dtc, f16 *__restrict__ states,
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
         {
             const int jp = ht / (P / 8), pg = ht % (P / 8), j = JB * m + 2 * jp;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) px[m][e].load(rx, (uint32_t)((j + e) * sx + 8 * pg));
+            for (int e = 0; e < 2; ++e) px[m][e].template load<XCP>(rx, (uint32_t)((j + e) * sx + 8 * pg));
         }
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
@@ -242,16 +243,23 @@ hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt
     const dim3 grid(d.nc, d.H / 2 + 4 * d.G, d.B);
     const bf16_t *dd = static_cast<const bf16_t *>(dt);
     f16 *st = static_cast<f16 *>(states);
-#define SSD_CSP_LAUNCH(NN)                                                                                          \
+#define SSD_CSP_LAUNCH2(NN, CP)                                                                                     \
     do {                                                                                                            \
         if (d.in == kInFp8)                                                                                         \
-            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<fp8_t, NN>, grid, 512, s,            \
+            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<fp8_t, NN, CP>, grid, 512, s,        \
                           static_cast<const fp8_t *>(x), static_cast<const fp8_t *>(Bm), dd, A, acum, dtc, st,    \
                           static_cast<const fp8_t *>(Cm), cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc);        \
         else                                                                                                        \
-            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<bf16_t, NN>, grid, 512, s,           \
+            launch_kernel("chunk_state_pair_kernel", chunk_state_pair_kernel<bf16_t, NN, CP>, grid, 512, s,       \
                           static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(Bm), dd, A, acum, dtc, st,  \
                           static_cast<const bf16_t *>(Cm), cb, o, d.L, d.H, d.G, d.sx, d.sbc, d.sdt, d.nc);       \
+    } while (0)
+#define SSD_CSP_LAUNCH(NN)                   \
+    do {                                     \
+        if (o.stream_x)                      \
+            SSD_CSP_LAUNCH2(NN, kStream);    \
+        else                                 \
+            SSD_CSP_LAUNCH2(NN, 0);          \
     } while (0)
     switch (d.N) {
     case 32: SSD_CSP_LAUNCH(32); break;
@@ -260,6 +268,7 @@ hipError_t launch_chunk_state_pair(const void *x, const void *Bm, const void *dt
     default: return hipErrorInvalidValue;
     }
 #undef SSD_CSP_LAUNCH
+#undef SSD_CSP_LAUNCH2
     return hipGetLastError();
 }
 

@@ -147,6 +147,9 @@ struct SsdOpts {
     // Bound of every wait between workgroups: 0 = the default; n > 0 = n - 1 polls (1: give up
     // at once, which only a test of the give-up path asks for).
     unsigned spin;
+    // Nonzero: the prefill's X is too large to stay in the Infinity Cache from the first launch
+    // to the chunk scan, and the launches that stream it read it with the kStream policy.
+    int stream_x;
 };
 // Polls a bounded wait makes: the default bound, or the one SsdOpts::spin asks for.
 constexpr unsigned kSpinLimit = 1u << 22;
@@ -234,9 +237,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// Cache policy of a buffer access: 0 (the default), or kStream: non-temporal, for data read
+// once per launch that cannot stay in the Infinity Cache until it is read again, so that it
+// does not displace what the next launch reads back.
+constexpr int kStream = 2;
+template <int CP = 0> __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP));
 }
 
 // Eight consecutive raw input elements held in registers between a global
@@ -246,7 +253,10 @@ template <> struct Raw8<bf16_t> {
     uint4 v;
     __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
     // element offset `e` inside the buffer resource `r`
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e) { v = buf_load16(r, 2u * e); }
+    template <int CP = 0> __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e)
+    {
+        v = buf_load16<CP>(r, 2u * e);
+    }
     __device__ __forceinline__ void zero() { v = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ void store(bf16_t *dst) const { *reinterpret_cast<uint4 *>(dst) = v; }
     __device__ __forceinline__ void to_f32(float f[8]) const
@@ -266,10 +276,10 @@ template <> struct Raw8<float> {
         a = reinterpret_cast<const float4 *>(p)[0];
         b = reinterpret_cast<const float4 *>(p)[1];
     }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e)
+    template <int CP = 0> __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e)
     {
-        a = __builtin_bit_cast(float4, buf_load16(r, 4u * e));
-        b = __builtin_bit_cast(float4, buf_load16(r, 4u * e + 16u));
+        a = __builtin_bit_cast(float4, buf_load16<CP>(r, 4u * e));
+        b = __builtin_bit_cast(float4, buf_load16<CP>(r, 4u * e + 16u));
     }
     __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ __forceinline__ void store(float *dst) const
@@ -284,14 +294,17 @@ template <> struct Raw8<float> {
     }
 };
 
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+template <int CP = 0> __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP));
 }
 template <> struct Raw8<fp8_t> {
     uint2 v;
     __device__ __forceinline__ void load(const fp8_t *p) { v = *reinterpret_cast<const uint2 *>(p); }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e) { v = buf_load8(r, e); }
+    template <int CP = 0> __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t e)
+    {
+        v = buf_load8<CP>(r, e);
+    }
     __device__ __forceinline__ void zero() { v = make_uint2(0u, 0u); }
     // widened to fp16 when staged (Traits<fp8_t>::raw_t)
     __device__ __forceinline__ void store(f16 *dst) const { *reinterpret_cast<uint4 *>(dst) = f8x8_to_f16x8(v); }
@@ -368,13 +381,13 @@ __device__ __forceinline__ int tr16_offset(int lane, int k0, int m0, int ld)
 // `lds + 16 * lane` (or `lds + 4 * lane`) (the LDS address must be wave-uniform).  Out-of-range reads
 // deliver zeros.  The load counts in the wavefront's vector-memory counter like any other.
 typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
+template <int CP = 0> __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)off, 0, 0, CP);
 }
-__device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
+template <int CP = 0> __device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, (int)off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, (int)off, 0, 0, CP);
 }
 
 // Eight raw inputs converted to fp16 and packed into 16 bytes (one LDS store).
