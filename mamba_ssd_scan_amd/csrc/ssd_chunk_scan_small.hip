@@ -57,6 +57,10 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
     __shared__ f16 xs[ROWS * LDX];
     __shared__ f16 hs[P * LDH];
     __shared__ float acs[TAB], dts[TAB], ecs[TAB];
+    // bf16 y (OPT only): each wavefront's 16-row output tile, regrouped so that the stores
+    // write whole rows
+    constexpr int YLD = P + 8;
+    __shared__ __align__(16) uint16_t ybuf[OPT ? 8 * 16 * YLD : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,22 +416,38 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
                 for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= silu(__uint_as_float(zr[pt][r] << 16));
         }
         // ---- y: buffer stores over the item's valid rows (rows past the sequence dropped);
-        // bf16: the even lane of each pair of columns stores both values.  The stores write
+        // bf16: whole rows through LDS (below).  The stores write
         // through the L2 (device scope): left dirty there, the whole y (25 MB at the 130M
         // shape, most of the L2s) is written back when the kernel ends, after the last
         // workgroup, where nothing overlaps it; streamed out as produced, the step is
         // ~1.4 us shorter.  (The persistent kernel streams many rounds of y through the L2,
         // whose write combining it needs: write-through there costs 10%.)
-        const bool drop = y16 && (li & 1);
+        if (OPT && y16) {
+            // bf16: the tile goes through this wavefront's own LDS rows (LDS operations of one
+            // wavefront complete in order, so no barrier), then every lane stores 16 bytes of
+            // one row: eight lanes write a whole 128-byte row, a wavefront eight rows at once
+            uint16_t *yb = ybuf + wave * (16 * YLD);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int pt = 0; pt < TP; ++pt) {
-                const float v = acc[pt][r];
-                uint32_t data = __float_as_uint(v);
-                if constexpr (OPT) data = y16 ? pack_bf16x2(v, swap_adjacent_lanes(v)) : data;
-                const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * H * P + pt * 16 + li);
-                __builtin_amdgcn_raw_buffer_store_b32(data, ry, (int)(drop ? 0x7ffffff0u : es * e), 0, kDeviceCoherent);
+                for (int pt = 0; pt < TP; ++pt) yb[(4 * lg + r) * YLD + pt * 16 + li] = f32_to_bf16_rne(acc[pt][r]);
+            constexpr int CH = P / 8;  // 16-byte pieces of a row
+#pragma unroll
+            for (int k = 0; k < 16 * CH / 64; ++k) {
+                const int u = lane + 64 * k, row = u / CH, piece = u % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&yb[row * YLD + 8 * piece]);
+                const uint32_t e = (uint32_t)((ibase + row) * H * P + 8 * piece);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                                       ry, (int)(2u * e), 0, kDeviceCoherent);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int pt = 0; pt < TP; ++pt) {
+                    const uint32_t e = (uint32_t)((ibase + 4 * lg + r) * H * P + pt * 16 + li);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pt][r]), ry, (int)(es * e), 0, kDeviceCoherent);
+                }
             }
         }
     }
