@@ -107,17 +107,20 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, i
     return w;
 }
 
-// Whether X is too large to stay in the Infinity Cache (256 MiB on MI355X) from the prefill's
-// first launch to its chunk scan: the chunk states are written, read, and written back as
-// entering states in between.  Then the launches that stream X read it non-temporally, which
-// leaves the cache to the states; measured at the 2.7B 16384-token shape (336 MB of X and
-// states) the step is ~3% shorter, while at the 130M 4096-token shape (25 MB), whose chunk
-// scan still finds X in the cache, it would be ~5% longer.
-bool stream_x(const ssd::Dims &d)
+// Whether X cannot stay in the Infinity Cache (256 MiB on MI355X) from the prefill's first
+// launch to its chunk scan: in between, the chunk states are written, read and written back
+// as entering states, and the scan writes y as it goes.  Then the launches that stream X (and
+// the scan's entering states, read once) read them non-temporally, which leaves the cache to
+// the states and to y on its way out.  In-process A/B: the 2.7B 16384-token step 238 -> 231 us,
+// the 370M 8 x 2048-token step 119.4 -> 116.8 us; at the 130M 4096-token shape (50 MB in all)
+// the chunk scan still finds X in the cache, and streaming would make the step ~5% longer.
+bool stream_x(const ssd::Dims &d, bool y_bf16)
 {
-    const double xb = (double)d.B * d.L * d.H * d.P * (d.in == ssd::kInFp8 ? 1 : d.in == ssd::kInBf16 ? 2 : 4);
+    const double tok = (double)d.B * d.L * d.H * d.P;
+    const double xb = tok * (d.in == ssd::kInFp8 ? 1 : d.in == ssd::kInBf16 ? 2 : 4);
     const double sb = (double)d.B * d.H * d.nc * d.P * d.N * (d.half() ? 2 : 4);
-    return xb + 2.0 * sb > 256.0 * 1024 * 1024;
+    const double yb = tok * (y_bf16 ? 2 : 4);
+    return xb + 2.0 * sb + yb > 256.0 * 1024 * 1024;
 }
 
 // How the prefill runs a shape whose P or N the kernels are not built for: P and N padded to
@@ -470,7 +473,7 @@ int prefill_impl(const void *x, const void *dt, const float *A, const void *Bm, 
     ssd::SsdOpts o = {dt_bias, dt_softplus ? 1 : 0, z, y_dtype == SSD_BF16 ? 1 : 0};
     o.ctl = reinterpret_cast<unsigned *>(ws + w.ctl);
     o.spin = spin_limit < 0 ? 0u : (unsigned)std::min(spin_limit, 0x7fffffffLL) + 1u;
-    o.stream_x = stream_x(d) ? 1 : 0;
+    o.stream_x = stream_x(d, y_dtype == SSD_BF16) ? 1 : 0;
     int ncu = 0;
     SSD_TRY(hip_status(ssd::device_cu_count(&ncu)));
     // The one-round path needs every workgroup of the chunk scan resident at once (its

@@ -165,16 +165,25 @@ __global__ __launch_bounds__(64 * NW) void chunk_scan_kernel(
             for (int k = 0; k < (XI + NL - 1) / NL; ++k) {
                 const int wi = k * NL + wave;
                 const int byte = 1024 * wi + 16 * lane, row = byte / (2 * P), col = byte % (2 * P);
-                buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
-                                 (uint32_t)(row * sx * 2 + col));
+                // (a uniform branch: X streamed past the Infinity Cache, see SsdOpts::stream_x)
+                if (opt.stream_x)
+                    buf_load_lds16<kStream>(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
+                                            (uint32_t)(row * sx * 2 + col));
+                else
+                    buf_load_lds16(wi < XI ? rx : make_rsrc(x, 0u), wi < XI ? stg + 1024 * wi : spare,
+                                   (uint32_t)(row * sx * 2 + col));
             }
             const f16 *hen = static_cast<const f16 *>(henv);
             const __amdgpu_buffer_rsrc_t rh = make_rsrc(hen + it.bhc * P * N, live ? (uint32_t)S::SH : 0u);
 #pragma unroll
             for (int k = 0; k < (HI + NL - 1) / NL; ++k) {
                 const int wi = k * NL + wave;
-                buf_load_lds16(wi < HI ? rh : make_rsrc(hen, 0u), wi < HI ? stg + S::SX + 1024 * wi : spare,
-                                 (uint32_t)(1024 * wi + 16 * lane));
+                if (opt.stream_x)
+                    buf_load_lds16<kStream>(wi < HI ? rh : make_rsrc(hen, 0u), wi < HI ? stg + S::SX + 1024 * wi : spare,
+                                            (uint32_t)(1024 * wi + 16 * lane));
+                else
+                    buf_load_lds16(wi < HI ? rh : make_rsrc(hen, 0u), wi < HI ? stg + S::SX + 1024 * wi : spare,
+                                   (uint32_t)(1024 * wi + 16 * lane));
             }
             // tables: slots 0 .. TI-1 stream dA_cum, TI .. 2TI-1 stream dt (zeros past Q)
 #pragma unroll

@@ -118,7 +118,13 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
             if (XU % 256 == 0 || u < XU) {  // (true at compile time when every thread has a unit)
                 const int jp = u / (P / 8), pg = u % (P / 8), j = j0 + 2 * jp;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) st.x[k][e].load(bx, (uint32_t)((j + e) * sx + 8 * pg));
+                for (int e = 0; e < 2; ++e) {
+                    // (a uniform branch: X streamed past the Infinity Cache, see SsdOpts::stream_x)
+                    if (opt.stream_x)
+                        st.x[k][e].template load<kStream>(bx, (uint32_t)((j + e) * sx + 8 * pg));
+                    else
+                        st.x[k][e].load(bx, (uint32_t)((j + e) * sx + 8 * pg));
+                }
             }
         }
 #pragma unroll
