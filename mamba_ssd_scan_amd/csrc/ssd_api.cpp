@@ -111,16 +111,17 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int headdim, int dstate, i
 // launch to its chunk scan: in between, the chunk states are written, read and written back
 // as entering states, and the scan writes y as it goes.  Then the launches that stream X (and
 // the scan's entering states, read once) read them non-temporally, which leaves the cache to
-// the states and to y on its way out.  In-process A/B: the 2.7B 16384-token step 238 -> 231 us,
-// the 370M 8 x 2048-token step 119.4 -> 116.8 us; at the 130M 4096-token shape (50 MB in all)
-// the chunk scan still finds X in the cache, and streaming would make the step ~5% longer.
+// the states and to y on its way out.  The bound is half the cache, as measured: in-process
+// A/B, the 2.7B 16384-token step 235 -> 226-229 us, the 370M 8 x 2048-token step 119.5 -> 117
+// us (fp32 y) and 117 -> 112.5 us (bf16 y, 268 MB in all); at the 130M 4096-token shape (50 MB)
+// the chunk scan still finds X in the cache, and streaming made the step ~5% longer.
 bool stream_x(const ssd::Dims &d, bool y_bf16)
 {
     const double tok = (double)d.B * d.L * d.H * d.P;
     const double xb = tok * (d.in == ssd::kInFp8 ? 1 : d.in == ssd::kInBf16 ? 2 : 4);
     const double sb = (double)d.B * d.H * d.nc * d.P * d.N * (d.half() ? 2 : 4);
     const double yb = tok * (y_bf16 ? 2 : 4);
-    return xb + 2.0 * sb + yb > 256.0 * 1024 * 1024;
+    return xb + 2.0 * sb + yb > 128.0 * 1024 * 1024;
 }
 
 // How the prefill runs a shape whose P or N the kernels are not built for: P and N padded to
