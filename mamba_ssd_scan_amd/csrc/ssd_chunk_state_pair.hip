@@ -13,7 +13,9 @@
 // per head), which is what bounds this launch when its whole grid is resident.
 //
 // The whole chunk is requested at once (four 64-token blocks in registers), then
-// contracted block by block through double-buffered LDS with one barrier per block.
+// contracted block by block through double-buffered LDS with one barrier per block.  fp8
+// inputs are requested 16 values per load (one token's 16 channels or state columns), half
+// the loads of the bf16 layout for the same elements.
 // Workgroups share nothing, so the grid may take any number of rounds; on grids much
 // larger than the GPU the whole-chunk requests keep 128 KB of X per compute unit in
 // flight (two workgroups of two heads), which is what HBM needs to stream near its rate.
@@ -39,6 +41,10 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
     constexpr int TPW = (NT + 3) / 4;  // output tiles per wavefront of a head
     constexpr int XU = (JB / 2) * (P / 8);                      // units of two tokens x 8 channels, per head
     constexpr int BU = (JB / 2) * (N / 8), BPT = (BU + 511) / 512;  // of B, over the whole workgroup
+    // fp8: one 16-byte load carries 16 values, so a unit is one token x 16 channels (state
+    // columns): half the loads of the two-token bf16 units for the same elements
+    constexpr bool F8 = std::is_same<TX, fp8_t>::value;
+    constexpr int BU8 = JB * (N / 16), BPT8 = (BU8 + 511) / 512;
     static_assert(XU == 256, "one X unit per thread of a head");
     typedef Gemm1Chunk<TX, N, 4, 256> G1;
     constexpr int kStateBytes = 2 * (2 * XSZ + BSZ) * 2 + 2 * Q * 4;
@@ -90,21 +96,35 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) dtraw[k] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)((lane * 4 + k) * sdt * 2), 0, 0);
     }
-    Raw8<TX> px[NBLK][2], pb[NBLK][BPT][2];
+    Raw8<TX> px[F8 ? 1 : NBLK][2], pb[F8 ? 1 : NBLK][BPT][2];
+    uint4 px8[F8 ? NBLK : 1], pb8[F8 ? NBLK : 1][BPT8];
 #pragma unroll
     for (int m = 0; m < NBLK; ++m) {
-        {
-            const int jp = ht / (P / 8), pg = ht % (P / 8), j = JB * m + 2 * jp;
+        if constexpr (F8) {
+            const int j = JB * m + ht / (P / 16), pg = ht % (P / 16);
+            px8[m] = buf_load16<XCP>(rx, (uint32_t)(j * sx + 16 * pg));
 #pragma unroll
-            for (int e = 0; e < 2; ++e) px[m][e].template load<XCP>(rx, (uint32_t)((j + e) * sx + 8 * pg));
-        }
+            for (int k = 0; k < BPT8; ++k) {
+                const int u = tid + k * 512;
+                if (BU8 % 512 == 0 || u < BU8) {
+                    const int jb = JB * m + u / (N / 16), ng = u % (N / 16);
+                    pb8[m][k] = buf_load16(rb, (uint32_t)(jb * sbc + 16 * ng));
+                }
+            }
+        } else {
+            {
+                const int jp = ht / (P / 8), pg = ht % (P / 8), j = JB * m + 2 * jp;
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int u = tid + k * 512;
-            if (BU % 512 == 0 || u < BU) {
-                const int jp = u / (N / 8), ng = u % (N / 8), j = JB * m + 2 * jp;
+                for (int e = 0; e < 2; ++e) px[m][e].template load<XCP>(rx, (uint32_t)((j + e) * sx + 8 * pg));
+            }
 #pragma unroll
-                for (int e = 0; e < 2; ++e) pb[m][k][e].load(rb, (uint32_t)((j + e) * sbc + 8 * ng));
+            for (int k = 0; k < BPT; ++k) {
+                const int u = tid + k * 512;
+                if (BU % 512 == 0 || u < BU) {
+                    const int jp = u / (N / 8), ng = u % (N / 8), j = JB * m + 2 * jp;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) pb[m][k][e].load(rb, (uint32_t)((j + e) * sbc + 8 * ng));
+                }
             }
         }
     }
@@ -148,19 +168,40 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
 
     // block m into LDS buffer buf: the head's X weighted by w_j (fp16), the shared B (fp16)
     auto commit = [&](int m, int buf) {
-        {
-            const int jp = ht / (P / 8), pg = ht % (P / 8), j = 2 * jp;
-            const float w0 = ws[JB * m + j], w1 = ws[JB * m + j + 1];
-            *reinterpret_cast<uint4 *>(&xs(buf, hw)[j * LDXR + 8 * pg]) = raw8_to_f16x8(px[m][0], w0);
-            *reinterpret_cast<uint4 *>(&xs(buf, hw)[(j + 1) * LDXR + 8 * pg]) = raw8_to_f16x8(px[m][1], w1);
-        }
+        if constexpr (F8) {
+            const int j = ht / (P / 16), pg = ht % (P / 16);
+            const float w = ws[JB * m + j];
+            Raw8<fp8_t> lo, hi;
+            lo.v = make_uint2(px8[m].x, px8[m].y);
+            hi.v = make_uint2(px8[m].z, px8[m].w);
+            *reinterpret_cast<uint4 *>(&xs(buf, hw)[j * LDXR + 16 * pg]) = raw8_to_f16x8(lo, w);
+            *reinterpret_cast<uint4 *>(&xs(buf, hw)[j * LDXR + 16 * pg + 8]) = raw8_to_f16x8(hi, w);
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int u = tid + k * 512;
-            if (BU % 512 == 0 || u < BU) {
-                const int jp = u / (N / 8), ng = u % (N / 8);
-                *reinterpret_cast<uint4 *>(&bs(buf)[(2 * jp) * LDBR + 8 * ng]) = raw8_to_f16x8(pb[m][k][0]);
-                *reinterpret_cast<uint4 *>(&bs(buf)[(2 * jp + 1) * LDBR + 8 * ng]) = raw8_to_f16x8(pb[m][k][1]);
+            for (int k = 0; k < BPT8; ++k) {
+                const int u = tid + k * 512;
+                if (BU8 % 512 == 0 || u < BU8) {
+                    const int jb = u / (N / 16), ng = u % (N / 16);
+                    *reinterpret_cast<uint4 *>(&bs(buf)[jb * LDBR + 16 * ng]) =
+                        f8x8_to_f16x8(make_uint2(pb8[m][k].x, pb8[m][k].y));
+                    *reinterpret_cast<uint4 *>(&bs(buf)[jb * LDBR + 16 * ng + 8]) =
+                        f8x8_to_f16x8(make_uint2(pb8[m][k].z, pb8[m][k].w));
+                }
+            }
+        } else {
+            {
+                const int jp = ht / (P / 8), pg = ht % (P / 8), j = 2 * jp;
+                const float w0 = ws[JB * m + j], w1 = ws[JB * m + j + 1];
+                *reinterpret_cast<uint4 *>(&xs(buf, hw)[j * LDXR + 8 * pg]) = raw8_to_f16x8(px[m][0], w0);
+                *reinterpret_cast<uint4 *>(&xs(buf, hw)[(j + 1) * LDXR + 8 * pg]) = raw8_to_f16x8(px[m][1], w1);
+            }
+#pragma unroll
+            for (int k = 0; k < BPT; ++k) {
+                const int u = tid + k * 512;
+                if (BU % 512 == 0 || u < BU) {
+                    const int jp = u / (N / 8), ng = u % (N / 8);
+                    *reinterpret_cast<uint4 *>(&bs(buf)[(2 * jp) * LDBR + 8 * ng]) = raw8_to_f16x8(pb[m][k][0]);
+                    *reinterpret_cast<uint4 *>(&bs(buf)[(2 * jp + 1) * LDBR + 8 * ng]) = raw8_to_f16x8(pb[m][k][1]);
+                }
             }
         }
     };
