@@ -251,7 +251,15 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
         }
     }
 
-    // ---- S_c [P][N] (fp16): lane holds columns n = 16 nt + 4 lg + r of row p = 16 pt + li
+    // ---- S_c [P][N] (fp16): lane holds columns n = 16 nt + 4 lg + r of row p = 16 pt + li.
+    // The tiles go through LDS (the blocks' buffers are free once every wavefront is past the
+    // last contraction), so that the state -- one contiguous P x N block per head -- leaves as
+    // whole rows, 16 bytes per lane and 1 KB per store instruction, instead of 32-byte pieces
+    // of 16 rows.
+    constexpr int LDS_ = N + 8;  // padded row of the staged state (fp16)
+    static_assert(2 * P * LDS_ * 2 <= kBytes, "staged chunk states fit the block buffers");
+    f16 *sst = reinterpret_cast<f16 *>(smem) + hw * P * LDS_;
+    __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         int pt, nt;
@@ -263,11 +271,19 @@ __global__ __launch_bounds__(512) void chunk_state_pair_kernel(
             pt = lw / TN + (4 / TN) * tt;
             nt = lw % TN;
         }
-        const size_t e = bhc * P * N + (size_t)(pt * 16 + li) * N + nt * 16 + 4 * lg;
         uint2 v;
         v.x = pack_f16x2(acc[tt][0], acc[tt][1]);
         v.y = pack_f16x2(acc[tt][2], acc[tt][3]);
-        *reinterpret_cast<uint2 *>(states + e) = v;
+        *reinterpret_cast<uint2 *>(&sst[(pt * 16 + li) * LDS_ + nt * 16 + 4 * lg]) = v;
+    }
+    __syncthreads();
+    constexpr int RU = N / 8;  // 16-byte pieces of a state row
+    static_assert((P * RU) % 256 == 0, "whole pieces per thread of a head");
+#pragma unroll
+    for (int k = 0; k < P * RU / 256; ++k) {
+        const int u = ht + 256 * k, row = u / RU, piece = u % RU;
+        *reinterpret_cast<uint4 *>(states + bhc * P * N + (size_t)row * N + 8 * piece) =
+            *reinterpret_cast<const uint4 *>(&sst[row * LDS_ + 8 * piece]);
     }
 }
 
