@@ -381,7 +381,14 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
     }
 
     // ---- write S_c [P][N] (fp32, or fp16 for bf16 inputs): lane holds columns
-    // n = 16 nt + 4 lg + r of row p = 16 pt + li
+    // n = 16 nt + 4 lg + r of row p = 16 pt + li.  fp16 states go through LDS (the block
+    // buffers, free after the last contraction) when they fit there, so that the state -- one
+    // contiguous P x N block -- is stored as whole rows, 16 bytes per lane, instead of 32-byte
+    // pieces of 16 rows.
+    constexpr int LDS_ = N + 8;
+    constexpr bool STAGE = !F32 && P * LDS_ * 2 <= 2 * (XSZ + BSZ) * (int)sizeof(op_t);
+    f16 *sst = reinterpret_cast<f16 *>(smem);
+    if constexpr (STAGE) __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int t = wave + 4 * tt;
@@ -395,8 +402,22 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn *__restrict_
                 uint2 v;
                 v.x = pack_f16x2(acc[tt][0], acc[tt][1]);
                 v.y = pack_f16x2(acc[tt][2], acc[tt][3]);
-                *reinterpret_cast<uint2 *>(static_cast<f16 *>(states) + e) = v;
+                if constexpr (STAGE)
+                    *reinterpret_cast<uint2 *>(&sst[(pt * 16 + li) * LDS_ + nt * 16 + 4 * lg]) = v;
+                else
+                    *reinterpret_cast<uint2 *>(static_cast<f16 *>(states) + e) = v;
             }
+        }
+    }
+    if constexpr (STAGE) {
+        __syncthreads();
+        constexpr int RU = N / 8, NU = P * RU;  // 16-byte pieces of a state row, of the state
+#pragma unroll
+        for (int k = 0; k < (NU + 255) / 256; ++k) {
+            const int u = tid + 256 * k, row = u / RU, piece = u % RU;
+            if (NU % 256 == 0 || u < NU)
+                *reinterpret_cast<uint4 *>(static_cast<f16 *>(states) + bhc * P * N + (size_t)row * N + 8 * piece) =
+                    *reinterpret_cast<const uint4 *>(&sst[row * LDS_ + 8 * piece]);
         }
     }
 }
