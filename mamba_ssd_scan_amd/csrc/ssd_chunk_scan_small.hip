@@ -431,6 +431,9 @@ __global__ __launch_bounds__(512, 4) void chunk_scan_small_kernel(  // 4 waves p
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int pt = 0; pt < TP; ++pt) yb[(4 * lg + r) * YLD + pt * 16 + li] = f32_to_bf16_rne(acc[pt][r]);
+            // the 2-byte writes are read back as 16-byte words by other lanes: wait for them and
+            // keep the compiler from moving the reads above them (they differ in type)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             constexpr int CH = P / 8;  // 16-byte pieces of a row
 #pragma unroll
             for (int k = 0; k < 16 * CH / 64; ++k) {
