@@ -307,6 +307,35 @@ def test_full_size_workload_sampled_heads(cfg, heads):
     assert torch.isfinite(y).all().item()
 
 
+@pytest.mark.parametrize("cfg,heads,seed", [(1, [2, 11, 22], 1000), (2, [3, 20, 30], 1000), (3, [5, 38, 77], 1000),
+                                           (3, [1, 40, 78], 2000)])
+def test_full_size_workload_other_draws(cfg, heads, seed):
+    """The full workloads again with other seeded draws and other heads sampled, so that the
+    bar is not met by one draw alone."""
+    torch = gh.torch()
+    s = synth.WORKLOADS[cfg]
+    full = synth.prefill_inputs(s, synth.SEED_BASE + cfg + seed)
+    g = gh.upload(full)
+    y, hT = ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk)
+    y0, _ = ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], None, g["h0"], chunk=s.chunk, final_state=None)
+    torch.cuda.synchronize()
+    bsel = slice(0, 2) if s.batch > 2 else slice(None)
+    sub = synth.select_heads(full, heads, s.ngroups, s.nheads)
+    for k in ("x", "dt", "B", "C"):
+        sub[k] = sub[k][bsel]
+    if sub["h0"] is not None:
+        sub["h0"] = sub["h0"][bsel]
+    yo, ho = gh.oracle_prefill(sub)
+    yo0, _ = gh.oracle_prefill(sub, D=None)
+    errs = dict(y=rel_err(y[bsel][:, :, heads].cpu().numpy(), yo),
+                y_D0=rel_err(y0[bsel][:, :, heads].cpu().numpy(), yo0),
+                state=rel_err(hT[bsel][:, heads].cpu().numpy(), ho))
+    print(f"[full cfg{cfg} seed+{seed}] heads={heads} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for k, v in errs.items():
+        assert v < TOL["bf16"], (k, v)
+
+
 def test_full_size_decode_sampled():
     """Decode at the full batch/head shape for 64 tokens; oracle on a sample of (b, h)."""
     torch = gh.torch()
