@@ -336,6 +336,30 @@ def test_full_size_workload_other_draws(cfg, heads, seed):
         assert v < TOL["bf16"], (k, v)
 
 
+@pytest.mark.parametrize("L", [8192, 16384])
+def test_130m_long_prefill_either_side_of_the_streaming_bound(L):
+    """The 130M layer at 8192 and 16384 tokens: X, twice the states and y come to ~100 MB and
+    ~200 MB, on either side of the bound past which the prefill streams X past the Infinity
+    Cache; both run the three-launch path with the pipelined chunk scan (more than 16 chunks).
+    Sampled heads against the oracle."""
+    torch = gh.torch()
+    s = synth.PrefillShape(1, L, 24, 64, 128, 1, 256, "bf16", "randn")
+    full = synth.prefill_inputs(s, synth.SEED_BASE + 50 + L)
+    g = gh.upload(full)
+    heads = [0, 13, 23]
+    y, hT = ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=s.chunk)
+    y0, _ = ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], None, g["h0"], chunk=s.chunk, final_state=None)
+    torch.cuda.synchronize()
+    sub = synth.select_heads(full, heads, s.ngroups, s.nheads)
+    yo, ho = gh.oracle_prefill(sub)
+    yo0, _ = gh.oracle_prefill(sub, D=None)
+    errs = dict(y=rel_err(y[:, :, heads].cpu().numpy(), yo), y_D0=rel_err(y0[:, :, heads].cpu().numpy(), yo0),
+                state=rel_err(hT[:, heads].cpu().numpy(), ho))
+    print(f"[130M L={L}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v < TOL["bf16"], (k, v)
+
+
 def test_full_size_decode_sampled():
     """Decode at the full batch/head shape for 64 tokens; oracle on a sample of (b, h)."""
     torch = gh.torch()
