@@ -91,3 +91,20 @@ def test_method_bytes_of_the_headline_prefill():
     assert k["chunk_state_pair_kernel"]["method_bytes"] == x + dt + 2 * bc
     assert k["state_passing_kernel"]["method_bytes"] == 2 * st
     assert bench.step_kernels(s, NCU)[-1] == "chunk_scan_pipe_kernel"
+
+
+def test_fp8_inputs_take_the_same_launches_and_count_one_byte_per_value():
+    """x, B and C in fp8 e4m3 (dt in bf16): the same kernels as bf16 inputs, and method bytes
+    of one byte per x, B and C value (two per dt value)."""
+    import dataclasses
+    s = dataclasses.replace(synth.WORKLOADS[3], dtype="fp8")
+    assert bench.step_kernels(s, NCU) == ["chunk_state_pair_kernel", "state_passing_kernel", "chunk_scan_pipe_kernel"]
+    s1 = dataclasses.replace(synth.WORKLOADS[1], dtype="fp8")
+    assert bench.step_kernels(s1, NCU) == ["chunk_state_pair_kernel", "chunk_scan_small_kernel"]
+    L, H, P, N = 16384, 80, 64, 128
+    x, dt, bc, y, st = L * H * P, L * H * 2, L * N, L * H * P * 4, H * P * N * 4
+    c = bench.alg_counts(s, NCU)
+    assert c["fused_bytes"] == x + dt + 2 * bc + y + 2 * st == 431489024
+    # the intermediates stay fp16, as for bf16 inputs
+    assert c["kernels"]["state_passing_kernel"]["bytes"] == bench.alg_counts(synth.WORKLOADS[3], NCU)["kernels"][
+        "state_passing_kernel"]["bytes"]
