@@ -45,11 +45,21 @@ def _upload(inp, opt):
     return g
 
 
-@pytest.mark.parametrize("dtype,Q,L,P,N,G", [("bf16", 256, 700, 64, 128, 1), ("bf16", 64, 333, 32, 64, 2),
-                                             ("f32", 64, 300, 64, 64, 1), ("bf16", 128, 129, 128, 32, 4)])
-def test_prefill_ex_softplus_gate(dtype, Q, L, P, N, G):
+def _expect_pipelined(B, L, H, P, N, G, Q):
+    """The shape has more items than two per CU: the pipelined chunk scan takes it."""
+    import bench
+    kernels = bench.step_kernels(synth.PrefillShape(B, L, H, P, N, G, Q, "bf16"))
+    assert "chunk_scan_pipe_kernel" in kernels, kernels
+
+
+@pytest.mark.parametrize("dtype,Q,L,P,N,G,H", [("bf16", 256, 700, 64, 128, 1, 4), ("bf16", 64, 333, 32, 64, 2, 4),
+                                               ("f32", 64, 300, 64, 64, 1, 4), ("bf16", 128, 129, 128, 32, 4, 4),
+                                               ("bf16", 256, 2100, 64, 128, 4, 40)])
+def test_prefill_ex_softplus_gate(dtype, Q, L, P, N, G, H):
     torch = gh.torch()
-    inp, opt = _case(dtype, L=L, P=P, N=N, G=G, H=max(G, 4))
+    inp, opt = _case(dtype, L=L, P=P, N=N, G=G, H=H)
+    if H == 40:
+        _expect_pipelined(2, L, H, P, N, G, Q)
     g = _upload(inp, opt)
     y, hT = ssd.prefill_ex(g["x"], g["dt_raw"], g["A"], g["B"], g["C"], g["D"], g["h0"], dt_bias=g["dt_bias"],
                            dt_softplus=True, z=g["z"], chunk=Q)
@@ -65,10 +75,13 @@ def test_prefill_ex_softplus_gate(dtype, Q, L, P, N, G):
     assert all(np.isfinite(v) and v < TOL[dtype] for v in e.values()), e
 
 
-@pytest.mark.parametrize("dtype,Q", [("bf16", 256), ("bf16", 64), ("f32", 128)])
-def test_prefill_ex_bf16_output(dtype, Q):
+@pytest.mark.parametrize("dtype,Q,L,H,G", [("bf16", 256, 611, 4, 1), ("bf16", 64, 611, 4, 1), ("f32", 128, 611, 4, 1),
+                                         ("bf16", 256, 2100, 40, 4)])
+def test_prefill_ex_bf16_output(dtype, Q, L, H, G):
     torch = gh.torch()
-    inp, opt = _case(dtype, L=611, seed=22)
+    inp, opt = _case(dtype, L=L, H=H, G=G, seed=22)
+    if H == 40:
+        _expect_pipelined(2, L, H, 64, 128, G, Q)
     g = _upload(inp, opt)
     for z in (None, g["z"]):
         y32, _ = ssd.prefill_ex(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], z=z, chunk=Q)
@@ -82,7 +95,7 @@ def test_prefill_ex_bf16_output(dtype, Q):
         yo, _ = gated.prefill(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
                               z=None if z is None else opt["z"])
         e = rel_err(y16.float().cpu().numpy(), yo)
-        print(f"[prefill_ex bf16 y] {dtype} Q={Q} gate={z is not None} err={e:.2e}", flush=True)
+        print(f"[prefill_ex bf16 y] {dtype} Q={Q} L={L} H={H} G={G} gate={z is not None} err={e:.2e}", flush=True)
         assert e < TOL[dtype] + 2.0 ** -8
 
 

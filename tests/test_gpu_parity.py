@@ -208,6 +208,9 @@ def test_stage_chunk_scan(dtype, Q, P, N, G):
     ("f32", 2, 260, 3, 32, 128, 1, 128, "softplus", True),
     ("bf16", 3, 1, 4, 64, 64, 1, 64, "softplus", True),         # one token
     ("bf16", 1, 64, 4, 64, 64, 1, 64, "weak", True),            # exactly one chunk
+    # 720 items (more than two per CU): two-head chunk state and the pipelined scan, with
+    # four groups, two sequences and a ragged last chunk
+    ("bf16", 2, 2100, 40, 64, 128, 4, 256, "softplus", True),
 ])
 def test_prefill_matches_oracle(case):
     dtype, B, L, H, P, N, G, Q, mode, init = case
