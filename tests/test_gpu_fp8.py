@@ -71,13 +71,15 @@ def test_fp8_paths_agree_bit_for_bit():
         ssd.prefill(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["h0"], chunk=256, path=ssd.PATH_SINGLE_PASS)
 
 
-@pytest.mark.parametrize("Q,N,y16", [(256, 128, False), (64, 64, True)])
-def test_fp8_prefill_options(Q, N, y16):
+@pytest.mark.parametrize("Q,N,y16,L,H,G", [(256, 128, False, 700, 4, 1), (64, 64, True, 700, 4, 1),
+                                          # 720 items: the pipelined chunk scan with the gate and bf16 y
+                                          (256, 128, True, 2100, 40, 4)])
+def test_fp8_prefill_options(Q, N, y16, L, H, G):
     """dt = softplus(dt + bias) and the gate y * silu(z) with bf16 dt and z beside e4m3 x, B
     and C; bf16 y within the fp32-y bar plus its own rounding (2^-8)."""
     torch = gh.torch()
     rng = _rng(2 + Q)
-    inp = synth.random_prefill(rng, 2, 700, 4, 64, N, 1, "fp8")
+    inp = synth.random_prefill(rng, 2, L, H, 64, N, G, "fp8")
     opt = synth.option_inputs(rng, inp)
     g = gh.upload(inp)
     dtr = synth.to_torch(opt["dt_raw"], "bf16")
@@ -90,7 +92,7 @@ def test_fp8_prefill_options(Q, N, y16):
     kw = dict(dt_bias=opt["dt_bias"], dt_softplus=True, z=opt["z"])
     yo, ho = gated.prefill(inp["x"], opt["dt_raw"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"], **kw)
     ey, es = rel_err(y.float().cpu().numpy(), yo), rel_err(fin.cpu().numpy(), ho)
-    print(f"[fp8 options] Q={Q} N={N} y16={y16} y={ey:.2e} state={es:.2e}", flush=True)
+    print(f"[fp8 options] Q={Q} N={N} L={L} H={H} G={G} y16={y16} y={ey:.2e} state={es:.2e}", flush=True)
     assert ey < TOL["fp8"] + (2.0 ** -8 if y16 else 0.0) and es < TOL["fp8"]
     with pytest.raises(TypeError):  # dt beside e4m3 inputs is bf16
         ssd.prefill(g["x"], g["x"][..., 0].contiguous(), g["A"], g["B"], g["C"], chunk=Q)
